@@ -1,0 +1,97 @@
+"""H2O (heavy-hitter) budgeted decode in float64 (test infrastructure only).
+
+[KVC] section "Heavy-Hitter Oracle (H2O) e a esparsidade de cauda pesada": each
+cached token j carries the attention it has received summed over decode steps,
+s_j = sum_t alpha_{t,j}.  When the cache reaches its budget K_budget the manager
+prunes: a recent partition keeps the L_local newest tokens, a heavy-hitter
+partition keeps the K_HH historical tokens with the largest s_j, and the rest is
+freed.
+
+Readings (the pages leave these open):
+* Order inside a step: evict one token if the cache is at its budget, write the
+  new token (s = 0), attend over the cache, then add this step's attention
+  weights to every cached token's s.  The span is therefore exactly the budget
+  and the new token receives its own weight in the step it arrives.
+* The recent partition includes the new token: at step t the tokens with
+  position > t - L_local are protected; the victim is the smallest s among the
+  others, the decision taken on s rounded to float32 (the GPU's precision), ties
+  evicting the newer token (the same order as SnapKV's keep rule: higher score,
+  then lower index, is kept).
+* With grouped-query attention one s is kept per KV head and is the sum of the
+  weights of the G query heads that share it.
+* No positional rotation is applied: cached keys are used as given.
+"""
+import numpy as np
+
+from .attention import attend_one, softmax
+
+
+class H2OHead:
+    """The H2O cache of one (batch row, KV head) shared by G query heads."""
+
+    def __init__(self, budget: int, n_recent: int, positions=(), keys=(), values=(), scores=()):
+        if not 0 < n_recent <= budget:
+            raise ValueError("need 0 < n_recent <= budget")
+        self.budget, self.n_recent = int(budget), int(n_recent)
+        self.pos = [int(p) for p in positions]
+        self.k = [np.asarray(x, np.float64) for x in keys]
+        self.v = [np.asarray(x, np.float64) for x in values]
+        self.s = [float(x) for x in scores]
+        if not (len(self.pos) == len(self.k) == len(self.v) == len(self.s) <= budget):
+            raise ValueError("inconsistent initial state")
+
+    def victim_index(self, t: int) -> int:
+        """Entry evicted before writing token ``t`` (the cache must be full)."""
+        cands = [i for i, p in enumerate(self.pos) if p <= t - self.n_recent]
+        if not cands:
+            raise ValueError("no eviction candidate")
+        return min(cands, key=lambda i: (float(np.float32(self.s[i])), -self.pos[i]))
+
+    def step(self, t: int, q: np.ndarray, k_t: np.ndarray, v_t: np.ndarray, scale=None):
+        """Decode token ``t`` with queries q[G][D]; returns (out[G][D], evicted position or None)."""
+        q = np.asarray(q, np.float64)
+        evicted = None
+        if len(self.pos) == self.budget:
+            i = self.victim_index(t)
+            evicted = self.pos[i]
+            for lst in (self.pos, self.k, self.v, self.s):
+                del lst[i]
+        self.pos.append(int(t))
+        self.k.append(np.asarray(k_t, np.float64))
+        self.v.append(np.asarray(v_t, np.float64))
+        self.s.append(0.0)
+        K, V = np.stack(self.k), np.stack(self.v)
+        sc = 1.0 / np.sqrt(q.shape[-1]) if scale is None else float(scale)
+        out = np.empty((q.shape[0], V.shape[1]))
+        weights = np.zeros(len(self.pos))
+        for h in range(q.shape[0]):
+            out[h], p = attend_one(q[h], K, V, sc)
+            weights += p
+        self.s = [a + b for a, b in zip(self.s, weights)]
+        return out, evicted
+
+
+def h2o_prompt_select(Q, K, budget: int, n_recent: int, scale=None):
+    """Prompt-phase selection for one KV head (small prompts only).
+
+    Q[T][G][D] are the prompt queries of the G heads sharing K[T][D].  Each prompt
+    token j accumulates s_j = sum over rows t >= j and heads of the causal
+    attention weight; the last ``n_recent`` tokens are kept, and of the older ones
+    the ``budget - n_recent`` best by (higher float32 s, lower position).
+    Returns (kept positions ascending, s of every prompt token).
+    """
+    Q = np.asarray(Q, np.float64)
+    K = np.asarray(K, np.float64)
+    T, G, D = Q.shape
+    sc = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    s = np.zeros(T)
+    for h in range(G):
+        for t in range(T):
+            s[: t + 1] += softmax((K[: t + 1] @ Q[t, h]) * sc)
+    if budget >= T:
+        return np.arange(T, dtype=np.int64), s
+    old = T - n_recent
+    s32 = s[:old].astype(np.float32)
+    order = sorted(range(old), key=lambda j: (-float(s32[j]), j))
+    keep = sorted(order[: budget - n_recent]) + list(range(old, T))
+    return np.array(keep, dtype=np.int64), s
