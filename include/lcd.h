@@ -1,0 +1,244 @@
+/*
+ * lcd.h -- C ABI of the compressed-KV decode library for AMD MI355X (gfx950).
+ *
+ * Single-token decode attention over a compressed KV cache, and the SnapKV
+ * prefill compression that produces one.  Sources, cited by title and section:
+ *   [KVC]  "Compressão e Poda Dinâmica de KV Cache: StreamingLLM, SnapKV,
+ *          PyramidKV e DuoAttention" (produtoramaxvision.com.br).
+ *   [SINK] "attention sinks" (tonho.wtf encyclopedia entry).
+ *   [KVL]  "O KV cache", lesson 7.2 (llmdeepdive.com).
+ *
+ * Conventions shared by every entry point
+ *   Ownership   All device memory (cache, auxiliary state, workspaces, inputs,
+ *               outputs) is allocated and owned by the caller.  The library
+ *               allocates no device memory; a cache handle owns only host-side
+ *               state (configuration, per-layer token counters) and
+ *               lcd_kv_cache_destroy frees only that.
+ *   Pointers    "device" pointers must be device memory of the current HIP
+ *               device, 16-byte aligned, laid out exactly as documented
+ *               (row-major, innermost dimension last, no padding).
+ *   Streams     `stream` is a hipStream_t passed as void*; NULL is the null
+ *               stream.  Every call only enqueues work on that stream and
+ *               returns; the library never synchronises.  Ordering across
+ *               streams is the caller's responsibility.
+ *   Errors      Every argument is validated on the host before anything is
+ *               enqueued.  On error the call returns a non-zero lcd_status,
+ *               enqueues nothing, leaves the handle's state unchanged and sets a
+ *               thread-local message readable with lcd_last_error().  A failed
+ *               kernel launch returns LCD_EHIP; faults inside a kernel surface at
+ *               the caller's next synchronisation.  No C++ exception crosses the
+ *               ABI.
+ *   Threads     A handle is not thread-safe; distinct handles are independent.
+ *   Dtypes      LCD_BF16 tensors hold bfloat16 bit patterns (uint16); LCD_F32
+ *               tensors hold IEEE float32.  Attention outputs are always float32
+ *               and accumulation is float32.
+ */
+#ifndef LCD_H
+#define LCD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LCD_ABI_VERSION 1
+
+typedef enum lcd_status {
+  LCD_OK = 0,
+  LCD_EINVAL = 1,       /* invalid argument value or null pointer             */
+  LCD_ESHAPE = 2,       /* unsupported or inconsistent shape                  */
+  LCD_EALIGN = 3,       /* pointer not 16-byte aligned                        */
+  LCD_ECAPACITY = 4,    /* operation would exceed the cache capacity          */
+  LCD_ESIZE = 5,        /* a caller buffer is smaller than required          */
+  LCD_EHIP = 6,         /* a HIP runtime call or kernel launch failed        */
+  LCD_EUNSUPPORTED = 7  /* valid request this build does not implement        */
+} lcd_status;
+
+typedef enum lcd_dtype { LCD_F32 = 0, LCD_BF16 = 1 } lcd_dtype;
+
+/* Cache policies.
+ * LCD_SINK_RING  [KVC] "Attention Sinks e o StreamingLLM para fluxos contínuos";
+ *                [SINK] "como funciona".  n_sink fixed attention-sink slots followed
+ *                by a circular buffer of `window` slots.  The window counts the
+ *                token being decoded: kv_append writes (evicting the oldest window
+ *                entry once full) before decode_attn attends, so the newest token
+ *                attends itself.  Token a lives in slot a if a < n_sink, else in
+ *                slot n_sink + (a - n_sink) mod window.
+ * LCD_APPEND     Fixed capacity, rows appended in order and never evicted: the
+ *                layout of a SnapKV-compressed cache ([KVC] "SnapKV e a seleção de
+ *                contexto no prefill") that decode continues from.
+ * LCD_H2O        [KVC] "Heavy-Hitter Oracle (H2O) e a esparsidade de cauda pesada".
+ *                Fixed budget = capacity; one accumulated attention score per slot;
+ *                when full, each append overwrites the slot of the lowest score
+ *                among tokens older than the n_recent newest (ties evict the newer
+ *                token).  decode_attn adds the step's attention weights (summed
+ *                over the query heads sharing the KV head) to the scores and picks
+ *                the next victim. */
+typedef enum lcd_policy { LCD_SINK_RING = 0, LCD_APPEND = 1, LCD_H2O = 2 } lcd_policy;
+
+typedef struct lcd_cache_config {
+  int32_t batch;       /* B >= 1 (all rows advance in lockstep)                   */
+  int32_t n_layers;    /* L >= 1 cached attention layers                           */
+  int32_t n_q_heads;   /* H_q, a multiple of n_kv_heads; H_q / H_kv <= 8           */
+  int32_t n_kv_heads;  /* H_kv >= 1; query head h reads KV head h / (H_q / H_kv)  */
+  int32_t head_dim;    /* D in {64, 128, 256}                                      */
+  int32_t dtype;       /* lcd_dtype of K, V and q                                  */
+  int32_t policy;      /* lcd_policy                                               */
+  int32_t n_sink;      /* SINK_RING: sink slots S >= 0                             */
+  int32_t window;      /* SINK_RING: ring slots W >= 1; capacity C = S + W          */
+  int32_t capacity;    /* APPEND, H2O: slots C >= 1 per (layer, batch row, KV head) */
+  int32_t n_recent;    /* H2O: protected newest tokens, 1 <= n_recent <= capacity;
+                          includes the token being decoded                          */
+  int32_t rope;        /* SINK_RING only: 1 = keys are stored un-rotated and q and
+                          every key are rotated at decode time at their in-cache
+                          positions ([SINK] "como funciona"), 0 = no rotation.
+                          Must be 0 for APPEND and H2O (their inputs are used as
+                          given).  Rotation pairs element i with i + D/2 and turns
+                          pair i by position * rope_base^(-2i/D).                  */
+  double rope_base;    /* > 1 when rope = 1                                        */
+  double scale;        /* logit scale; 0 selects 1/sqrt(head_dim)                  */
+} lcd_cache_config;
+
+typedef struct lcd_cache lcd_cache; /* opaque host handle */
+
+/* Version of this ABI (LCD_ABI_VERSION). */
+int lcd_abi_version(void);
+
+/* Message of the last error on the calling thread ("" if none).  The pointer is
+ * valid until the next lcd_* call on this thread. */
+const char* lcd_last_error(void);
+
+/* Sizes of the caller-owned buffers a cache with this configuration needs.
+ *   kv_bytes   K and V of every layer:
+ *              2 * n_layers * n_kv_heads * head_dim * C * bytes_per_elem * batch,
+ *              the size model of [KVC] "O gargalo de memória do KV Cache em
+ *              contextos longos" and [KVL] "01 · Conceito" with C retained slots.
+ *              Layout: for layer l, K at l*2*P and V at (l*2+1)*P bytes, each
+ *              [batch][n_kv_heads][C][head_dim], P = kv_bytes / (2 * n_layers).
+ *   aux_bytes  Per-cache state: the float32 cos/sin table of the in-cache
+ *              positions (SINK_RING with rope), per-slot token positions and
+ *              scores and per-(layer, row, head) victim slots (H2O).  Opaque.
+ *   ws_bytes   Workspace one lcd_decode_attn call needs (split partials, and
+ *              logits for H2O).  Opaque; may be reused across calls that are
+ *              ordered on one stream.
+ * Any output pointer may be NULL.  Pure host function, no HIP call. */
+lcd_status lcd_cache_sizes(const lcd_cache_config* cfg, uint64_t* kv_bytes, uint64_t* aux_bytes,
+                           uint64_t* ws_bytes);
+
+/* kv_cache_init: bind a cache to caller memory ([KVC] "Attention Sinks e o
+ * StreamingLLM..." two contiguous partitions; [KVL] "01 · Conceito" KV cache).
+ * kv_mem (device, >= kv_bytes) holds K/V; aux_mem (device, >= aux_bytes, may be
+ * NULL when aux_bytes is 0) is initialised on `stream` (cos/sin table computed
+ * on the device in float64 and rounded to float32; H2O state cleared).  The
+ * K/V contents are not touched: no slot is attended before it is written.  On
+ * success *out receives a new handle with every layer empty. */
+lcd_status lcd_kv_cache_init(const lcd_cache_config* cfg, void* kv_mem, uint64_t kv_bytes, void* aux_mem,
+                             uint64_t aux_bytes, void* stream, lcd_cache** out);
+
+/* Free the host handle (never touches device memory).  NULL is ignored. */
+void lcd_kv_cache_destroy(lcd_cache* cache);
+
+/* kv_append: write the K/V of n_new new tokens of one layer ([KVL] "01 ·
+ * Conceito": each step appends its own k_t, v_t; [SINK] "como funciona": keys are
+ * stored before rotation).
+ *   k, v   device, [batch][n_kv_heads][n_new][head_dim] in the cache dtype.
+ *   n_new  >= 1.  SINK_RING writes only the tokens that survive (the sinks among
+ *          them and the newest `window`), exactly as n_new single appends would.
+ *          APPEND requires tokens + n_new <= capacity (else LCD_ECAPACITY).  H2O
+ *          requires n_new == 1 (bulk state goes through lcd_kv_load); when the
+ *          cache is full the row overwrites the victim slot chosen on the device
+ *          by the previous lcd_decode_attn of this layer.
+ * Advances the layer's token counter by n_new. */
+lcd_status lcd_kv_append(lcd_cache* cache, int32_t layer, const void* k, const void* v, int32_t n_new,
+                         void* stream);
+
+/* decode_attn: one decode step of one layer ([KVL] "01 · Conceito": the newest
+ * query attends every cached key and mixes the cached values; [KVC] "O gargalo de
+ * memória...": a decode step reads the whole cache; [KVC] "Implementação
+ * prática...": the work is split along the sequence, FlashDecoding-style).
+ *   q    device, [batch][n_q_heads][head_dim], cache dtype: the query of the token
+ *        appended last (its in-cache position is the newest one).
+ *   out  device float32 [batch][n_q_heads][head_dim].
+ *   ws   device workspace of ws_bytes >= lcd_cache_sizes' ws_bytes.
+ * Attends all retained tokens of the layer, including the newest.  SINK_RING with
+ * rope rotates q and every key at its in-cache position.  H2O also adds the step's
+ * attention weights to the slot scores and selects the next victim; call it once
+ * after each append.  LCD_EINVAL if the layer holds no token. */
+lcd_status lcd_decode_attn(lcd_cache* cache, int32_t layer, const void* q, float* out, void* ws,
+                           uint64_t ws_bytes, void* stream);
+
+/* Host-side queries (pure host functions, no HIP call; -1 on invalid arguments).
+ *   lcd_kv_tokens   tokens appended so far to `layer` (int64 counter).
+ *   lcd_kv_filled   slots currently holding a token (<= capacity).
+ *   lcd_kv_slot_of  SINK_RING: slot that holds / held token `token`; APPEND:
+ *                   the row index of the token-th appended row; H2O: -1 (the slot
+ *                   is chosen on the device).
+ *   lcd_kv_rank_of  SINK_RING: in-cache position of the token in `slot` right now
+ *                   (-1 if the slot is empty); others: -1. */
+int64_t lcd_kv_tokens(const lcd_cache* cache, int32_t layer);
+int64_t lcd_kv_filled(const lcd_cache* cache, int32_t layer);
+int64_t lcd_kv_slot_of(const lcd_cache* cache, int32_t layer, int64_t token);
+int64_t lcd_kv_rank_of(const lcd_cache* cache, int32_t layer, int64_t slot);
+
+/* Device addresses of one layer's state, for callers that fill a cache in place
+ * (e.g. SnapKV output written straight into an APPEND cache).  k/v point at
+ * [batch][n_kv_heads][C][head_dim]; pos (int32) and score (float32) at
+ * [batch][n_kv_heads][C] (H2O only, else NULL).  Any output may be NULL. */
+lcd_status lcd_kv_layer_view(const lcd_cache* cache, int32_t layer, void** k, void** v, int32_t** pos,
+                             float** score);
+
+/* Seed a layer whose first n rows (per batch row and KV head) were already
+ * written in place through lcd_kv_layer_view: sets the fill count to n and the
+ * token counter to next_token.  APPEND and H2O only (n <= capacity).  For H2O the
+ * caller has also written pos and score of those rows.  Enqueues nothing. */
+lcd_status lcd_kv_set_filled(lcd_cache* cache, int32_t layer, int32_t n, int64_t next_token);
+
+/* SnapKV ---------------------------------------------------------------------
+ * [KVC] "SnapKV e a seleção de contexto no prefill": at the end of prefill each
+ * head keeps the prompt positions with the highest smoothed observation-window
+ * score.  Steps: (1) the last l_obs prompt queries attend the prompt causally
+ * (row t is prompt token N - l_obs + t and sees keys 0..N - l_obs + t), softmax
+ * over those keys; (2) s_i = mean over the rows of the weight of key i; (3) s
+ * over the prefix i < N - l_obs is pooled with a centred window of kernel_size
+ * (zero padding; average divides by kernel_size, max takes the maximum); (4) the
+ * k_keep prefix positions of highest pooled score are kept, ties to the lower
+ * index, decided on float32 scores.  The kept rows are the selected positions in
+ * ascending order followed by the observation window N - l_obs .. N - 1. */
+typedef struct lcd_snapkv_params {
+  int32_t batch;        /* >= 1                                                  */
+  int32_t n_heads;      /* >= 1 (q_obs, k and v have the same head count)         */
+  int32_t head_dim;     /* D in {64, 128, 256}                                    */
+  int32_t n_prompt;     /* N >= 1                                                 */
+  int32_t l_obs;        /* 1 <= l_obs <= min(N, 64)                               */
+  int32_t kernel_size;  /* odd, 1 <= kernel_size <= 31                            */
+  int32_t k_keep;       /* 0 <= k_keep <= N - l_obs                               */
+  int32_t pool;         /* 0 = average, 1 = max                                   */
+  int32_t dtype;        /* LCD_BF16 (the scoring contraction runs on bf16 MFMA)   */
+  int32_t out_rows;     /* rows per head of k_out / v_out / idx_out; 0 selects
+                           k_keep + l_obs; otherwise >= k_keep + l_obs (rows past
+                           k_keep + l_obs are left untouched)                     */
+  double scale;         /* logit scale; 0 selects 1/sqrt(head_dim)                */
+} lcd_snapkv_params;
+
+/* Workspace bytes lcd_snapkv_compress needs for these parameters. */
+lcd_status lcd_snapkv_sizes(const lcd_snapkv_params* p, uint64_t* ws_bytes);
+
+/* snapkv_compress:
+ *   q_obs       device [batch][n_heads][l_obs][head_dim]: queries of the last l_obs
+ *               prompt tokens (already position-encoded, used as given).
+ *   k, v        device [batch][n_heads][N][head_dim] (position-encoded keys).
+ *   k_out,v_out device [batch][n_heads][out_rows][head_dim]: kept rows.
+ *   idx_out     device int32 [batch][n_heads][out_rows]: kept prompt positions.
+ *   scores_out  device float32 [batch][n_heads][N - l_obs] pooled scores, or NULL.
+ *   ws          device workspace of ws_bytes >= lcd_snapkv_sizes.
+ * All buffers distinct (no aliasing between inputs and outputs). */
+lcd_status lcd_snapkv_compress(const lcd_snapkv_params* p, const void* q_obs, const void* k, const void* v,
+                               void* k_out, void* v_out, int32_t* idx_out, float* scores_out, void* ws,
+                               uint64_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LCD_H */

@@ -1,0 +1,36 @@
+"""Compressed-KV decode attention on AMD MI355X (gfx950).
+
+Thin Python binding of the C ABI in ``include/lcd.h`` (``liblcd.so``): argument
+marshalling only.  torch supplies device memory and streams; every step of the
+decode and compression path runs in the library's HIP kernels.  Importing this
+package fails loudly if the library has not been built
+(``python long_context_decode_amd/build.py``).
+"""
+from ._lib import (  # noqa: F401
+    LCD_APPEND,
+    LCD_BF16,
+    LCD_F32,
+    LCD_H2O,
+    LCD_SINK_RING,
+    LIB_PATH,
+    KVCache,
+    LcdError,
+    abi_version,
+    cache_config,
+    cache_sizes,
+    decode_attn,
+    kv_append,
+    kv_cache_destroy,
+    kv_cache_init,
+    kv_filled,
+    kv_layer_view,
+    kv_rank_of,
+    kv_set_filled,
+    kv_slot_of,
+    kv_tokens,
+    last_error,
+    lib,
+    snapkv_compress,
+    snapkv_params,
+    snapkv_sizes,
+)

@@ -1,0 +1,242 @@
+"""ctypes binding of liblcd.so.  Names follow the C entry points without the
+``lcd_`` prefix.  Tensor arguments are torch tensors (device memory); they are
+passed as raw pointers after dtype/shape/contiguity checks.  The library itself
+validates everything again and never allocates device memory.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+# LCD_LIB_PATH selects another build of the same library (e.g. a kernel variant).
+LIB_PATH = os.environ.get("LCD_LIB_PATH") or os.path.join(PKG, "liblcd.so")
+
+LCD_F32, LCD_BF16 = 0, 1
+LCD_SINK_RING, LCD_APPEND, LCD_H2O = 0, 1, 2
+
+_STATUS = {0: "LCD_OK", 1: "LCD_EINVAL", 2: "LCD_ESHAPE", 3: "LCD_EALIGN", 4: "LCD_ECAPACITY",
+           5: "LCD_ESIZE", 6: "LCD_EHIP", 7: "LCD_EUNSUPPORTED"}
+
+
+class LcdError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+        self.name = _STATUS.get(status, str(status))
+
+
+class CacheConfig(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_layers", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("policy", ctypes.c_int32), ("n_sink", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("capacity", ctypes.c_int32), ("n_recent", ctypes.c_int32), ("rope", ctypes.c_int32),
+                ("rope_base", ctypes.c_double), ("scale", ctypes.c_double)]
+
+
+class SnapkvParams(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("n_prompt", ctypes.c_int32), ("l_obs", ctypes.c_int32), ("kernel_size", ctypes.c_int32),
+                ("k_keep", ctypes.c_int32), ("pool", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("out_rows", ctypes.c_int32), ("scale", ctypes.c_double)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python long_context_decode_amd/build.py` "
+            "(there is no fallback implementation)")
+    return ctypes.CDLL(LIB_PATH)
+
+
+lib = _load()
+
+_P = ctypes.c_void_p
+_U64 = ctypes.c_uint64
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_S = ctypes.c_int
+
+_SIGS = {
+    "lcd_abi_version": (_S, []),
+    "lcd_last_error": (ctypes.c_char_p, []),
+    "lcd_cache_sizes": (_S, [ctypes.POINTER(CacheConfig), ctypes.POINTER(_U64), ctypes.POINTER(_U64),
+                             ctypes.POINTER(_U64)]),
+    "lcd_kv_cache_init": (_S, [ctypes.POINTER(CacheConfig), _P, _U64, _P, _U64, _P, ctypes.POINTER(_P)]),
+    "lcd_kv_cache_destroy": (None, [_P]),
+    "lcd_kv_append": (_S, [_P, _I32, _P, _P, _I32, _P]),
+    "lcd_decode_attn": (_S, [_P, _I32, _P, _P, _P, _U64, _P]),
+    "lcd_kv_tokens": (_I64, [_P, _I32]),
+    "lcd_kv_filled": (_I64, [_P, _I32]),
+    "lcd_kv_slot_of": (_I64, [_P, _I32, _I64]),
+    "lcd_kv_rank_of": (_I64, [_P, _I32, _I64]),
+    "lcd_kv_layer_view": (_S, [_P, _I32, ctypes.POINTER(_P), ctypes.POINTER(_P), ctypes.POINTER(_P),
+                               ctypes.POINTER(_P)]),
+    "lcd_kv_set_filled": (_S, [_P, _I32, _I32, _I64]),
+    "lcd_snapkv_sizes": (_S, [ctypes.POINTER(SnapkvParams), ctypes.POINTER(_U64)]),
+    "lcd_snapkv_compress": (_S, [ctypes.POINTER(SnapkvParams), _P, _P, _P, _P, _P, _P, _P, _P, _U64, _P]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _f = getattr(lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+EXPORTED = tuple(_SIGS)
+
+
+def abi_version() -> int:
+    return lib.lcd_abi_version()
+
+
+def last_error() -> str:
+    return lib.lcd_last_error().decode()
+
+
+def _check(status: int):
+    if status != 0:
+        raise LcdError(status, last_error())
+
+
+def _ptr(t):
+    """Raw address of a torch tensor (or an int / None)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def cache_config(batch, n_q_heads, n_kv_heads, head_dim, dtype=LCD_BF16, policy=LCD_SINK_RING, n_layers=1,
+                 n_sink=0, window=0, capacity=0, n_recent=0, rope=0, rope_base=10000.0, scale=0.0):
+    return CacheConfig(batch, n_layers, n_q_heads, n_kv_heads, head_dim, dtype, policy, n_sink, window,
+                       capacity, n_recent, rope, rope_base, scale)
+
+
+def cache_sizes(cfg: CacheConfig):
+    kv, aux, ws = _U64(), _U64(), _U64()
+    _check(lib.lcd_cache_sizes(ctypes.byref(cfg), ctypes.byref(kv), ctypes.byref(aux), ctypes.byref(ws)))
+    return kv.value, aux.value, ws.value
+
+
+def kv_cache_init(cfg: CacheConfig, kv_mem, kv_bytes, aux_mem, aux_bytes, stream=None):
+    h = _P()
+    _check(lib.lcd_kv_cache_init(ctypes.byref(cfg), _ptr(kv_mem), kv_bytes, _ptr(aux_mem), aux_bytes,
+                                 _stream(stream), ctypes.byref(h)))
+    return h
+
+
+def kv_cache_destroy(h):
+    lib.lcd_kv_cache_destroy(h)
+
+
+def kv_append(h, layer, k, v, n_new, stream=None):
+    _check(lib.lcd_kv_append(h, layer, _ptr(k), _ptr(v), n_new, _stream(stream)))
+
+
+def decode_attn(h, layer, q, out, ws, ws_bytes, stream=None):
+    _check(lib.lcd_decode_attn(h, layer, _ptr(q), _ptr(out), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def kv_tokens(h, layer):
+    return lib.lcd_kv_tokens(h, layer)
+
+
+def kv_filled(h, layer):
+    return lib.lcd_kv_filled(h, layer)
+
+
+def kv_slot_of(h, layer, token):
+    return lib.lcd_kv_slot_of(h, layer, token)
+
+
+def kv_rank_of(h, layer, slot):
+    return lib.lcd_kv_rank_of(h, layer, slot)
+
+
+def kv_layer_view(h, layer):
+    k, v, pos, score = _P(), _P(), _P(), _P()
+    _check(lib.lcd_kv_layer_view(h, layer, ctypes.byref(k), ctypes.byref(v), ctypes.byref(pos),
+                                 ctypes.byref(score)))
+    return k.value, v.value, pos.value, score.value
+
+
+def kv_set_filled(h, layer, n, next_token):
+    _check(lib.lcd_kv_set_filled(h, layer, n, next_token))
+
+
+def snapkv_params(batch, n_heads, head_dim, n_prompt, l_obs, kernel_size, k_keep, pool=0, dtype=LCD_BF16,
+                  out_rows=0, scale=0.0):
+    return SnapkvParams(batch, n_heads, head_dim, n_prompt, l_obs, kernel_size, k_keep, pool, dtype, out_rows,
+                        scale)
+
+
+def snapkv_sizes(p: SnapkvParams) -> int:
+    ws = _U64()
+    _check(lib.lcd_snapkv_sizes(ctypes.byref(p), ctypes.byref(ws)))
+    return ws.value
+
+
+def snapkv_compress(p: SnapkvParams, q_obs, k, v, k_out, v_out, idx_out, scores_out, ws, ws_bytes, stream=None):
+    _check(lib.lcd_snapkv_compress(ctypes.byref(p), _ptr(q_obs), _ptr(k), _ptr(v), _ptr(k_out), _ptr(v_out),
+                                   _ptr(idx_out), _ptr(scores_out), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+class KVCache:
+    """A cache whose K/V, auxiliary state and decode workspace live in torch tensors.
+
+    Allocation only; every operation calls the C ABI.
+    """
+
+    def __init__(self, cfg: CacheConfig, device="cuda", stream=None):
+        import torch
+
+        self.cfg = cfg
+        self.kv_bytes, self.aux_bytes, self.ws_bytes = cache_sizes(cfg)
+        self.kv_mem = torch.empty(max(self.kv_bytes, 16), dtype=torch.uint8, device=device)
+        self.aux_mem = torch.empty(max(self.aux_bytes, 16), dtype=torch.uint8, device=device)
+        self.ws = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=device)
+        self.handle = kv_cache_init(cfg, self.kv_mem, self.kv_bytes, self.aux_mem if self.aux_bytes else None,
+                                    self.aux_bytes, stream)
+
+    def append(self, layer, k, v, stream=None):
+        kv_append(self.handle, layer, k, v, k.shape[-2], stream)
+
+    def decode(self, layer, q, out, stream=None):
+        decode_attn(self.handle, layer, q, out, self.ws, self.ws_bytes, stream)
+
+    def layer_tensors(self, layer):
+        """(K, V) views of one layer as [B][H_kv][C][D] torch tensors."""
+        import torch
+
+        c = self.cfg
+        C = c.n_sink + c.window if c.policy == LCD_SINK_RING else c.capacity
+        dt = torch.float32 if c.dtype == LCD_F32 else torch.bfloat16
+        es = 4 if c.dtype == LCD_F32 else 2
+        per = c.batch * c.n_kv_heads * C * c.head_dim
+        base = layer * 2 * per * es
+        kv = self.kv_mem[base: base + 2 * per * es].view(dt)
+        return kv[:per].view(c.batch, c.n_kv_heads, C, c.head_dim), kv[per:].view(c.batch, c.n_kv_heads, C,
+                                                                                   c.head_dim)
+
+    def close(self):
+        if self.handle:
+            kv_cache_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

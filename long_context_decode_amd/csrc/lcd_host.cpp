@@ -1,0 +1,559 @@
+// Host side of the C ABI declared in include/lcd.h: validation, memory layout,
+// per-layer token bookkeeping and kernel launches.  Every check runs before any
+// HIP call, so the validation paths work (and are tested) on machines without a
+// GPU.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "lcd.h"
+#include "lcd_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+lcd_status fail(lcd_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+lcd_status ok() {
+  g_err.clear();
+  return LCD_OK;
+}
+
+lcd_status hip_fail(hipError_t e, const char* what) {
+  return fail(LCD_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+uint64_t align256(uint64_t x) { return (x + 255u) & ~uint64_t(255); }
+
+// Checked product of non-negative factors; false on overflow.
+bool mul_ok(uint64_t* acc, uint64_t f) { return !__builtin_mul_overflow(*acc, f, acc); }
+
+constexpr int64_t kMaxSlots = int64_t(1) << 24;
+constexpr int kTargetWorkgroups = 2048;  // decode grid size aimed for (8 per CU on 256 CUs)
+
+int env_int(const char* name, int dflt) {
+  const char* s = std::getenv(name);
+  if (!s || !*s) return dflt;
+  return std::atoi(s);
+}
+
+struct Layout {
+  int C = 0, esize = 0, G = 0;
+  uint64_t layer_bytes = 0;  // one of K or V of one layer
+  uint64_t kv_bytes = 0;
+  uint64_t aux_bytes = 0, off_cos = 0, off_sin = 0, off_pos = 0, off_score = 0, off_victim = 0, off_arrive = 0;
+  uint64_t ws_bytes = 0, ws_off_ml = 0, ws_off_logits = 0;
+  int max_splits = 0, chunk_cap = 0, chunk_force = 0;
+};
+
+// Largest split chunk whose LDS footprint stays within 64 KiB.
+int chunk_cap_for(int G, int D) {
+  const long floats = 16384 - 4L * G - 4L * G * D;
+  long c = floats / G;
+  c = (c / 64) * 64;
+  if (c > lcd::kMaxChunk) c = lcd::kMaxChunk;
+  return (int)c;
+}
+
+lcd_status check_config(const lcd_cache_config* c, Layout* L) {
+  if (!c) return fail(LCD_EINVAL, "config is NULL");
+  if (c->batch < 1 || c->n_layers < 1 || c->n_kv_heads < 1 || c->n_q_heads < 1)
+    return fail(LCD_ESHAPE, "batch, n_layers, n_q_heads and n_kv_heads must be >= 1");
+  if (c->n_q_heads % c->n_kv_heads)
+    return fail(LCD_ESHAPE, "n_q_heads (%d) must be a multiple of n_kv_heads (%d)", c->n_q_heads, c->n_kv_heads);
+  const int G = c->n_q_heads / c->n_kv_heads;
+  if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256)
+    return fail(LCD_ESHAPE, "head_dim %d not in {64, 128, 256}", c->head_dim);
+  if (c->dtype != LCD_F32 && c->dtype != LCD_BF16) return fail(LCD_EINVAL, "unknown dtype %d", c->dtype);
+  if (!lcd::decode_supported(c->dtype, c->head_dim, G))
+    return fail(LCD_EUNSUPPORTED, "query heads per KV head %d not in {1, 2, 4, 6, 8}", G);
+  int64_t C = 0;
+  switch (c->policy) {
+    case LCD_SINK_RING:
+      if (c->n_sink < 0 || c->window < 1) return fail(LCD_ESHAPE, "need n_sink >= 0 and window >= 1");
+      C = (int64_t)c->n_sink + c->window;
+      break;
+    case LCD_APPEND:
+    case LCD_H2O:
+      if (c->capacity < 1) return fail(LCD_ESHAPE, "capacity must be >= 1");
+      C = c->capacity;
+      if (c->policy == LCD_H2O && (c->n_recent < 1 || c->n_recent > c->capacity))
+        return fail(LCD_ESHAPE, "H2O needs 1 <= n_recent <= capacity");
+      break;
+    default:
+      return fail(LCD_EINVAL, "unknown policy %d", c->policy);
+  }
+  if (C > kMaxSlots) return fail(LCD_ESHAPE, "capacity %lld exceeds %lld slots", (long long)C, (long long)kMaxSlots);
+  if (c->rope != 0 && c->rope != 1) return fail(LCD_EINVAL, "rope must be 0 or 1");
+  if (c->rope == 1 && c->policy != LCD_SINK_RING)
+    return fail(LCD_EUNSUPPORTED, "rotation at in-cache positions is defined for the sink + window cache only");
+  if (c->rope == 1 && !(std::isfinite(c->rope_base) && c->rope_base > 1.0))
+    return fail(LCD_EINVAL, "rope_base must be finite and > 1");
+  if (!(std::isfinite(c->scale) && c->scale >= 0.0)) return fail(LCD_EINVAL, "scale must be finite and >= 0");
+
+  L->C = (int)C;
+  L->esize = c->dtype == LCD_F32 ? 4 : 2;
+  L->G = G;
+  uint64_t lb = (uint64_t)c->batch;
+  if (!mul_ok(&lb, c->n_kv_heads) || !mul_ok(&lb, (uint64_t)C) || !mul_ok(&lb, c->head_dim) ||
+      !mul_ok(&lb, L->esize))
+    return fail(LCD_ESIZE, "cache size overflows 64 bits");
+  uint64_t kv = lb;
+  if (!mul_ok(&kv, 2) || !mul_ok(&kv, c->n_layers)) return fail(LCD_ESIZE, "cache size overflows 64 bits");
+  L->layer_bytes = lb;
+  L->kv_bytes = kv;
+
+  // arrival counters of the split merge: one per (layer, batch row, KV head)
+  uint64_t aux = align256((uint64_t)c->n_layers * c->batch * c->n_kv_heads * sizeof(int32_t));
+  L->off_arrive = 0;
+  if (c->rope == 1) {
+    const uint64_t tab = (uint64_t)C * (c->head_dim / 2) * sizeof(float);
+    L->off_cos = aux;
+    aux = align256(aux + tab);
+    L->off_sin = aux;
+    aux = align256(aux + tab);
+  }
+  if (c->policy == LCD_H2O) {
+    const uint64_t per = (uint64_t)c->n_layers * c->batch * c->n_kv_heads * C;
+    L->off_pos = aux;
+    aux = align256(aux + per * sizeof(int32_t));
+    L->off_score = aux;
+    aux = align256(aux + per * sizeof(float));
+    L->off_victim = aux;
+    aux = align256(aux + (uint64_t)c->n_layers * c->batch * c->n_kv_heads * sizeof(int32_t));
+  }
+  L->aux_bytes = aux;
+
+  L->chunk_cap = chunk_cap_for(G, c->head_dim);
+  const int force = env_int("LCD_DECODE_CHUNK", 0);
+  L->chunk_force = (force >= 64 && force % 64 == 0 && force <= L->chunk_cap) ? force : 0;
+  const int64_t bg = (int64_t)c->batch * c->n_kv_heads;
+  const int64_t target = env_int("LCD_DECODE_TARGET_WGS", kTargetWorkgroups);
+  int64_t smax = (target + bg - 1) / bg;
+  const int64_t by_cap = (C + L->chunk_cap - 1) / L->chunk_cap;
+  if (smax < by_cap) smax = by_cap;
+  if (L->chunk_force) smax = (C + L->chunk_force - 1) / L->chunk_force;
+  const int64_t by_min = (C + 63) / 64;
+  if (smax > by_min) smax = by_min;
+  if (smax < 1) smax = 1;
+  L->max_splits = (int)smax;
+
+  const uint64_t bhq = (uint64_t)c->batch * c->n_q_heads;
+  uint64_t ws = align256((uint64_t)smax * bhq * c->head_dim * sizeof(float));
+  L->ws_off_ml = ws;
+  ws = align256(ws + (uint64_t)smax * bhq * 2 * sizeof(float));
+  L->ws_off_logits = ws;
+  if (c->policy == LCD_H2O) ws = align256(ws + bhq * (uint64_t)C * sizeof(float));
+  L->ws_bytes = ws;
+  return LCD_OK;
+}
+
+// Split plan for n attended slots: chunk is a multiple of 64, splits = ceil(n / chunk).
+void plan_splits(const Layout& L, int n, int* n_splits, int* chunk) {
+  int ch;
+  if (L.chunk_force) {
+    ch = L.chunk_force;
+  } else {
+    int s = L.max_splits;
+    const int by_min = (n + 63) / 64;
+    if (s > by_min) s = by_min;
+    if (s < 1) s = 1;
+    ch = (n + s - 1) / s;
+    ch = ((ch + 63) / 64) * 64;
+    if (ch > L.chunk_cap) ch = L.chunk_cap;
+  }
+  *chunk = ch;
+  *n_splits = (n + ch - 1) / ch;
+}
+
+}  // namespace
+
+struct lcd_cache {
+  lcd_cache_config cfg;
+  Layout L;
+  char* kv = nullptr;
+  char* aux = nullptr;
+  std::vector<int64_t> tokens;  // tokens appended per layer
+  std::vector<int64_t> filled;  // slots holding a token per layer
+  float qscale = 0.f;
+
+  char* k_layer(int l) const { return kv + (uint64_t)l * 2 * L.layer_bytes; }
+  char* v_layer(int l) const { return k_layer(l) + L.layer_bytes; }
+  float* cos_t() const { return cfg.rope ? reinterpret_cast<float*>(aux + L.off_cos) : nullptr; }
+  float* sin_t() const { return cfg.rope ? reinterpret_cast<float*>(aux + L.off_sin) : nullptr; }
+  uint64_t per_layer_slots() const { return (uint64_t)cfg.batch * cfg.n_kv_heads * L.C; }
+  int32_t* pos(int l) const {
+    return cfg.policy == LCD_H2O ? reinterpret_cast<int32_t*>(aux + L.off_pos) + l * per_layer_slots() : nullptr;
+  }
+  float* score(int l) const {
+    return cfg.policy == LCD_H2O ? reinterpret_cast<float*>(aux + L.off_score) + l * per_layer_slots() : nullptr;
+  }
+  int32_t* arrivals(int l) const {
+    return reinterpret_cast<int32_t*>(aux + L.off_arrive) + (uint64_t)l * cfg.batch * cfg.n_kv_heads;
+  }
+  int32_t* victim(int l) const {
+    return cfg.policy == LCD_H2O
+               ? reinterpret_cast<int32_t*>(aux + L.off_victim) + (uint64_t)l * cfg.batch * cfg.n_kv_heads
+               : nullptr;
+  }
+};
+
+extern "C" {
+
+int lcd_abi_version(void) { return LCD_ABI_VERSION; }
+
+const char* lcd_last_error(void) { return g_err.c_str(); }
+
+lcd_status lcd_cache_sizes(const lcd_cache_config* cfg, uint64_t* kv_bytes, uint64_t* aux_bytes,
+                           uint64_t* ws_bytes) {
+  Layout L;
+  const lcd_status st = check_config(cfg, &L);
+  if (st) return st;
+  if (kv_bytes) *kv_bytes = L.kv_bytes;
+  if (aux_bytes) *aux_bytes = L.aux_bytes;
+  if (ws_bytes) *ws_bytes = L.ws_bytes;
+  return ok();
+}
+
+lcd_status lcd_kv_cache_init(const lcd_cache_config* cfg, void* kv_mem, uint64_t kv_bytes, void* aux_mem,
+                             uint64_t aux_bytes, void* stream, lcd_cache** out) {
+  if (!out) return fail(LCD_EINVAL, "out is NULL");
+  Layout L;
+  const lcd_status st = check_config(cfg, &L);
+  if (st) return st;
+  if (!kv_mem) return fail(LCD_EINVAL, "kv_mem is NULL");
+  if (!aligned16(kv_mem)) return fail(LCD_EALIGN, "kv_mem is not 16-byte aligned");
+  if (kv_bytes < L.kv_bytes)
+    return fail(LCD_ESIZE, "kv_bytes %llu < required %llu", (unsigned long long)kv_bytes,
+                (unsigned long long)L.kv_bytes);
+  if (!aux_mem) return fail(LCD_EINVAL, "aux_mem is NULL but %llu bytes are required",
+                            (unsigned long long)L.aux_bytes);
+  if (!aligned16(aux_mem)) return fail(LCD_EALIGN, "aux_mem is not 16-byte aligned");
+  if (aux_bytes < L.aux_bytes)
+    return fail(LCD_ESIZE, "aux_bytes %llu < required %llu", (unsigned long long)aux_bytes,
+                (unsigned long long)L.aux_bytes);
+  lcd_cache* c = new (std::nothrow) lcd_cache();
+  if (!c) return fail(LCD_EINVAL, "out of host memory");
+  c->cfg = *cfg;
+  c->L = L;
+  c->kv = static_cast<char*>(kv_mem);
+  c->aux = static_cast<char*>(aux_mem);
+  c->tokens.assign(cfg->n_layers, 0);
+  c->filled.assign(cfg->n_layers, 0);
+  const double scale = cfg->scale > 0 ? cfg->scale : 1.0 / std::sqrt((double)cfg->head_dim);
+  c->qscale = (float)(scale * 1.4426950408889634074);  // scale * log2(e), rounded once
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = lcd::launch_fill_i32(c->arrivals(0), 0, (int64_t)cfg->n_layers * cfg->batch * cfg->n_kv_heads, s);
+  if (e == hipSuccess && cfg->rope) e = lcd::launch_rope_table(c->cos_t(), c->sin_t(), L.C, cfg->head_dim, cfg->rope_base, s);
+  if (e == hipSuccess && cfg->policy == LCD_H2O) {
+    const int64_t n = (int64_t)cfg->n_layers * c->per_layer_slots();
+    e = lcd::launch_fill_i32(c->pos(0), -1, n, s);
+    if (e == hipSuccess) e = lcd::launch_fill_f32(c->score(0), 0.f, n, s);
+    if (e == hipSuccess) e = lcd::launch_fill_i32(c->victim(0), 0, (int64_t)cfg->n_layers * cfg->batch * cfg->n_kv_heads, s);
+  }
+  if (e != hipSuccess) {
+    delete c;
+    return hip_fail(e, "kv_cache_init launch");
+  }
+  *out = c;
+  return ok();
+}
+
+void lcd_kv_cache_destroy(lcd_cache* cache) { delete cache; }
+
+static lcd_status check_layer(const lcd_cache* c, int32_t layer) {
+  if (!c) return fail(LCD_EINVAL, "cache is NULL");
+  if (layer < 0 || layer >= c->cfg.n_layers)
+    return fail(LCD_EINVAL, "layer %d out of range [0, %d)", layer, c->cfg.n_layers);
+  return LCD_OK;
+}
+
+lcd_status lcd_kv_append(lcd_cache* c, int32_t layer, const void* k, const void* v, int32_t n_new, void* stream) {
+  lcd_status st = check_layer(c, layer);
+  if (st) return st;
+  if (!k || !v) return fail(LCD_EINVAL, "k or v is NULL");
+  if (!aligned16(k) || !aligned16(v)) return fail(LCD_EALIGN, "k or v is not 16-byte aligned");
+  if (n_new < 1) return fail(LCD_EINVAL, "n_new must be >= 1");
+  const lcd_cache_config& cfg = c->cfg;
+  const int C = c->L.C;
+  const int64_t t0 = c->tokens[layer];
+  lcd::AppendParams p{};
+  p.k_in = static_cast<const char*>(k);
+  p.v_in = static_cast<const char*>(v);
+  p.k_cache = c->k_layer(layer);
+  p.v_cache = c->v_layer(layer);
+  p.BHkv = cfg.batch * cfg.n_kv_heads;
+  p.C = C;
+  p.n_new = n_new;
+  p.row_bytes = cfg.head_dim * c->L.esize;
+  p.S = cfg.n_sink;
+  p.W = cfg.window > 0 ? cfg.window : 1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int64_t new_filled = c->filled[layer];
+  if (cfg.policy == LCD_SINK_RING) {
+    const int64_t S = cfg.n_sink, W = cfg.window;
+    const int64_t t_end = t0 + n_new - 1;
+    // sinks among the new tokens
+    const int64_t sink_end = std::min<int64_t>(S, t0 + n_new);
+    const int64_t n_sink_rows = sink_end > t0 ? sink_end - t0 : 0;
+    // newest W tokens that are not sinks
+    const int64_t a_first = std::max<int64_t>({S, t_end - W + 1, t0});
+    const int64_t n_ring_rows = t_end >= a_first ? t_end - a_first + 1 : 0;
+    hipError_t e = hipSuccess;
+    if (n_sink_rows > 0) {
+      lcd::AppendParams q = p;
+      q.r0 = 0;
+      q.n_rows = (int)n_sink_rows;
+      q.r_split = (int)n_sink_rows;
+      q.slot_lin = (int)t0;
+      e = lcd::launch_append(q, s);
+    }
+    if (e == hipSuccess && n_ring_rows > 0) {
+      lcd::AppendParams q = p;
+      q.r0 = (int)(a_first - t0);
+      q.n_rows = (int)n_ring_rows;
+      q.r_split = q.r0;
+      q.ring_off = (int)((a_first - S) % W);
+      e = lcd::launch_append(q, s);
+    }
+    if (e != hipSuccess) return hip_fail(e, "kv_append launch");
+    new_filled = std::min<int64_t>(t0 + n_new, C);
+  } else if (cfg.policy == LCD_APPEND) {
+    if (c->filled[layer] + n_new > C)
+      return fail(LCD_ECAPACITY, "append of %d rows to %lld filled of capacity %d", n_new,
+                  (long long)c->filled[layer], C);
+    p.r0 = 0;
+    p.n_rows = n_new;
+    p.r_split = n_new;
+    p.slot_lin = (int)c->filled[layer];
+    const hipError_t e = lcd::launch_append(p, s);
+    if (e != hipSuccess) return hip_fail(e, "kv_append launch");
+    new_filled = c->filled[layer] + n_new;
+  } else {  // H2O
+    if (n_new != 1) return fail(LCD_EINVAL, "H2O appends one token per call (got %d)", n_new);
+    if (t0 > INT32_MAX) return fail(LCD_ECAPACITY, "H2O token positions are int32");
+    p.h2o = 1;
+    p.fill = (int)c->filled[layer];
+    p.victim = c->victim(layer);
+    p.pos = c->pos(layer);
+    p.score = c->score(layer);
+    p.token = t0;
+    const hipError_t e = lcd::launch_append(p, s);
+    if (e != hipSuccess) return hip_fail(e, "kv_append launch");
+    new_filled = std::min<int64_t>(c->filled[layer] + 1, C);
+  }
+  c->tokens[layer] = t0 + n_new;
+  c->filled[layer] = new_filled;
+  return ok();
+}
+
+lcd_status lcd_decode_attn(lcd_cache* c, int32_t layer, const void* q, float* out, void* ws, uint64_t ws_bytes,
+                           void* stream) {
+  lcd_status st = check_layer(c, layer);
+  if (st) return st;
+  if (!q || !out || !ws) return fail(LCD_EINVAL, "q, out or ws is NULL");
+  if (!aligned16(q) || !aligned16(out) || !aligned16(ws)) return fail(LCD_EALIGN, "q, out or ws not 16-byte aligned");
+  if (ws_bytes < c->L.ws_bytes)
+    return fail(LCD_ESIZE, "ws_bytes %llu < required %llu", (unsigned long long)ws_bytes,
+                (unsigned long long)c->L.ws_bytes);
+  if (c->tokens[layer] < 1 || c->filled[layer] < 1) return fail(LCD_EINVAL, "layer %d holds no token", layer);
+  const lcd_cache_config& cfg = c->cfg;
+  const Layout& L = c->L;
+  const int n = (int)c->filled[layer];
+  lcd::DecodeParams p{};
+  p.k = c->k_layer(layer);
+  p.v = c->v_layer(layer);
+  p.q = q;
+  p.cos_t = c->cos_t();
+  p.sin_t = c->sin_t();
+  char* w = static_cast<char*>(ws);
+  p.part_o = reinterpret_cast<float*>(w);
+  p.part_ml = reinterpret_cast<float*>(w + L.ws_off_ml);
+  p.logits = cfg.policy == LCD_H2O ? reinterpret_cast<float*>(w + L.ws_off_logits) : nullptr;
+  p.B = cfg.batch;
+  p.Hq = cfg.n_q_heads;
+  p.Hkv = cfg.n_kv_heads;
+  p.C = L.C;
+  p.n = n;
+  plan_splits(L, n, &p.n_splits, &p.chunk);
+  p.qscale = c->qscale;
+  int mode = lcd::kModePlain;
+  if (cfg.rope) {
+    mode = lcd::kModeRope;
+    const int64_t t = c->tokens[layer] - 1;
+    p.S = cfg.n_sink;
+    p.W = cfg.window;
+    p.full = (t + 1 > L.C) ? 1 : 0;
+    p.ring_head = p.full ? (int)((t - cfg.window + 1 - cfg.n_sink) % cfg.window) : 0;
+    p.q_rank = n - 1;
+  } else if (cfg.policy == LCD_H2O) {
+    mode = lcd::kModePlainLogits;
+  }
+  p.out = out;
+  p.arrivals = c->arrivals(layer);
+  if (cfg.policy == LCD_H2O) {
+    p.score = c->score(layer);
+    p.pos = c->pos(layer);
+    p.victim = c->victim(layer);
+    p.pick_victim = n == L.C ? 1 : 0;
+    p.max_pos = c->tokens[layer] - cfg.n_recent;  // next token id minus the protected count
+  }
+  const hipError_t e =
+      lcd::launch_decode_split(cfg.dtype, cfg.head_dim, L.G, mode, p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return ok();
+}
+
+int64_t lcd_kv_tokens(const lcd_cache* c, int32_t layer) {
+  if (check_layer(c, layer)) return -1;
+  return c->tokens[layer];
+}
+
+int64_t lcd_kv_filled(const lcd_cache* c, int32_t layer) {
+  if (check_layer(c, layer)) return -1;
+  return c->filled[layer];
+}
+
+int64_t lcd_kv_slot_of(const lcd_cache* c, int32_t layer, int64_t token) {
+  if (check_layer(c, layer) || token < 0) return -1;
+  const lcd_cache_config& cfg = c->cfg;
+  if (cfg.policy == LCD_SINK_RING) {
+    if (token < cfg.n_sink) return token;
+    return cfg.n_sink + (token - cfg.n_sink) % cfg.window;
+  }
+  if (cfg.policy == LCD_APPEND) return token < c->filled[layer] ? token : -1;
+  return -1;
+}
+
+int64_t lcd_kv_rank_of(const lcd_cache* c, int32_t layer, int64_t slot) {
+  if (check_layer(c, layer) || slot < 0) return -1;
+  const lcd_cache_config& cfg = c->cfg;
+  if (cfg.policy != LCD_SINK_RING) return -1;
+  const int64_t n = c->filled[layer];
+  if (slot >= n) return -1;
+  const int64_t t = c->tokens[layer] - 1;
+  if (t + 1 <= c->L.C || slot < cfg.n_sink) return slot;
+  const int64_t head = (t - cfg.window + 1 - cfg.n_sink) % cfg.window;
+  int64_t r = slot - cfg.n_sink - head;
+  if (r < 0) r += cfg.window;
+  return cfg.n_sink + r;
+}
+
+lcd_status lcd_kv_layer_view(const lcd_cache* c, int32_t layer, void** k, void** v, int32_t** pos, float** score) {
+  lcd_status st = check_layer(c, layer);
+  if (st) return st;
+  if (k) *k = c->k_layer(layer);
+  if (v) *v = c->v_layer(layer);
+  if (pos) *pos = c->pos(layer);
+  if (score) *score = c->score(layer);
+  return ok();
+}
+
+lcd_status lcd_kv_set_filled(lcd_cache* c, int32_t layer, int32_t n, int64_t next_token) {
+  lcd_status st = check_layer(c, layer);
+  if (st) return st;
+  if (c->cfg.policy == LCD_SINK_RING)
+    return fail(LCD_EUNSUPPORTED, "set_filled applies to APPEND and H2O caches");
+  if (n < 0 || n > c->L.C) return fail(LCD_ECAPACITY, "n=%d outside [0, %d]", n, c->L.C);
+  if (next_token < n) return fail(LCD_EINVAL, "next_token must be >= n");
+  c->filled[layer] = n;
+  c->tokens[layer] = next_token;
+  return ok();
+}
+
+lcd_status lcd_snapkv_sizes(const lcd_snapkv_params* p, uint64_t* ws_bytes);
+lcd_status lcd_snapkv_compress(const lcd_snapkv_params* p, const void* q_obs, const void* k, const void* v,
+                               void* k_out, void* v_out, int32_t* idx_out, float* scores_out, void* ws,
+                               uint64_t ws_bytes, void* stream);
+
+}  // extern "C"
+
+// ------------------------------------------------------------------------------ SnapKV
+namespace {
+
+lcd_status check_snapkv(const lcd_snapkv_params* p) {
+  if (!p) return fail(LCD_EINVAL, "params is NULL");
+  if (p->batch < 1 || p->n_heads < 1 || p->n_prompt < 1) return fail(LCD_ESHAPE, "batch, n_heads, n_prompt >= 1");
+  if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 256)
+    return fail(LCD_ESHAPE, "head_dim %d not in {64, 128, 256}", p->head_dim);
+  if (p->l_obs < 1 || p->l_obs > 64 || p->l_obs > p->n_prompt)
+    return fail(LCD_ESHAPE, "l_obs %d outside [1, min(N, 64)]", p->l_obs);
+  if (p->kernel_size < 1 || p->kernel_size > 31 || p->kernel_size % 2 == 0)
+    return fail(LCD_ESHAPE, "kernel_size must be odd and in [1, 31]");
+  if (p->k_keep < 0 || p->k_keep > p->n_prompt - p->l_obs)
+    return fail(LCD_ESHAPE, "k_keep %d outside [0, N - l_obs]", p->k_keep);
+  if (p->pool != 0 && p->pool != 1) return fail(LCD_EINVAL, "pool must be 0 (avg) or 1 (max)");
+  if (p->dtype != LCD_BF16) return fail(LCD_EUNSUPPORTED, "SnapKV scoring runs on bf16 inputs only");
+  if (p->out_rows != 0 && p->out_rows < p->k_keep + p->l_obs)
+    return fail(LCD_ESHAPE, "out_rows %d < k_keep + l_obs", p->out_rows);
+  if ((int64_t)p->n_prompt > (1 << 26)) return fail(LCD_ESHAPE, "n_prompt too large");
+  if (!(std::isfinite(p->scale) && p->scale >= 0.0)) return fail(LCD_EINVAL, "scale must be finite and >= 0");
+  return LCD_OK;
+}
+
+}  // namespace
+
+extern "C" lcd_status lcd_snapkv_sizes(const lcd_snapkv_params* p, uint64_t* ws_bytes) {
+  const lcd_status st = check_snapkv(p);
+  if (st) return st;
+  if (ws_bytes) *ws_bytes = lcd::snapkv_ws_bytes(p->batch, p->n_heads, p->n_prompt, p->l_obs);
+  return ok();
+}
+
+extern "C" lcd_status lcd_snapkv_compress(const lcd_snapkv_params* p, const void* q_obs, const void* k,
+                                          const void* v, void* k_out, void* v_out, int32_t* idx_out,
+                                          float* scores_out, void* ws, uint64_t ws_bytes, void* stream) {
+  lcd_status st = check_snapkv(p);
+  if (st) return st;
+  if (!q_obs || !k || !v || !k_out || !v_out || !idx_out || !ws)
+    return fail(LCD_EINVAL, "a required pointer is NULL");
+  const void* ptrs[] = {q_obs, k, v, k_out, v_out, idx_out, ws};
+  for (const void* x : ptrs)
+    if (!aligned16(x)) return fail(LCD_EALIGN, "pointers must be 16-byte aligned");
+  if (scores_out && !aligned16(scores_out)) return fail(LCD_EALIGN, "scores_out not 16-byte aligned");
+  const uint64_t need = lcd::snapkv_ws_bytes(p->batch, p->n_heads, p->n_prompt, p->l_obs);
+  if (ws_bytes < need)
+    return fail(LCD_ESIZE, "ws_bytes %llu < required %llu", (unsigned long long)ws_bytes, (unsigned long long)need);
+  lcd::SnapkvParams s{};
+  s.q_obs = q_obs;
+  s.k = k;
+  s.v = v;
+  s.k_out = k_out;
+  s.v_out = v_out;
+  s.idx_out = idx_out;
+  s.scores_out = scores_out;
+  s.B = p->batch;
+  s.H = p->n_heads;
+  s.D = p->head_dim;
+  s.N = p->n_prompt;
+  s.Lobs = p->l_obs;
+  s.ksize = p->kernel_size;
+  s.k_keep = p->k_keep;
+  s.pool = p->pool;
+  s.out_rows = p->out_rows ? p->out_rows : p->k_keep + p->l_obs;
+  const double scale = p->scale > 0 ? p->scale : 1.0 / std::sqrt((double)p->head_dim);
+  s.qscale = (float)(scale * 1.4426950408889634074);
+  char* w = static_cast<char*>(ws);
+  s.rowstat = reinterpret_cast<float*>(w);  // carved further inside launch_snapkv
+  const hipError_t e = lcd::launch_snapkv(s, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "snapkv launch");
+  return ok();
+}

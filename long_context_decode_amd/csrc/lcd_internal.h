@@ -1,0 +1,90 @@
+// Internal launch interface between the host library (lcd_host.cpp) and the HIP
+// kernels.  Plain structs of pointers and sizes; nothing here crosses the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lcd {
+
+// Decode workgroup: 4 waves of 64 lanes.
+constexpr int kDecodeThreads = 256;
+// Most slots one decode workgroup reduces (bounds its LDS logit buffer).
+constexpr int kMaxChunk = 4096;
+
+enum DecodeMode { kModeRope = 0, kModePlain = 1, kModePlainLogits = 2 };
+
+struct DecodeParams {
+  const void* k;       // layer K [B][Hkv][C][D] (cache dtype)
+  const void* v;       // layer V
+  const void* q;       // [B][Hq][D]
+  const float* cos_t;  // [C][D/2] (rope mode)
+  const float* sin_t;
+  float* out;          // [B][Hq][D] float32
+  float* part_o;       // [splits][B][Hq][D]
+  float* part_ml;      // [splits][B][Hq][2]  (max, sum) in the log2 domain
+  float* logits;       // [B][Hq][C] log2-domain logits (logits mode)
+  int* arrivals;       // layer [B][Hkv] arrival counters, zero between calls
+  // H2O epilogue (logits mode)
+  float* score;        // layer [B][Hkv][C]
+  const int* pos;      // layer [B][Hkv][C]
+  int* victim;         // layer [B][Hkv]
+  int pick_victim;     // cache full: choose the slot the next append overwrites
+  int64_t max_pos;     // victim candidates have pos <= max_pos
+  int B, Hq, Hkv, C;
+  int n;               // attended slots 0..n-1
+  int chunk;           // slots per split (multiple of 64, <= kMaxChunk)
+  int n_splits;
+  int full;            // ring has wrapped: ranks follow the ring order
+  int S, W;            // sinks and window (rope mode)
+  int ring_head;       // ring index of the oldest window token (rope mode, full)
+  int q_rank;          // in-cache position of the query (rope mode)
+  float qscale;        // logit scale * log2(e)
+};
+
+struct AppendParams {
+  const char* k_in;    // [B][Hkv][n_new][D]
+  const char* v_in;
+  char* k_cache;       // layer [B][Hkv][C][D]
+  char* v_cache;
+  int BHkv, C, n_new, row_bytes;
+  // rows [r0, r0 + n_rows) of the input are written; row r goes to
+  //   slot_lin + (r - r0)                      if r <  r_split
+  //   S + (ring_off + (r - r_split)) % W       if r >= r_split
+  int r0, n_rows, r_split, slot_lin, ring_off, S, W;
+  // H2O: one row per (b, kv head), slot = fill < C ? fill : victim[bh]
+  int h2o, fill;
+  const int* victim;
+  int* pos;
+  float* score;
+  int64_t token;
+};
+
+hipError_t launch_decode_split(int dtype, int D, int G, int mode, const DecodeParams& p, hipStream_t s);
+hipError_t launch_append(const AppendParams& p, hipStream_t s);
+hipError_t launch_rope_table(float* cos_t, float* sin_t, int C, int D, double base, hipStream_t s);
+hipError_t launch_fill_i32(int* p, int value, int64_t n, hipStream_t s);
+hipError_t launch_fill_f32(float* p, float value, int64_t n, hipStream_t s);
+
+bool decode_supported(int dtype, int D, int G);
+
+// SnapKV
+struct SnapkvParams {
+  const void* q_obs;   // [B][H][Lobs][D] bf16
+  const void* k;       // [B][H][N][D]
+  const void* v;
+  void* k_out;         // [B][H][out_rows][D]
+  void* v_out;
+  int* idx_out;        // [B][H][out_rows]
+  float* scores_out;   // [B][H][N - Lobs] or null
+  float* rowstat;      // ws: [B][H][tiles][Lobs][2]
+  float* rowfinal;     // ws: [B][H][Lobs][2] (max, 1/sum) log2 domain
+  float* colscore;     // ws: [B][H][N - Lobs] raw mean scores
+  float* pooled;       // ws: [B][H][N - Lobs]
+  int B, H, D, N, Lobs, ksize, k_keep, pool, out_rows, tiles;
+  float qscale;        // scale * log2(e)
+};
+size_t snapkv_ws_bytes(int B, int H, int N, int Lobs);
+hipError_t launch_snapkv(const SnapkvParams& p, hipStream_t s);
+
+}  // namespace lcd

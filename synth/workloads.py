@@ -107,23 +107,43 @@ class Workload:
         return np.ascontiguousarray(np.transpose(out, (1, 2, 0, 3)))
 
     def token_block_torch(self, tensor: str, layer: int, t0: int, t1: int, device):
-        """Tokens [t0, t1) of a token-major tensor on ``device`` as [b][h][token][d]."""
+        """Tokens [t0, t1) of a token-major tensor on ``device`` as [b][h][token][d]
+        (the bulk-append layout); generated one batch row at a time."""
         import torch
 
-        shape = self.token_shape(tensor)
-        T, B, H, D = shape
+        T, B, H, D = self.token_shape(tensor)
+        st = self.stream(tensor, layer)
+        out = torch.empty((B, H, t1 - t0, D), device=device,
+                          dtype=torch.float32 if self.dtype == "f32" else torch.bfloat16)
         t = torch.arange(t0, t1, device=device, dtype=torch.int64)
-        b = torch.arange(B, device=device, dtype=torch.int64)
         h = torch.arange(H, device=device, dtype=torch.int64)
         d = torch.arange(D, device=device, dtype=torch.int64)
-        # build in [b][h][t][d] order directly
-        idx = ((t[None, None, :, None] * B + b[:, None, None, None]) * H + h[None, :, None, None]) * D
-        idx = idx + d[None, None, None, :]
+        for b in range(B):
+            idx = ((t[None, :, None] * B + b) * H + h[:, None, None]) * D + d[None, None, :]
+            out[b] = st.torch_stored(idx)
+            if tensor == "k" and self.sink_key_scale != 1.0 and t0 < 4:
+                m = min(4, t1) - t0
+                out[b, :, :m] = st.torch_stored(idx[:, :m], self.sink_key_scale)
+        return out
+
+    def token_major_torch(self, tensor: str, layer: int, t0: int, t1: int, device, chunk_tokens=None):
+        """Tokens [t0, t1) on ``device`` as [token][b][h][d]: each token's slice is a
+        contiguous [b][h][d] block (the single-token append / query layout)."""
+        import torch
+
+        T, B, H, D = self.token_shape(tensor)
+        per = B * H * D
         st = self.stream(tensor, layer)
-        out = st.torch_stored(idx)
-        if tensor == "k" and self.sink_key_scale != 1.0 and t0 < 4:
-            hi = st.torch_stored(idx[:, :, : min(4, t1) - t0], self.sink_key_scale)
-            out[:, :, : min(4, t1) - t0] = hi
+        out = torch.empty((t1 - t0, B, H, D), device=device,
+                          dtype=torch.float32 if self.dtype == "f32" else torch.bfloat16)
+        step = chunk_tokens or max(1, (1 << 25) // per)
+        for a in range(t0, t1, step):
+            e = min(t1, a + step)
+            idx = torch.arange(a * per, e * per, device=device, dtype=torch.int64)
+            out[a - t0: e - t0] = st.torch_stored(idx).view(e - a, B, H, D)
+            if tensor == "k" and self.sink_key_scale != 1.0 and a < 4:
+                m = min(4, e) - a
+                out[a - t0: a - t0 + m] = st.torch_stored(idx[: m * per], self.sink_key_scale).view(m, B, H, D)
         return out
 
     # ------------------------------------------------------------------ snapkv

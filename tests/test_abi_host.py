@@ -1,0 +1,122 @@
+"""C ABI host-side checks that need no GPU: the library loads, exports every entry
+point include/lcd.h declares, sizes its buffers by the KV size model, validates
+arguments before any HIP call and keeps its slot / position bookkeeping."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    import long_context_decode_amd as lib
+
+    return lib
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "lcd.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lcd_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    declared = _declared()
+    assert len(declared) >= 15
+    for name in declared:
+        assert hasattr(L.lib, name), name
+    assert set(declared) == set(L._lib.EXPORTED)
+    assert L.abi_version() == 1
+
+
+def test_sizes_follow_the_kv_size_model(L):
+    for (B, Hq, Hkv, D, dt, S, W, layers) in [(16, 32, 32, 128, 1, 4, 2044, 1), (16, 24, 4, 256, 1, 4, 32764, 16),
+                                              (1, 4, 1, 64, 0, 4, 60, 1)]:
+        cfg = L.cache_config(B, Hq, Hkv, D, dt, L.LCD_SINK_RING, n_layers=layers, n_sink=S, window=W, rope=1)
+        kv, aux, ws = L.cache_sizes(cfg)
+        assert kv == oracle.kv_cache_bytes(layers, Hkv, D, S + W, 4 if dt == 0 else 2, batch=B)
+        assert aux >= 2 * (S + W) * (D // 2) * 4  # cos + sin table
+        assert ws > 0
+    # the two full-size decode configurations
+    cfg = L.cache_config(16, 32, 32, 128, 1, L.LCD_SINK_RING, n_sink=4, window=2044, rope=1)
+    assert L.cache_sizes(cfg)[0] == 512 * 2**20
+    cfg = L.cache_config(16, 24, 4, 256, 1, L.LCD_SINK_RING, n_layers=16, n_sink=4, window=32764, rope=1)
+    assert L.cache_sizes(cfg)[0] == 32 * 2**30
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_q_heads=5, n_kv_heads=2), "LCD_ESHAPE"),
+    (dict(head_dim=96), "LCD_ESHAPE"),
+    (dict(n_q_heads=12, n_kv_heads=4), "LCD_EUNSUPPORTED"),  # G = 3
+    (dict(window=0), "LCD_ESHAPE"),
+    (dict(dtype=7), "LCD_EINVAL"),
+    (dict(policy=9), "LCD_EINVAL"),
+    (dict(policy=1, capacity=0), "LCD_ESHAPE"),
+    (dict(policy=2, capacity=16, n_recent=0), "LCD_ESHAPE"),
+    (dict(policy=2, capacity=16, n_recent=17), "LCD_ESHAPE"),
+    (dict(policy=1, capacity=16, rope=1), "LCD_EUNSUPPORTED"),
+    (dict(rope=1, rope_base=1.0), "LCD_EINVAL"),
+    (dict(scale=-1.0), "LCD_EINVAL"),
+    (dict(window=1 << 25), "LCD_ESHAPE"),
+])
+def test_config_validation(L, kw, status):
+    base = dict(batch=2, n_q_heads=4, n_kv_heads=2, head_dim=128, dtype=1, policy=0, n_sink=4, window=60,
+                rope=0)
+    base.update(kw)
+    cfg = L.cache_config(**base)
+    with pytest.raises(L.LcdError) as e:
+        L.cache_sizes(cfg)
+    assert e.value.name == status
+    assert L.last_error()
+
+
+def test_init_validation(L):
+    cfg = L.cache_config(1, 4, 1, 64, 0, L.LCD_SINK_RING, n_sink=4, window=60)
+    kv, aux, _ = L.cache_sizes(cfg)
+    assert aux > 0  # split-merge arrival counters
+    fake = 1 << 20  # never dereferenced: every case fails validation before any HIP call
+    for args, status in [(((1 << 20) + 8, kv, fake, aux), "LCD_EALIGN"), ((fake, kv - 1, fake, aux), "LCD_ESIZE"),
+                         ((None, kv, fake, aux), "LCD_EINVAL"), ((fake, kv, None, aux), "LCD_EINVAL"),
+                         ((fake, kv, fake + 8, aux), "LCD_EALIGN"), ((fake, kv, fake, aux - 1), "LCD_ESIZE")]:
+        with pytest.raises(L.LcdError) as e:
+            L.kv_cache_init(cfg, *args, 0)
+        assert e.value.name == status, args
+
+
+def test_null_handle_calls_fail_cleanly(L):
+    fake = 1 << 20
+    with pytest.raises(L.LcdError) as e:
+        L.kv_append(None, 0, fake, fake, 1, 0)
+    assert e.value.name == "LCD_EINVAL"
+    with pytest.raises(L.LcdError) as e:
+        L.decode_attn(None, 0, fake, fake, fake, 1 << 30, 0)
+    assert e.value.name == "LCD_EINVAL"
+    assert L.kv_tokens(None, 0) == -1 and L.kv_slot_of(None, 0, 5) == -1 and L.kv_rank_of(None, 0, 1) == -1
+    with pytest.raises(L.LcdError):
+        L.kv_set_filled(None, 0, 1, 1)
+
+
+def test_snapkv_param_validation(L):
+    ok = dict(batch=1, n_heads=32, head_dim=128, n_prompt=32768, l_obs=32, kernel_size=5, k_keep=5243)
+    assert L.snapkv_sizes(L.snapkv_params(**ok)) > 0
+    for kw, status in [(dict(kernel_size=4), "LCD_ESHAPE"), (dict(l_obs=65), "LCD_ESHAPE"),
+                       (dict(k_keep=32768 - 31), "LCD_ESHAPE"), (dict(dtype=0), "LCD_EUNSUPPORTED"),
+                       (dict(pool=2), "LCD_EINVAL"), (dict(out_rows=100), "LCD_ESHAPE"),
+                       (dict(head_dim=80), "LCD_ESHAPE")]:
+        p = dict(ok)
+        p.update(kw)
+        with pytest.raises(L.LcdError) as e:
+            L.snapkv_sizes(L.snapkv_params(**p))
+        assert e.value.name == status
+
+
+def test_destroy_null_is_ignored(L):
+    L.lib.lcd_kv_cache_destroy(None)
+    assert isinstance(L.last_error(), str)
+    assert ctypes.sizeof(L._lib.CacheConfig) == 12 * 4 + 2 * 8
