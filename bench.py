@@ -34,6 +34,7 @@ def _parse(argv=None):
                     choices=["llama2_7b_layer", "gqa_long", "tiny_streaming"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="bound of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-snapkv", action="store_true", help="skip the SnapKV compression timing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args(argv)
@@ -131,6 +132,46 @@ def _streaming_bench(L, w, steps, warmup):
     return res
 
 
+def _snapkv_bench(L, w, reps=20):
+    """SnapKV compression of the 32k prompt: ms per compress (median of ``reps``)."""
+    import torch
+
+    B, H, D, N, Lo, K = w.batch, w.n_q_heads, w.head_dim, w.n_prompt, w.l_obs, w.k_keep
+    dev = "cuda"
+    p = L.snapkv_params(B, H, D, N, Lo, w.kernel_size, K)
+    wsb = L.snapkv_sizes(p)
+    q = w.snapkv_tensor_torch("q_obs", dev)
+    k = w.snapkv_tensor_torch("k", dev)
+    v = w.snapkv_tensor_torch("v", dev)
+    ko = torch.empty((B, H, K + Lo, D), dtype=torch.bfloat16, device=dev)
+    vo = torch.empty_like(ko)
+    idx = torch.empty((B, H, K + Lo), dtype=torch.int32, device=dev)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        L.snapkv_compress(p, q, k, v, ko, vo, idx, None, ws, wsb)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        L.snapkv_compress(p, q, k, v, ko, vo, idx, None, ws, wsb)
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    times.sort()
+    ms = times[len(times) // 2]
+    # algorithmic: K read once, the kept K/V rows read and written, q, indices
+    kbytes = B * H * N * D * 2
+    gather = 2 * 2 * B * H * (K + Lo) * D * 2
+    alg_bytes = kbytes + gather + B * H * Lo * D * 2 + B * H * (K + Lo) * 4
+    flops = 2 * B * H * Lo * N * D  # one observation-window Q K^T
+    return {"workload": w.title, "compress_ms": round(ms, 4), "reps": reps,
+            "algorithmic_bytes": alg_bytes, "hbm_gb_s": round(alg_bytes / (ms / 1e3) / 1e9, 1),
+            "hbm_frac": round(alg_bytes / (ms / 1e3) / HBM_PEAK, 4),
+            "qk_tflops": round(flops / (ms / 1e3) / 1e12, 2),
+            "mfma_frac_bf16": round(flops / (ms / 1e3) / 2.5e15, 5)}
+
+
 def _cpu_baseline_streaming(w, budget_s):
     """The fp64 oracle on a bounded sample of one decode step (single thread)."""
     import numpy as np
@@ -224,6 +265,8 @@ def main(argv=None):
                      "median_launch_us": round(r["median_kernel_ms"] * 1e3, 2),
                      "launches_timed": r["kernel_launches"]},
     }
+    if not a.no_snapkv:
+        line["snapkv"] = _snapkv_bench(L, WORKLOADS["snapkv_32k"])
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = _cpu_baseline_streaming(w, a.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -116,9 +116,11 @@ const char* lcd_last_error(void);
  *              contextos longos" and [KVL] "01 · Conceito" with C retained slots.
  *              Layout: for layer l, K at l*2*P and V at (l*2+1)*P bytes, each
  *              [batch][n_kv_heads][C][head_dim], P = kv_bytes / (2 * n_layers).
- *   aux_bytes  Per-cache state: the float32 cos/sin table of the in-cache
- *              positions (SINK_RING with rope), per-slot token positions and
- *              scores and per-(layer, row, head) victim slots (H2O).  Opaque.
+ *   aux_bytes  Per-cache state: int32 arrival counters of the split merge (one
+ *              per layer, batch row and KV head), the float32 cos/sin table of
+ *              the in-cache positions (SINK_RING with rope), per-slot token
+ *              positions and scores and per-(layer, row, head) victim slots
+ *              (H2O).  Opaque.
  *   ws_bytes   Workspace one lcd_decode_attn call needs (split partials, and
  *              logits for H2O).  Opaque; may be reused across calls that are
  *              ordered on one stream.
@@ -190,9 +192,13 @@ lcd_status lcd_kv_layer_view(const lcd_cache* cache, int32_t layer, void** k, vo
 
 /* Seed a layer whose first n rows (per batch row and KV head) were already
  * written in place through lcd_kv_layer_view: sets the fill count to n and the
- * token counter to next_token.  APPEND and H2O only (n <= capacity).  For H2O the
- * caller has also written pos and score of those rows.  Enqueues nothing. */
-lcd_status lcd_kv_set_filled(lcd_cache* cache, int32_t layer, int32_t n, int64_t next_token);
+ * token counter to next_token (the position of the next appended token).  APPEND
+ * and H2O only (n <= capacity).  For H2O the caller has also written pos (distinct
+ * token positions < next_token) and score of those rows; when n == capacity the
+ * victim of the next append is chosen on `stream` from those scores (lowest score
+ * among positions <= next_token - n_recent, ties evicting the higher position).
+ * Otherwise nothing is enqueued. */
+lcd_status lcd_kv_set_filled(lcd_cache* cache, int32_t layer, int32_t n, int64_t next_token, void* stream);
 
 /* SnapKV ---------------------------------------------------------------------
  * [KVC] "SnapKV e a seleção de contexto no prefill": at the end of prefill each

@@ -72,7 +72,7 @@ _SIGS = {
     "lcd_kv_rank_of": (_I64, [_P, _I32, _I64]),
     "lcd_kv_layer_view": (_S, [_P, _I32, ctypes.POINTER(_P), ctypes.POINTER(_P), ctypes.POINTER(_P),
                                ctypes.POINTER(_P)]),
-    "lcd_kv_set_filled": (_S, [_P, _I32, _I32, _I64]),
+    "lcd_kv_set_filled": (_S, [_P, _I32, _I32, _I64, _P]),
     "lcd_snapkv_sizes": (_S, [ctypes.POINTER(SnapkvParams), ctypes.POINTER(_U64)]),
     "lcd_snapkv_compress": (_S, [ctypes.POINTER(SnapkvParams), _P, _P, _P, _P, _P, _P, _P, _P, _U64, _P]),
 }
@@ -172,8 +172,8 @@ def kv_layer_view(h, layer):
     return k.value, v.value, pos.value, score.value
 
 
-def kv_set_filled(h, layer, n, next_token):
-    _check(lib.lcd_kv_set_filled(h, layer, n, next_token))
+def kv_set_filled(h, layer, n, next_token, stream=None):
+    _check(lib.lcd_kv_set_filled(h, layer, n, next_token, _stream(stream)))
 
 
 def snapkv_params(batch, n_heads, head_dim, n_prompt, l_obs, kernel_size, k_keep, pool=0, dtype=LCD_BF16,
@@ -229,6 +229,19 @@ class KVCache:
         kv = self.kv_mem[base: base + 2 * per * es].view(dt)
         return kv[:per].view(c.batch, c.n_kv_heads, C, c.head_dim), kv[per:].view(c.batch, c.n_kv_heads, C,
                                                                                    c.head_dim)
+
+    def h2o_tensors(self, layer):
+        """(positions int32, scores float32) views of one H2O layer as [B][H_kv][C]."""
+        import torch
+
+        c = self.cfg
+        _, _, pos, score = kv_layer_view(self.handle, layer)
+        n = c.batch * c.n_kv_heads * c.capacity
+        base = self.aux_mem.data_ptr()
+        po, so = pos - base, score - base
+        P = self.aux_mem[po: po + 4 * n].view(torch.int32).view(c.batch, c.n_kv_heads, c.capacity)
+        S = self.aux_mem[so: so + 4 * n].view(torch.float32).view(c.batch, c.n_kv_heads, c.capacity)
+        return P, S
 
     def close(self):
         if self.handle:

@@ -480,6 +480,43 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodePara
   }
 }
 
+// Victim choice for a seeded H2O layer (no decode step has run yet): the lowest score
+// among slots whose token position is <= max_pos, ties evicting the higher position.
+__global__ void __launch_bounds__(256) h2o_pick_victim_kernel(const float* score, const int* pos, int* victim, int C,
+                                                              int n, int64_t max_pos) {
+  __shared__ unsigned long long wbest[4];
+  const size_t bg = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  unsigned long long best = ~0ull;
+  for (int i = threadIdx.x; i < n; i += 256) {
+    const int ps = pos[bg * C + i];
+    if ((int64_t)ps <= max_pos) {
+      const unsigned long long key = ((unsigned long long)__float_as_uint(score[bg * C + i]) << 32) |
+                                     (unsigned long long)(0xffffffffu - (uint32_t)ps);
+      best = key < best ? key : best;
+    }
+  }
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const unsigned long long other = __shfl_xor(best, off, 64);
+    best = other < best ? other : best;
+  }
+  if (lane == 0) wbest[wave] = best;
+  __syncthreads();
+  best = wbest[0];
+  for (int w = 1; w < 4; ++w) best = wbest[w] < best ? wbest[w] : best;
+  if (best == ~0ull) return;
+  const int win_pos = (int)(0xffffffffu - (uint32_t)(best & 0xffffffffull));
+  for (int i = threadIdx.x; i < n; i += 256)
+    if (pos[bg * C + i] == win_pos) victim[bg] = i;
+}
+
+hipError_t launch_h2o_pick_victim(const float* score, const int* pos, int* victim, int BHkv, int C, int n,
+                                  int64_t max_pos, hipStream_t s) {
+  hipLaunchKernelGGL(h2o_pick_victim_kernel, dim3(BHkv), dim3(256), 0, s, score, pos, victim, C, n, max_pos);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------- dispatch
 template <typename T, int D, int G>
 static hipError_t launch_tdg(int mode, const DecodeParams& p, hipStream_t s) {

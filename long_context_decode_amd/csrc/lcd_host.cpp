@@ -467,13 +467,20 @@ lcd_status lcd_kv_layer_view(const lcd_cache* c, int32_t layer, void** k, void**
   return ok();
 }
 
-lcd_status lcd_kv_set_filled(lcd_cache* c, int32_t layer, int32_t n, int64_t next_token) {
+lcd_status lcd_kv_set_filled(lcd_cache* c, int32_t layer, int32_t n, int64_t next_token, void* stream) {
   lcd_status st = check_layer(c, layer);
   if (st) return st;
   if (c->cfg.policy == LCD_SINK_RING)
     return fail(LCD_EUNSUPPORTED, "set_filled applies to APPEND and H2O caches");
   if (n < 0 || n > c->L.C) return fail(LCD_ECAPACITY, "n=%d outside [0, %d]", n, c->L.C);
   if (next_token < n) return fail(LCD_EINVAL, "next_token must be >= n");
+  if (c->cfg.policy == LCD_H2O && next_token > INT32_MAX) return fail(LCD_ECAPACITY, "H2O token positions are int32");
+  if (c->cfg.policy == LCD_H2O && n == c->L.C) {
+    const hipError_t e = lcd::launch_h2o_pick_victim(c->score(layer), c->pos(layer), c->victim(layer),
+                                                     c->cfg.batch * c->cfg.n_kv_heads, c->L.C, n,
+                                                     next_token - c->cfg.n_recent, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "set_filled victim launch");
+  }
   c->filled[layer] = n;
   c->tokens[layer] = next_token;
   return ok();
@@ -504,7 +511,8 @@ lcd_status check_snapkv(const lcd_snapkv_params* p) {
   if (p->dtype != LCD_BF16) return fail(LCD_EUNSUPPORTED, "SnapKV scoring runs on bf16 inputs only");
   if (p->out_rows != 0 && p->out_rows < p->k_keep + p->l_obs)
     return fail(LCD_ESHAPE, "out_rows %d < k_keep + l_obs", p->out_rows);
-  if ((int64_t)p->n_prompt > (1 << 26)) return fail(LCD_ESHAPE, "n_prompt too large");
+  if ((int64_t)p->n_prompt - p->l_obs > 64 * 1024)
+    return fail(LCD_ESHAPE, "n_prompt - l_obs must be <= 65536 (per-head selection is register-resident)");
   if (!(std::isfinite(p->scale) && p->scale >= 0.0)) return fail(LCD_EINVAL, "scale must be finite and >= 0");
   return LCD_OK;
 }

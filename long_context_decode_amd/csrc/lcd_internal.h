@@ -62,6 +62,8 @@ struct AppendParams {
 
 hipError_t launch_decode_split(int dtype, int D, int G, int mode, const DecodeParams& p, hipStream_t s);
 hipError_t launch_append(const AppendParams& p, hipStream_t s);
+hipError_t launch_h2o_pick_victim(const float* score, const int* pos, int* victim, int BHkv, int C, int n,
+                                  int64_t max_pos, hipStream_t s);
 hipError_t launch_rope_table(float* cos_t, float* sin_t, int C, int D, double base, hipStream_t s);
 hipError_t launch_fill_i32(int* p, int value, int64_t n, hipStream_t s);
 hipError_t launch_fill_f32(float* p, float value, int64_t n, hipStream_t s);

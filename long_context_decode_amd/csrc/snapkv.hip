@@ -1,18 +1,557 @@
-// SnapKV prefill compression kernels (placeholder until the MFMA scorer lands).
+// SnapKV prefill compression for gfx950 ([KVC] "SnapKV e a seleção de contexto no
+// prefill"): observation-window attention scores, their mean over the window rows,
+// 1-D pooling, per-head top-k and the gather of the kept K/V rows.
+//
+// Pipeline on one stream, no host round trip:
+//   1. snapkv_rowstats   per (row, head, 256-key tile): logits of the L_obs window
+//                        queries against the tile's keys on MFMA (bf16 in, fp32
+//                        accumulate), causal mask, per-row (max, sum of 2^(x-max)).
+//   2. snapkv_rowfinal   per (row, head): merge the tiles -> (M_t, 1/L_t).
+//   3. snapkv_colscore   per tile of prefix keys: the same MFMA product, weights
+//                        2^(x - M_t) / L_t summed over the window rows -> s_i
+//                        (times 1/L_obs: the mean of step 2).
+//   4. snapkv_select     one workgroup per head: pooled scores, 4-pass radix select
+//                        of the k-th largest on the float bits (scores are >= 0, so
+//                        the bit patterns order like the values), then a stable
+//                        compaction that lists the kept positions in ascending order
+//                        (ties at the threshold keep the lower indices), followed by
+//                        the observation window.
+//   5. snapkv_gather     copy the kept K and V rows.
+// The contraction is L_obs x N x D per head: 32 rows against every key, i.e. 32 flops
+// per byte of K read.  It is a dense product, so it runs on MFMA, but it remains
+// HBM-bound (K is read twice: steps 1 and 3).
 #include <hip/hip_runtime.h>
 
 #include "lcd_internal.h"
 
 namespace lcd {
 
-size_t snapkv_ws_bytes(int B, int H, int N, int Lobs) {
-  (void)B; (void)H; (void)N; (void)Lobs;
-  return 256;
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWaveBlocks = 4;   // 32-key blocks per wave in the scoring kernels
+constexpr int kTileKeys = 4 * kWaveBlocks * 32;  // keys per scoring workgroup
+constexpr int kMaxRows = 64;      // observation rows supported (two 32-row MFMA blocks)
+constexpr int kSelectThreads = 1024;
+
+__device__ inline bf16x8 load_frag(const uint16_t* p) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  return __builtin_bit_cast(bf16x8, u);
 }
 
-hipError_t launch_snapkv(const SnapkvParams& p, hipStream_t s) {
-  (void)p; (void)s;
-  return hipErrorNotSupported;
+__device__ inline bf16x8 zero_frag() { return __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0)); }
+
+// Observation-query fragments of row block rb: lane l holds row rb*32 + l%32, elements
+// 16*s + 8*(l/32) .. +7 of step s.  Rows past L_obs are zero.
+template <int D>
+__device__ inline void load_q_frags(const uint16_t* q, int Lobs, int rb, int lane, bf16x8 (&qf)[D / 16]) {
+  const int row = rb * 32 + (lane & 31);
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s)
+    qf[s] = row < Lobs ? load_frag(q + (size_t)row * D + 16 * s + 8 * (lane >> 5)) : zero_frag();
+}
+
+// K rows are staged through LDS so that global loads are fully coalesced: a 32-key
+// block is read in column chunks of CW = min(D, 128) elements as 16-byte pieces, 64
+// consecutive pieces per load instruction, then the MFMA fragments of that chunk are
+// read back from LDS.  Rows are padded by 16 bytes so that the fragment reads (one
+// row per lane) spread over the LDS banks.
+template <int D>
+constexpr int chunk_w() { return D < 128 ? D : 128; }
+template <int D>
+constexpr int lds_row_bytes() { return chunk_w<D>() * 2 + 16; }
+template <int D>
+constexpr int block_lds_bytes() { return 32 * lds_row_bytes<D>(); }
+template <int D>
+constexpr int chunk_pieces() { return chunk_w<D>() / 16; }  // 16-byte pieces per lane per chunk
+
+template <int D>
+__device__ inline void chunk_load(const uint16_t* k, int N, int key0, int c, int lane,
+                                  u32x4 (&raw)[chunk_pieces<D>()]) {
+  constexpr int PPR = chunk_w<D>() * 2 / 16;  // pieces per row of the chunk
+#pragma unroll
+  for (int i = 0; i < chunk_pieces<D>(); ++i) {
+    const int piece = i * 64 + lane;
+    const int row = piece / PPR, col = piece % PPR;
+    const int key = key0 + row;
+    raw[i] = key < N ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+                           k + (size_t)key * D + c * chunk_w<D>() + col * 8))
+                     : u32x4{0, 0, 0, 0};
+  }
+}
+
+template <int D>
+__device__ inline void chunk_store_lds(char* lds, int lane, const u32x4 (&raw)[chunk_pieces<D>()]) {
+  constexpr int PPR = chunk_w<D>() * 2 / 16;
+#pragma unroll
+  for (int i = 0; i < chunk_pieces<D>(); ++i) {
+    const int piece = i * 64 + lane;
+    *reinterpret_cast<u32x4*>(lds + (piece / PPR) * lds_row_bytes<D>() + (piece % PPR) * 16) = raw[i];
+  }
+}
+
+// Fragment s (within the chunk) of row lane%32: chunk elements 16*s + 8*(lane/32) .. +7.
+template <int D>
+__device__ inline void chunk_frags_lds(const char* lds, int lane, bf16x8 (&kf)[chunk_w<D>() / 16]) {
+#pragma unroll
+  for (int s = 0; s < chunk_w<D>() / 16; ++s)
+    kf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(lds + (lane & 31) * lds_row_bytes<D>() +
+                                                                       32 * s + 16 * (lane >> 5)));
+}
+
+// LDS accesses of one wave execute in program order; this keeps the compiler from
+// moving them across the hand-off between the staging store and the fragment reads.
+__device__ inline void wave_lds_order() { __asm__ volatile("" ::: "memory"); }
+
+// Result element r of a 32x32 MFMA tile sits at A-row 8*(r/4) + 4*(lane/32) + r%4 and
+// B-column lane%32.
+__device__ inline int mfma_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+
+// ---------------------------------------------------------------------------- 1. rowstats
+template <int D, int RB>
+__global__ void __launch_bounds__(256) snapkv_rowstats_kernel(SnapkvParams p) {
+  __shared__ float sm[4][kMaxRows], sl[4][kMaxRows];
+  __shared__ __attribute__((aligned(16))) char stage[4][block_lds_bytes<D>()];
+  const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const size_t bh = (size_t)b * p.H + h;
+  const uint16_t* q = reinterpret_cast<const uint16_t*>(p.q_obs) + bh * p.Lobs * D;
+  const uint16_t* k = reinterpret_cast<const uint16_t*>(p.k) + bh * (size_t)p.N * D;
+  const int last_visible0 = p.N - p.Lobs;  // row t sees keys <= last_visible0 + t
+  const int wkey0 = tile * kTileKeys + wave * kWaveBlocks * 32;
+  bf16x8 qf[RB][D / 16];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) load_q_frags<D>(q, p.Lobs, rb, lane, qf[rb]);
+  float m[RB], l[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    m[rb] = -INFINITY;
+    l[rb] = 0.f;
+  }
+  constexpr int NC = D / chunk_w<D>();
+  constexpr int FS = chunk_w<D>() / 16;  // fragments per chunk
+  u32x4 raw[chunk_pieces<D>()];
+  chunk_load<D>(k, p.N, wkey0, 0, lane, raw);
+  for (int blk = 0; blk < kWaveBlocks; ++blk) {
+    const int key0 = wkey0 + blk * 32;
+    if (key0 >= p.N) break;  // wave-uniform
+    f32x16 acc[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) acc[rb] = f32x16{};
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      chunk_store_lds<D>(stage[wave], lane, raw);
+      // prefetch the next chunk (of this block or the next one)
+      if (c + 1 < NC) chunk_load<D>(k, p.N, key0, c + 1, lane, raw);
+      else if (blk + 1 < kWaveBlocks) chunk_load<D>(k, p.N, key0 + 32, 0, lane, raw);
+      wave_lds_order();
+      bf16x8 kf[FS];
+      chunk_frags_lds<D>(stage[wave], lane, kf);
+      wave_lds_order();
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+        for (int s = 0; s < FS; ++s)
+          acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[rb][c * FS + s], acc[rb], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      // acc[rb][r]: key key0 + mfma_row(r), observation row t
+      const int t = rb * 32 + (lane & 31);
+      float x[16];
+      float bm = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + mfma_row(r, lane);
+        const bool vis = key < p.N && key <= last_visible0 + t && t < p.Lobs;
+        x[r] = vis ? acc[rb][r] * p.qscale : -INFINITY;
+        bm = fmaxf(bm, x[r]);
+      }
+      const float mn = fmaxf(m[rb], bm);
+      if (mn > -INFINITY) {
+        float add = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) add += exp2f(x[r] - mn);
+        l[rb] = l[rb] * exp2f(m[rb] - mn) + add;
+        m[rb] = mn;
+      }
+    }
+  }
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    // lanes l and l ^ 32 hold the same row
+    const float mo = __shfl_xor(m[rb], 32, 64), lo = __shfl_xor(l[rb], 32, 64);
+    const float mm = fmaxf(m[rb], mo);
+    float ll = 0.f;
+    if (mm > -INFINITY) ll = l[rb] * exp2f(m[rb] - mm) + lo * exp2f(mo - mm);
+    if (lane < 32) {
+      sm[wave][rb * 32 + lane] = mm;
+      sl[wave][rb * 32 + lane] = ll;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < RB * 32) {
+    const int t = threadIdx.x;
+    float mm = -INFINITY;
+    for (int w = 0; w < 4; ++w) mm = fmaxf(mm, sm[w][t]);
+    float ll = 0.f;
+    if (mm > -INFINITY)
+      for (int w = 0; w < 4; ++w) ll += sl[w][t] * exp2f(sm[w][t] - mm);
+    float* out = p.rowstat + ((bh * p.tiles + tile) * kMaxRows + t) * 2;
+    out[0] = mm;
+    out[1] = ll;
+  }
+}
+
+// ---------------------------------------------------------------------------- 2. rowfinal
+// One workgroup per (row, head): threads stride over (tile, observation row) pairs,
+// then each row's partial maxima / sums are merged through LDS.
+constexpr int kFinalThreads = 1024;
+__global__ void __launch_bounds__(kFinalThreads) snapkv_rowfinal_kernel(SnapkvParams p) {
+  __shared__ float pm[kFinalThreads], pl[kFinalThreads];
+  const size_t bh = blockIdx.x;
+  const int rows = ((p.Lobs + 31) / 32) * 32;
+  const int t = threadIdx.x % rows, part = threadIdx.x / rows, parts = kFinalThreads / rows;
+  float M = -INFINITY, L = 0.f;
+  for (int i = part; i < p.tiles; i += parts) {
+    const float* st = p.rowstat + ((bh * p.tiles + i) * kMaxRows + t) * 2;
+    const float m = st[0], l = st[1];
+    const float mn = fmaxf(M, m);
+    if (mn > -INFINITY) {
+      L = L * exp2f(M - mn) + l * exp2f(m - mn);
+      M = mn;
+    }
+  }
+  pm[threadIdx.x] = M;
+  pl[threadIdx.x] = L;
+  __syncthreads();
+  if (threadIdx.x < rows) {
+    float mm = -INFINITY;
+    for (int q = 0; q < parts; ++q) mm = fmaxf(mm, pm[q * rows + t]);
+    float ll = 0.f;
+    if (mm > -INFINITY)
+      for (int q = 0; q < parts; ++q) ll += pl[q * rows + t] * exp2f(pm[q * rows + t] - mm);
+    // rows past L_obs get zero weight (their logits are exactly 0: 2^(0 - 0) * 0 = 0)
+    const bool real = t < p.Lobs && ll > 0.f;
+    p.rowfinal[(bh * kMaxRows + t) * 2] = real ? mm : 0.f;
+    p.rowfinal[(bh * kMaxRows + t) * 2 + 1] = real ? 1.f / ll : 0.f;
+  }
+  if (threadIdx.x >= rows && threadIdx.x < kMaxRows) {
+    p.rowfinal[(bh * kMaxRows + threadIdx.x) * 2] = 0.f;
+    p.rowfinal[(bh * kMaxRows + threadIdx.x) * 2 + 1] = 0.f;
+  }
+}
+
+// ---------------------------------------------------------------------------- 3. colscore
+template <int D, int RB>
+__global__ void __launch_bounds__(256) snapkv_colscore_kernel(SnapkvParams p) {
+  __shared__ float sM[kMaxRows], sI[kMaxRows];
+  __shared__ __attribute__((aligned(16))) char stage[4][block_lds_bytes<D>()];
+  const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const size_t bh = (size_t)b * p.H + h;
+  if (threadIdx.x < kMaxRows) {
+    sM[threadIdx.x] = p.rowfinal[(bh * kMaxRows + threadIdx.x) * 2];
+    sI[threadIdx.x] = p.rowfinal[(bh * kMaxRows + threadIdx.x) * 2 + 1];
+  }
+  __syncthreads();
+  const uint16_t* q = reinterpret_cast<const uint16_t*>(p.q_obs) + bh * p.Lobs * D;
+  const uint16_t* k = reinterpret_cast<const uint16_t*>(p.k) + bh * (size_t)p.N * D;
+  const int Np = p.N - p.Lobs;  // prefix keys: visible to every observation row
+  const float inv_rows = 1.f / (float)p.Lobs;
+  const int wkey0 = tile * kTileKeys + wave * kWaveBlocks * 32;
+  if (wkey0 >= Np) return;  // after the only __syncthreads
+  bf16x8 qf[RB][D / 16];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) load_q_frags<D>(q, p.Lobs, rb, lane, qf[rb]);
+  constexpr int NC = D / chunk_w<D>();
+  constexpr int FS = chunk_w<D>() / 16;
+  u32x4 raw[chunk_pieces<D>()];
+  chunk_load<D>(k, Np, wkey0, 0, lane, raw);
+  for (int blk = 0; blk < kWaveBlocks; ++blk) {
+    const int key0 = wkey0 + blk * 32;
+    if (key0 >= Np) break;  // wave-uniform
+    f32x16 acc[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) acc[rb] = f32x16{};
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      chunk_store_lds<D>(stage[wave], lane, raw);
+      if (c + 1 < NC) chunk_load<D>(k, Np, key0, c + 1, lane, raw);
+      else if (blk + 1 < kWaveBlocks) chunk_load<D>(k, Np, key0 + 32, 0, lane, raw);
+      wave_lds_order();
+      bf16x8 kf[FS];
+      chunk_frags_lds<D>(stage[wave], lane, kf);
+      wave_lds_order();
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+        for (int st = 0; st < FS; ++st)
+          acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[rb][c * FS + st], kf[st], acc[rb], 0, 0, 0);
+      }
+    }
+    float sc = 0.f;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      // acc[rb][r]: observation row rb*32 + mfma_row(r), key key0 + lane%32
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = rb * 32 + mfma_row(r, lane);
+        sc += exp2f(acc[rb][r] * p.qscale - sM[t]) * sI[t];
+      }
+    }
+    sc += __shfl_xor(sc, 32, 64);
+    const int key = key0 + (lane & 31);
+    if (lane < 32 && key < Np) p.colscore[bh * Np + key] = sc * inv_rows;
+  }
+}
+
+// ---------------------------------------------------------------------------- 4. select
+// Exclusive prefix sum over the 1024 threads of the block; *total receives the sum.
+__device__ int block_exclusive_scan(int v, int* warp_tot, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) warp_tot[wave] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int acc = 0;
+    for (int w = 0; w < kSelectThreads / 64; ++w) {
+      const int t = warp_tot[w];
+      warp_tot[w] = acc;
+      acc += t;
+    }
+    *total = acc;
+  }
+  __syncthreads();
+  const int r = warp_tot[wave] + x - v;
+  __syncthreads();
+  return r;
+}
+
+// Pooling of the prefix scores: centred window of kernel_size, zero padding; the
+// average divides by kernel_size everywhere.  Fixed summation order (-r .. r).
+__global__ void snapkv_pool_kernel(SnapkvParams p) {
+  const int Np = p.N - p.Lobs;
+  const size_t total = (size_t)p.B * p.H * Np;
+  const int rad = p.ksize / 2;
+  const float inv_k = 1.f / (float)p.ksize;
+  for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (size_t)gridDim.x * blockDim.x) {
+    const size_t bh = e / Np;
+    const int i = (int)(e % Np);
+    const float* s = p.colscore + bh * Np;
+    float acc = 0.f;  // scores are >= 0: also the identity of max
+    for (int d = -rad; d <= rad; ++d) {
+      const int j = i + d;
+      if (j < 0 || j >= Np) continue;
+      acc = p.pool ? fmaxf(acc, s[j]) : acc + s[j];
+    }
+    const float v = p.pool ? acc : acc * inv_k;
+    p.pooled[e] = v;
+    if (p.scores_out) p.scores_out[e] = v;
+  }
+}
+
+// Radix select of the k-th largest pooled score of one head, with the scores held in
+// registers: thread t owns the contiguous positions [t*PER, (t+1)*PER).  Three passes of
+// 11-bit digits (bits 31..21, 20..10, 9..0) over the float bit patterns; each pass
+// histograms the candidates that match the prefix fixed so far (4 interleaved copies
+// of the histogram cut LDS atomic conflicts), then a block scan over the bins, highest
+// digit first, finds the digit where the count of larger values reaches k.
+constexpr int kDigitBits = 11;
+constexpr int kBins = 1 << kDigitBits;
+constexpr int kHistCopies = 4;
+
+template <int PER>
+__global__ void __launch_bounds__(kSelectThreads) snapkv_select_kernel(SnapkvParams p) {
+  __shared__ int hist[kHistCopies * kBins];
+  __shared__ int warp_tot[kSelectThreads / 64];
+  __shared__ int total;
+  __shared__ int s_digit, s_krem;
+  const int h = blockIdx.x, b = blockIdx.y;
+  const size_t bh = (size_t)b * p.H + h;
+  const int Np = p.N - p.Lobs;
+  const float* pooled = p.pooled + bh * Np;
+  const int i0 = threadIdx.x * PER;
+  uint32_t u[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) u[j] = i0 + j < Np ? __float_as_uint(pooled[i0 + j]) : 0u;
+  const int k = p.k_keep;
+  uint32_t prefix = 0, mask = 0;
+  int krem = k;
+  if (k > 0) {
+    for (int pass = 0; pass < 3; ++pass) {
+      const int shift = 32 - kDigitBits * (pass + 1) > 0 ? 32 - kDigitBits * (pass + 1) : 0;
+      const int bits = pass < 2 ? kDigitBits : 32 - 2 * kDigitBits;
+      const uint32_t dmask = (1u << bits) - 1u;
+      for (int i = threadIdx.x; i < kHistCopies * kBins; i += kSelectThreads) hist[i] = 0;
+      __syncthreads();
+      int* hcopy = hist + (threadIdx.x & (kHistCopies - 1)) * kBins;
+#pragma unroll
+      for (int j = 0; j < PER; ++j)
+        if (i0 + j < Np && (u[j] & mask) == prefix) atomicAdd(&hcopy[(u[j] >> shift) & dmask], 1);
+      __syncthreads();
+      // bins in descending digit order, two per thread
+      const int nb = 1 << bits;
+      int c[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int bin = nb - 1 - (2 * (int)threadIdx.x + e);
+        int v = 0;
+        if (bin >= 0)
+          for (int q = 0; q < kHistCopies; ++q) v += hist[q * kBins + bin];
+        c[e] = v;
+      }
+      const int before = block_exclusive_scan(c[0] + c[1], warp_tot, &total);
+      if (before < krem && before + c[0] + c[1] >= krem) {
+        const int e = before + c[0] >= krem ? 0 : 1;
+        s_digit = nb - 1 - (2 * (int)threadIdx.x + e);
+        s_krem = krem - before - (e ? c[0] : 0);
+      }
+      __syncthreads();
+      prefix |= (uint32_t)s_digit << shift;
+      mask |= dmask << shift;
+      krem = s_krem;
+      __syncthreads();
+    }
+  }
+  const uint32_t T = prefix;                // bit pattern of the k-th largest score
+  const int take_eq_total = k > 0 ? krem : 0;  // how many values equal to T are kept
+  int n_gt = 0, n_eq = 0;
+  if (k > 0) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const bool in = i0 + j < Np;
+      n_gt += in && u[j] > T;
+      n_eq += in && u[j] == T;
+    }
+  }
+  const int eq_before = block_exclusive_scan(n_eq, warp_tot, &total);
+  const int take_eq = max(0, min(n_eq, take_eq_total - eq_before));
+  const int off = block_exclusive_scan(n_gt + take_eq, warp_tot, &total);
+  int* idx = p.idx_out + bh * p.out_rows;
+  if (k > 0) {
+    int o = off, seen = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      if (i0 + j >= Np) break;
+      bool keep = u[j] > T;
+      if (u[j] == T) {
+        keep = seen < take_eq;
+        ++seen;
+      }
+      if (keep) idx[o++] = i0 + j;
+    }
+  }
+  for (int t = threadIdx.x; t < p.Lobs; t += kSelectThreads) idx[k + t] = Np + t;
+}
+
+// ---------------------------------------------------------------------------- 5. gather
+__global__ void snapkv_gather_kernel(SnapkvParams p, int rows) {
+  const int h = blockIdx.y, b = blockIdx.z;
+  const size_t bh = (size_t)b * p.H + h;
+  const int chunks = p.D * 2 / 16;  // 16-byte pieces per row
+  const int* idx = p.idx_out + bh * p.out_rows;
+  const char* k = reinterpret_cast<const char*>(p.k) + bh * (size_t)p.N * p.D * 2;
+  const char* v = reinterpret_cast<const char*>(p.v) + bh * (size_t)p.N * p.D * 2;
+  char* ko = reinterpret_cast<char*>(p.k_out) + bh * (size_t)p.out_rows * p.D * 2;
+  char* vo = reinterpret_cast<char*>(p.v_out) + bh * (size_t)p.out_rows * p.D * 2;
+  const int total = rows * chunks;
+  for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < total; e += gridDim.x * blockDim.x) {
+    const int row = e / chunks, c = e % chunks;
+    const size_t src = (size_t)idx[row] * p.D * 2 + (size_t)c * 16;
+    const size_t dst = (size_t)row * p.D * 2 + (size_t)c * 16;
+    *reinterpret_cast<uint4*>(ko + dst) = *reinterpret_cast<const uint4*>(k + src);
+    *reinterpret_cast<uint4*>(vo + dst) = *reinterpret_cast<const uint4*>(v + src);
+  }
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct WsLayout {
+  size_t rowstat, rowfinal, colscore, pooled, total;
+};
+
+WsLayout ws_layout(int B, int H, int N, int Lobs) {
+  const size_t bh = (size_t)B * H;
+  const size_t tiles = (size_t)(N + kTileKeys - 1) / kTileKeys;
+  const size_t np = (size_t)(N - Lobs);
+  WsLayout w;
+  w.rowstat = 0;
+  w.rowfinal = align256(w.rowstat + bh * tiles * kMaxRows * 2 * sizeof(float));
+  w.colscore = align256(w.rowfinal + bh * kMaxRows * 2 * sizeof(float));
+  w.pooled = align256(w.colscore + bh * (np ? np : 1) * sizeof(float));
+  w.total = align256(w.pooled + bh * (np ? np : 1) * sizeof(float));
+  return w;
+}
+
+template <int D>
+hipError_t launch_d(SnapkvParams p, hipStream_t s) {
+  const dim3 sgrid(p.tiles, p.H, p.B);
+  const bool two = p.Lobs > 32;
+  if (two)
+    hipLaunchKernelGGL((snapkv_rowstats_kernel<D, 2>), sgrid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((snapkv_rowstats_kernel<D, 1>), sgrid, dim3(256), 0, s, p);
+  hipLaunchKernelGGL(snapkv_rowfinal_kernel, dim3(p.B * p.H), dim3(kFinalThreads), 0, s, p);
+  const int np = p.N - p.Lobs;
+  if (np > 0) {
+    const dim3 cgrid((np + kTileKeys - 1) / kTileKeys, p.H, p.B);
+    if (two)
+      hipLaunchKernelGGL((snapkv_colscore_kernel<D, 2>), cgrid, dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL((snapkv_colscore_kernel<D, 1>), cgrid, dim3(256), 0, s, p);
+  }
+  if (np > 0) {
+    const size_t work = (size_t)p.B * p.H * np;
+    const size_t blocks = (work + 255) / 256;
+    hipLaunchKernelGGL(snapkv_pool_kernel, dim3(blocks < 8192 ? blocks : 8192), dim3(256), 0, s, p);
+  }
+  const int per = (np + kSelectThreads - 1) / kSelectThreads;
+  const dim3 sel_grid(p.H, p.B);
+  if (per <= 8)
+    hipLaunchKernelGGL(snapkv_select_kernel<8>, sel_grid, dim3(kSelectThreads), 0, s, p);
+  else if (per <= 16)
+    hipLaunchKernelGGL(snapkv_select_kernel<16>, sel_grid, dim3(kSelectThreads), 0, s, p);
+  else if (per <= 32)
+    hipLaunchKernelGGL(snapkv_select_kernel<32>, sel_grid, dim3(kSelectThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL(snapkv_select_kernel<64>, sel_grid, dim3(kSelectThreads), 0, s, p);
+  const int rows = p.k_keep + p.Lobs;
+  const int chunks = p.D * 2 / 16;
+  const int blocks_x = (rows * chunks + 255) / 256;
+  hipLaunchKernelGGL(snapkv_gather_kernel, dim3(blocks_x < 1024 ? blocks_x : 1024, p.H, p.B), dim3(256), 0, s, p,
+                     rows);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t snapkv_ws_bytes(int B, int H, int N, int Lobs) { return ws_layout(B, H, N, Lobs).total; }
+
+hipError_t launch_snapkv(const SnapkvParams& in, hipStream_t s) {
+  SnapkvParams p = in;
+  const WsLayout w = ws_layout(p.B, p.H, p.N, p.Lobs);
+  char* base = reinterpret_cast<char*>(p.rowstat);
+  p.rowstat = reinterpret_cast<float*>(base + w.rowstat);
+  p.rowfinal = reinterpret_cast<float*>(base + w.rowfinal);
+  p.colscore = reinterpret_cast<float*>(base + w.colscore);
+  p.pooled = reinterpret_cast<float*>(base + w.pooled);
+  p.tiles = (p.N + kTileKeys - 1) / kTileKeys;
+  switch (p.D) {
+    case 64: return launch_d<64>(p, s);
+    case 128: return launch_d<128>(p, s);
+    case 256: return launch_d<256>(p, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace lcd

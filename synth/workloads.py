@@ -233,6 +233,39 @@ class Workload:
         return st.values(idx, scale) if f64 else st.stored(idx, scale)
 
 
+def h2o_state_torch(w: Workload, device):
+    """The seeded H2O state of every (row, KV head) on ``device``.
+
+    Returns (K, V [B][Hkv][C][D] in the cache dtype, positions int32 [B][Hkv][C],
+    scores float32 [B][Hkv][C]) with slots in ascending position order, the layout an
+    H2O cache holds after being seeded in place.
+    """
+    import torch
+
+    B, H, C, D = w.batch, w.n_kv_heads, w.budget, w.head_dim
+    dt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    K = torch.empty((B, H, C, D), dtype=dt, device=device)
+    V = torch.empty_like(K)
+    P = torch.empty((B, H, C), dtype=torch.int32, device=device)
+    S = torch.empty((B, H, C), dtype=torch.float32, device=device)
+    T = w.total_tokens
+    d = torch.arange(D, device=device, dtype=torch.int64)
+    for b in range(B):
+        for g in range(H):
+            pos, sc, planted = w.h2o_initial_state(b, g)
+            pt = torch.from_numpy(pos).to(device)
+            idx = ((pt[:, None] * B + b) * H + g) * D + d[None, :]
+            kk = w.stream("k", 0).torch_stored(idx)
+            pl = torch.from_numpy(np.flatnonzero(planted)).to(device)
+            kk[pl] = w.stream("k", 0).torch_stored(idx[pl], w.plant_scale)
+            K[b, g] = kk
+            V[b, g] = w.stream("v", 0).torch_stored(idx)
+            P[b, g] = pt.to(torch.int32)
+            S[b, g] = torch.from_numpy(sc).to(device)
+    assert T > int(P.max())
+    return K, V, P, S
+
+
 def _streaming(name, title, **kw):
     return Workload(name=name, title=title, kind="streaming", **kw)
 

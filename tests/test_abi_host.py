@@ -99,7 +99,7 @@ def test_null_handle_calls_fail_cleanly(L):
     assert e.value.name == "LCD_EINVAL"
     assert L.kv_tokens(None, 0) == -1 and L.kv_slot_of(None, 0, 5) == -1 and L.kv_rank_of(None, 0, 1) == -1
     with pytest.raises(L.LcdError):
-        L.kv_set_filled(None, 0, 1, 1)
+        L.kv_set_filled(None, 0, 1, 1, 0)
 
 
 def test_snapkv_param_validation(L):

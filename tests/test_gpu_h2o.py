@@ -1,0 +1,117 @@
+"""GPU parity: H2O budgeted decode (kv_append + decode_attn, H2O policy) vs the oracle.
+
+Lockstep per sampled (batch row, KV head): every step's outputs (2e-3 abs, 1e-2 row
+relative) and the cache contents (the set of token positions, i.e. the evicted token)
+must match the fp64 oracle.  If the GPU evicts a different token whose oracle score is
+within 1e-6 relative of the oracle's choice (a near-tie), that head's comparison stops
+there: the oracle is never fed GPU state.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from synth import WORKLOADS
+from synth.workloads import h2o_state_torch, scaled
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    import long_context_decode_amd as lib
+
+    return lib
+
+
+def _run(L, w, steps, sample, seeded):
+    dev = "cuda"
+    B, Hq, Hkv, D, C, R = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.budget, w.n_recent
+    G = Hq // Hkv
+    cache = L.KVCache(L.cache_config(B, Hq, Hkv, D, L.LCD_BF16, L.LCD_H2O, capacity=C, n_recent=R))
+    heads = {}
+    t0 = w.n_prompt if seeded else 0
+    if seeded:
+        K, V, P, S = h2o_state_torch(w, dev)
+        kview, vview = cache.layer_tensors(0)
+        pview, sview = cache.h2o_tensors(0)
+        kview.copy_(K)
+        vview.copy_(V)
+        pview.copy_(P)
+        sview.copy_(S)
+        L.kv_set_filled(cache.handle, 0, C, t0)
+        for (b, g) in sample:
+            pos, sc, _ = w.h2o_initial_state(b, g)
+            heads[(b, g)] = oracle.H2OHead(C, R, pos, w.h2o_kv("k", b, g, pos), w.h2o_kv("v", b, g, pos), sc)
+    else:
+        for (b, g) in sample:
+            heads[(b, g)] = oracle.H2OHead(C, R)
+    q_all = w.token_major_torch("q", 0, t0, t0 + steps, dev)
+    k_all = w.token_major_torch("k", 0, t0, t0 + steps, dev)
+    v_all = w.token_major_torch("v", 0, t0, t0 + steps, dev)
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    pview, _ = cache.h2o_tensors(0)
+    live = dict.fromkeys(sample, True)
+    compared = 0
+    evictions = 0
+    for s in range(steps):
+        t = t0 + s
+        cache.append(0, k_all[s].unsqueeze(2), v_all[s].unsqueeze(2))
+        cache.decode(0, q_all[s], out)
+        got = out.cpu().numpy().astype(np.float64)
+        pos_gpu = pview.cpu().numpy()
+        for (b, g) in sample:
+            if not live[(b, g)]:
+                continue
+            hd = heads[(b, g)]
+            before = dict(zip(hd.pos, hd.s))
+            q = w.token_block("q", 0, [t], batches=[b], heads=np.arange(g * G, g * G + G))[0, :, 0, :]
+            k = w.token_block("k", 0, [t], batches=[b], heads=[g])[0, 0, 0]
+            v = w.token_block("v", 0, [t], batches=[b], heads=[g])[0, 0, 0]
+            ref, ev = hd.step(t, q, k, v)
+            n = min(t - t0 + 1 + (C if seeded else 0), C)
+            gpu_set = set(pos_gpu[b, g, :n].tolist())
+            if gpu_set != set(hd.pos):
+                gone = sorted(set(before) - gpu_set)
+                assert ev is not None and len(gone) == 1, f"t={t} b={b} g={g}: cache sets differ"
+                a, o = np.float32(before[gone[0]]), np.float32(before[ev])
+                gap = abs(float(a) - float(o)) / max(float(o), 1e-30)
+                print(f"  near-tie at t={t} b={b} g={g}: gpu evicted {gone[0]}, oracle {ev}, rel gap {gap:.2e}")
+                assert gap <= 1e-6, f"eviction differs beyond a near-tie ({gap:.2e})"
+                live[(b, g)] = False
+                continue
+            evictions += ev is not None
+            err = np.abs(got[b, g * G:(g + 1) * G] - ref)
+            rel = np.linalg.norm(got[b, g * G:(g + 1) * G] - ref, axis=-1) / np.linalg.norm(ref, axis=-1)
+            assert err.max() <= 2e-3 and rel.max() <= 1e-2, f"t={t} b={b} g={g}: {err.max():.2e} {rel.max():.2e}"
+            compared += 1
+    torch.cuda.synchronize()
+    return compared, evictions
+
+
+def test_h2o_from_empty_small(L):
+    w = scaled(WORKLOADS["h2o_128k"], name="h2o_small", batch=2, n_q_heads=8, n_kv_heads=2, n_prompt=0,
+               budget=64, n_recent=8, steps=220)
+    sample = [(b, g) for b in range(2) for g in range(2)]
+    compared, ev = _run(L, w, 220, sample, seeded=False)
+    print(f"[h2o small] compared {compared} head-steps, {ev} evictions")
+    assert compared >= 4 * 150 and ev > 100
+
+
+def test_h2o_sliding_window_case(L):
+    # n_recent == budget: the oldest token is always the victim
+    w = scaled(WORKLOADS["h2o_128k"], name="h2o_window", batch=1, n_q_heads=4, n_kv_heads=1, head_dim=64,
+               n_prompt=0, budget=40, n_recent=40, steps=120)
+    compared, ev = _run(L, w, 120, [(0, 0)], seeded=False)
+    assert compared == 120 and ev == 80
+
+
+def test_h2o_full_size_seeded(L):
+    """B=16, 32/8 heads, D=128, budget 4096 (512 recent), seeded 128k state; 3 heads in lockstep."""
+    w = WORKLOADS["h2o_128k"]
+    print(f"[h2o_128k] {w.title}", flush=True)
+    compared, ev = _run(L, w, 200, [(0, 0), (7, 5), (15, 7)], seeded=True)
+    print(f"  compared {compared} head-steps, {ev} evictions")
+    assert compared >= 3 * 100 and ev >= 100
