@@ -1,14 +1,17 @@
 #!/usr/bin/env python3
 """Decode throughput of the compressed-KV library on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--only]
 
-A step is one decode step of the whole hot path on one batch: append the new
-token's K/V to every layer's cache (kv_append) and attend over it (decode_attn).
-Inputs are synthetic (seeded, synth/), already resident in HBM when the timed
-region starts.  Prints ONE JSON line with steps/s, achieved HBM bandwidth of the
-decode kernel (HIP events around every decode_attn launch, on the launch stream)
-against the 8 TB/s peak, and the fp64 CPU oracle timed on a bounded sample.
+A step is one decode step of the whole hot path on one batch: for every layer,
+append the new token's K/V (kv_append) and attend over the cache (decode_attn).
+Inputs are synthetic (seeded, synth/) and already resident in HBM when the timed
+region starts.  Prints ONE JSON line: the headline workload (the Llama-2-7B-shaped
+layer with a 4+2044 sink + ring cache) with steps/s, the decode kernel's achieved
+HBM bandwidth against the 8 TB/s peak (HIP events around every decode_attn launch,
+on the launch stream), the SnapKV compression time, secondary decode workloads
+(the 16-layer GQA 32k cache, the H2O 4096 budget, the tiny fp32 stream) unless
+--only, and the fp64 CPU oracle timed on a bounded sample of the headline step.
 """
 from __future__ import annotations
 
@@ -22,19 +25,21 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK = 8.0e12  # B/s, MI355X HBM3E
+MFMA_BF16_PEAK = 2.5e15  # flop/s, dense
 METRIC = "decode steps/s + achieved HBM TB/s (% of peak); SnapKV compress ms"
+DEFAULTS = {"llama2_7b_layer": (8192, 64), "gqa_long": (64, 4), "h2o_128k": (1024, 32), "tiny_streaming": (448, 64)}
 
 
 def _parse(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=None, help="timed steps (default: per workload)")
+    ap.add_argument("--steps", type=int, default=None, help="timed steps of the headline workload")
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="llama2_7b_layer",
-                    choices=["llama2_7b_layer", "gqa_long", "tiny_streaming"])
+    ap.add_argument("--workload", default="llama2_7b_layer", choices=sorted(DEFAULTS))
+    ap.add_argument("--only", action="store_true", help="skip the secondary workloads and SnapKV")
+    ap.add_argument("--no-snapkv", action="store_true", help="skip the SnapKV compression timing")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="bound of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-snapkv", action="store_true", help="skip the SnapKV compression timing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args(argv)
@@ -53,83 +58,120 @@ def _copy_calibration():
     del src, dst
 
 
-def _streaming_bench(L, w, steps, warmup):
-    import torch
+class _Stepper:
+    """Owns a cache, its staged per-step inputs and the step function."""
 
-    dev = "cuda"
-    cfg = L.cache_config(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim,
-                         L.LCD_F32 if w.dtype == "f32" else L.LCD_BF16, L.LCD_SINK_RING, n_layers=w.n_layers,
-                         n_sink=w.n_sink, window=w.window, rope=1, rope_base=w.rope_base)
-    cache = L.KVCache(cfg, device=dev)
-    for layer in range(w.n_layers):
-        if w.prefill:
-            k = w.token_block_torch("k", layer, 0, w.prefill, dev)
-            v = w.token_block_torch("v", layer, 0, w.prefill, dev)
-            cache.append(layer, k, v)
-            del k, v
-    n_tok = warmup + steps
-    t0 = w.prefill
-    q = [w.token_major_torch("q", l, t0, t0 + n_tok, dev) for l in range(w.n_layers)]
-    k = [w.token_major_torch("k", l, t0, t0 + n_tok, dev) for l in range(w.n_layers)]
-    v = [w.token_major_torch("v", l, t0, t0 + n_tok, dev) for l in range(w.n_layers)]
-    out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device=dev)
-    torch.cuda.synchronize()
+    def __init__(self, L, w, n_tokens, dev="cuda"):
+        import torch
 
-    def step(i, ev=None):
-        for l in range(w.n_layers):
-            cache.append(l, k[l][i].unsqueeze(2), v[l][i].unsqueeze(2))
+        self.L, self.w, self.dev = L, w, dev
+        dt = L.LCD_F32 if w.dtype == "f32" else L.LCD_BF16
+        if w.kind == "streaming":
+            cfg = L.cache_config(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, dt, L.LCD_SINK_RING,
+                                 n_layers=w.n_layers, n_sink=w.n_sink, window=w.window, rope=1,
+                                 rope_base=w.rope_base)
+            self.cache = L.KVCache(cfg, device=dev)
+            for layer in range(w.n_layers):
+                if w.prefill:
+                    k = w.token_block_torch("k", layer, 0, w.prefill, dev)
+                    v = w.token_block_torch("v", layer, 0, w.prefill, dev)
+                    self.cache.append(layer, k, v)
+                    del k, v
+            self.t0 = w.prefill
+            self.slots = w.n_sink + w.window
+        else:  # h2o
+            from synth.workloads import h2o_state_torch
+
+            cfg = L.cache_config(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, dt, L.LCD_H2O,
+                                 capacity=w.budget, n_recent=w.n_recent)
+            self.cache = L.KVCache(cfg, device=dev)
+            K, V, P, S = h2o_state_torch(w, dev)
+            kv, vv = self.cache.layer_tensors(0)
+            pv, sv = self.cache.h2o_tensors(0)
+            kv.copy_(K)
+            vv.copy_(V)
+            pv.copy_(P)
+            sv.copy_(S)
+            del K, V, P, S
+            L.kv_set_filled(self.cache.handle, 0, w.budget, w.n_prompt)
+            self.t0 = w.n_prompt
+            self.slots = w.budget
+        self.q = [w.token_major_torch("q", l, self.t0, self.t0 + n_tokens, dev) for l in range(w.n_layers)]
+        self.k = [w.token_major_torch("k", l, self.t0, self.t0 + n_tokens, dev) for l in range(w.n_layers)]
+        self.v = [w.token_major_torch("v", l, self.t0, self.t0 + n_tokens, dev) for l in range(w.n_layers)]
+        self.out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+        self.i = 0
+        torch.cuda.synchronize()
+
+    def step(self, ev=None):
+        i = self.i
+        for l in range(self.w.n_layers):
+            self.cache.append(l, self.k[l][i].unsqueeze(2), self.v[l][i].unsqueeze(2))
             if ev is not None:
                 ev[0][l].record()
-            cache.decode(l, q[l][i], out)
+            self.cache.decode(l, self.q[l][i], self.out)
             if ev is not None:
                 ev[1][l].record()
+        self.i += 1
 
-    for i in range(warmup):
-        step(i)
+    def launch_bytes(self):
+        """Algorithmic bytes of one decode_attn launch (one layer)."""
+        w = self.w
+        kv = 2 * w.batch * w.n_kv_heads * self.slots * w.head_dim * w.esize
+        io = w.batch * w.n_q_heads * w.head_dim * (w.esize + 4)  # q in, fp32 out
+        if w.kind == "h2o":
+            logits = 2 * w.batch * w.n_q_heads * self.slots * 4  # written then read
+            state = w.batch * w.n_kv_heads * self.slots * (4 + 4 + 4)  # score read+write, pos read
+            return kv + io + logits + state
+        return kv + io
+
+    def step_bytes(self):
+        w = self.w
+        append = 2 * w.batch * w.n_kv_heads * w.head_dim * w.esize
+        return w.n_layers * (self.launch_bytes() + append)
+
+
+def _decode_bench(L, w, steps, warmup):
+    import torch
+
+    ev_steps = min(steps, 256)
+    st = _Stepper(L, w, warmup + steps + ev_steps)
+    for _ in range(warmup):
+        st.step()
     torch.cuda.synchronize()
-    # timed region 1: the steps alone
+    # timed region: the steps alone
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
-    for i in range(warmup, warmup + steps):
-        step(i)
+    for _ in range(steps):
+        st.step()
     end.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
-    # timed region 2: the same number of steps again (continuing the stream), with an
-    # event pair around every decode_attn launch for the kernel's own duration
-    ev_steps = min(steps, 512)
-    evs = [([torch.cuda.Event(enable_timing=True) for _ in range(w.n_layers)],
-            [torch.cuda.Event(enable_timing=True) for _ in range(w.n_layers)]) for _ in range(ev_steps)]
-    kq = [w.token_major_torch("q", l, t0 + n_tok, t0 + n_tok + ev_steps, dev) for l in range(w.n_layers)]
-    kk = [w.token_major_torch("k", l, t0 + n_tok, t0 + n_tok + ev_steps, dev) for l in range(w.n_layers)]
-    kv_ = [w.token_major_torch("v", l, t0 + n_tok, t0 + n_tok + ev_steps, dev) for l in range(w.n_layers)]
-    torch.cuda.synchronize()
+    # the following steps with an event pair around every decode_attn launch
+    nl = w.n_layers
+    evs = [([torch.cuda.Event(enable_timing=True) for _ in range(nl)],
+            [torch.cuda.Event(enable_timing=True) for _ in range(nl)]) for _ in range(ev_steps)]
     for i in range(ev_steps):
-        for l in range(w.n_layers):
-            cache.append(l, kk[l][i].unsqueeze(2), kv_[l][i].unsqueeze(2))
-            evs[i][0][l].record()
-            cache.decode(l, kq[l][i], out)
-            evs[i][1][l].record()
+        st.step(evs[i])
     torch.cuda.synchronize()
-    kern_ms = [evs[i][0][l].elapsed_time(evs[i][1][l]) for i in range(ev_steps) for l in range(w.n_layers)]
-    kern_ms.sort()
+    kern_ms = sorted(evs[i][0][l].elapsed_time(evs[i][1][l]) for i in range(ev_steps) for l in range(nl))
     avg_kernel_ms = sum(kern_ms) / len(kern_ms)
-    C = w.n_sink + w.window
-    kv_bytes = 2 * w.batch * w.n_kv_heads * C * w.head_dim * w.esize  # one layer, full cache
-    io_bytes = w.batch * w.n_q_heads * w.head_dim * (w.esize + 4)     # q in, fp32 out
-    launch_bytes = kv_bytes + io_bytes
-    step_bytes = w.n_layers * (launch_bytes + 2 * w.batch * w.n_kv_heads * w.head_dim * w.esize)
-    res = dict(
-        steps_per_s=steps / (total_ms / 1e3),
-        ms_per_step=total_ms / steps,
-        avg_kernel_ms=avg_kernel_ms,
-        median_kernel_ms=kern_ms[len(kern_ms) // 2],
-        launch_bytes=launch_bytes,
-        step_bytes=step_bytes,
-        kernel_launches=len(kern_ms),
-    )
-    cache.close()
+    res = dict(steps_per_s=steps / (total_ms / 1e3), ms_per_step=total_ms / steps, avg_kernel_ms=avg_kernel_ms,
+               median_kernel_ms=kern_ms[len(kern_ms) // 2], launch_bytes=st.launch_bytes(),
+               step_bytes=st.step_bytes(), kernel_launches=len(kern_ms))
+    st.cache.close()
+    del st
+    torch.cuda.empty_cache()
     return res
+
+
+def _summary(w, r):
+    achieved = r["launch_bytes"] / (r["avg_kernel_ms"] / 1e3)
+    return {"workload": w.title, "steps_per_s": round(r["steps_per_s"], 2), "ms_per_step": round(r["ms_per_step"], 5),
+            "hbm_tb_s": round(r["step_bytes"] * r["steps_per_s"] / 1e12, 3),
+            "decode_launch_us": round(r["avg_kernel_ms"] * 1e3, 2),
+            "decode_launch_gb_s": round(achieved / 1e9, 1), "decode_launch_frac": round(achieved / HBM_PEAK, 4),
+            "bytes_per_launch": r["launch_bytes"]}
 
 
 def _snapkv_bench(L, w, reps=20):
@@ -169,7 +211,7 @@ def _snapkv_bench(L, w, reps=20):
             "algorithmic_bytes": alg_bytes, "hbm_gb_s": round(alg_bytes / (ms / 1e3) / 1e9, 1),
             "hbm_frac": round(alg_bytes / (ms / 1e3) / HBM_PEAK, 4),
             "qk_tflops": round(flops / (ms / 1e3) / 1e12, 2),
-            "mfma_frac_bf16": round(flops / (ms / 1e3) / 2.5e15, 5)}
+            "mfma_frac_bf16": round(flops / (ms / 1e3) / MFMA_BF16_PEAK, 5)}
 
 
 def _cpu_baseline_streaming(w, budget_s):
@@ -232,13 +274,10 @@ def main(argv=None):
     if a.copy_calibration:
         _copy_calibration()
     w = WORKLOADS[a.workload]
-    defaults = {"llama2_7b_layer": (8192, 64), "gqa_long": (128, 4), "tiny_streaming": (448, 64)}
-    steps, warmup = defaults[a.workload]
+    steps, warmup = DEFAULTS[a.workload]
     steps = a.steps if a.steps is not None else steps
     warmup = a.warmup if a.warmup is not None else warmup
-    if a.workload == "tiny_streaming":
-        warmup = min(warmup, w.steps)
-    r = _streaming_bench(L, w, steps, warmup)
+    r = _decode_bench(L, w, steps, warmup)
     achieved = r["launch_bytes"] / (r["avg_kernel_ms"] / 1e3)
     line = {
         "metric": METRIC,
@@ -254,8 +293,8 @@ def main(argv=None):
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.title, "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
-                   "head_dim": w.head_dim, "n_layers": w.n_layers, "cache_slots": w.n_sink + w.window,
-                   "n_sink": w.n_sink, "window": w.window},
+                   "head_dim": w.head_dim, "n_layers": w.n_layers,
+                   "cache_slots": w.n_sink + w.window if w.kind == "streaming" else w.budget},
         "hbm_tb_s": round(r["step_bytes"] * r["steps_per_s"] / 1e12, 3),
         "hbm_frac_of_peak": round(r["step_bytes"] * r["steps_per_s"] / HBM_PEAK, 4),
         "roofline": {"bound": "hbm", "kernel": "decode_split_kernel (lcd_decode_attn)",
@@ -265,9 +304,19 @@ def main(argv=None):
                      "median_launch_us": round(r["median_kernel_ms"] * 1e3, 2),
                      "launches_timed": r["kernel_launches"]},
     }
-    if not a.no_snapkv:
+    if not a.only and not a.no_snapkv:
         line["snapkv"] = _snapkv_bench(L, WORKLOADS["snapkv_32k"])
-    if not a.no_cpu_baseline:
+    if not a.only:
+        others = []
+        for name in ("gqa_long", "h2o_128k", "tiny_streaming"):
+            if name == a.workload:
+                continue
+            s2, w2 = DEFAULTS[name]
+            if name == "tiny_streaming":
+                w2 = min(w2, WORKLOADS[name].steps - s2)
+            others.append(_summary(WORKLOADS[name], _decode_bench(L, WORKLOADS[name], s2, w2)))
+        line["other_workloads"] = others
+    if not a.no_cpu_baseline and w.kind == "streaming":
         line["cpu_baseline"] = _cpu_baseline_streaming(w, a.cpu_seconds)
     print(json.dumps(line), flush=True)
     return 0

@@ -192,53 +192,77 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodePara
     }
   }
 
-  // ---- K pass: U keys per lane group per iteration, every load issued first
+  // ---- K pass: U keys per lane group per iteration, every load issued first.
+  // With RoPE, the lane's U keys of one iteration sit KPI slots apart; where their
+  // in-cache positions are also KPI apart (everywhere except across the ring's wrap
+  // point and the sink boundary) the cos/sin of key u+1 follow from key u's by one
+  // angle addition with the per-lane constant rotation (cos, sin)(KPI * theta_i), so
+  // only one table row is read per iteration.  Waves that straddle a discontinuity
+  // read every key's row from the table instead.
   constexpr int U = (G <= 2) ? 4 : 2;
   float mx[G];
 #pragma unroll
   for (int j = 0; j < G; ++j) mx[j] = -INFINITY;
+  float dc[HALF], ds[HALF];
+  if constexpr (ROPE) {
+#pragma unroll
+    for (int e = 0; e < HALF; ++e) {
+      dc[e] = p.cos_t[(size_t)KPI * D2 + i0 + e];
+      ds[e] = p.sin_t[(size_t)KPI * D2 + i0 + e];
+    }
+  }
+  auto rank_of = [&](int slot) {
+    int rank = slot;
+    if (p.full && slot >= p.S) {
+      int r = slot - p.S - p.ring_head;
+      if (r < 0) r += p.W;
+      rank = p.S + r;
+    }
+    return rank;
+  };
+  auto load_cs = [&](int rank, float (&c)[HALF], float (&sn)[HALF]) {
+    const float4* cr = reinterpret_cast<const float4*>(p.cos_t + (size_t)rank * D2 + i0);
+    const float4* sr = reinterpret_cast<const float4*>(p.sin_t + (size_t)rank * D2 + i0);
+#pragma unroll
+    for (int e = 0; e < HALF / 4; ++e) {
+      const float4 c4 = cr[e], s4 = sr[e];
+      c[4 * e] = c4.x; c[4 * e + 1] = c4.y; c[4 * e + 2] = c4.z; c[4 * e + 3] = c4.w;
+      sn[4 * e] = s4.x; sn[4 * e + 1] = s4.y; sn[4 * e + 2] = s4.z; sn[4 * e + 3] = s4.w;
+    }
+  };
 
   for (int base = 0; base < cnt; base += KPI * U) {
+    const int key0 = base + wave * KPW + kg;
     uint4 rlo[U], rhi[U];
-    float4 c4[U][HALF / 4], s4[U][HALF / 4];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int key = base + u * KPI + wave * KPW + kg;
+      const int key = key0 + u * KPI;
       if (key < cnt) {
-        const int slot = s_begin + key;
-        const char* row = kbase + (size_t)slot * D * sizeof(T);
+        const char* row = kbase + (size_t)(s_begin + key) * D * sizeof(T);
         rlo[u] = load16(row + lo_off);
         rhi[u] = load16(row + hi_off);
-        if constexpr (ROPE) {
-          int rank = slot;
-          if (p.full && slot >= p.S) {
-            int r = slot - p.S - p.ring_head;
-            if (r < 0) r += p.W;
-            rank = p.S + r;
-          }
-          const float4* cr = reinterpret_cast<const float4*>(p.cos_t + (size_t)rank * D2 + i0);
-          const float4* sr = reinterpret_cast<const float4*>(p.sin_t + (size_t)rank * D2 + i0);
-#pragma unroll
-          for (int e = 0; e < HALF / 4; ++e) {
-            c4[u][e] = cr[e];
-            s4[u][e] = sr[e];
-          }
-        }
       } else {
         rlo[u] = make_uint4(0, 0, 0, 0);
         rhi[u] = make_uint4(0, 0, 0, 0);
-        if constexpr (ROPE) {
-#pragma unroll
-          for (int e = 0; e < HALF / 4; ++e) {
-            c4[u][e] = make_float4(0.f, 0.f, 0.f, 0.f);
-            s4[u][e] = make_float4(0.f, 0.f, 0.f, 0.f);
-          }
-        }
       }
+    }
+    float c[HALF], sn[HALF];
+    bool stepwise = false;  // this wave straddles a rank discontinuity
+    int rank0 = 0;
+    if constexpr (ROPE) {
+      rank0 = rank_of(s_begin + min(key0, cnt - 1));
+      bool disc = false;
+#pragma unroll
+      for (int u = 1; u < U; ++u) {
+        const int key = key0 + u * KPI;
+        disc |= key < cnt && rank_of(s_begin + key) != rank0 + u * KPI;
+      }
+      stepwise = __any(disc);
+      load_cs(rank0, c, sn);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int key = base + u * KPI + wave * KPW + kg;
+      const int key = key0 + u * KPI;
       const bool valid = key < cnt;
       float kf[EPL];
       {
@@ -246,8 +270,18 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodePara
         Elem<T>::cvt(rlo[u], lo);
         Elem<T>::cvt(rhi[u], hi);
         if constexpr (ROPE) {
-          const float* c = reinterpret_cast<const float*>(c4[u]);
-          const float* sn = reinterpret_cast<const float*>(s4[u]);
+          if (u > 0) {
+            if (stepwise) {
+              load_cs(rank_of(s_begin + min(key, cnt - 1)), c, sn);
+            } else {
+#pragma unroll
+              for (int e = 0; e < HALF; ++e) {
+                const float cc = c[e] * dc[e] - sn[e] * ds[e];
+                sn[e] = sn[e] * dc[e] + c[e] * ds[e];
+                c[e] = cc;
+              }
+            }
+          }
 #pragma unroll
           for (int e = 0; e < HALF; ++e) {
             kf[e] = lo[e] * c[e] - hi[e] * sn[e];
@@ -277,6 +311,25 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodePara
       }
     }
   }
+
+  // first V rows are requested before the softmax barriers (their latency overlaps them)
+  constexpr int UV = 4;
+  uint4 vlo[UV], vhi[UV];
+  auto load_v = [&](int base) {
+#pragma unroll
+    for (int u = 0; u < UV; ++u) {
+      const int key = base + u * KPI + wave * KPW + kg;
+      if (key < cnt) {
+        const char* row = vbase + (size_t)(s_begin + key) * D * sizeof(T);
+        vlo[u] = load16(row + lo_off);
+        vhi[u] = load16(row + hi_off);
+      } else {
+        vlo[u] = make_uint4(0, 0, 0, 0);
+        vhi[u] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  load_v(0);
 
   // ---- range maximum per query head
 #pragma unroll
@@ -310,8 +363,8 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodePara
   }
   __syncthreads();
 
-  // ---- V pass: UV rows per lane group per iteration, loads issued first
-  constexpr int UV = 4;
+  // ---- V pass: UV rows per lane group per iteration; the next iteration's rows are
+  // requested before this iteration's arithmetic (software pipelining)
   float o[G][EPL];
 #pragma unroll
   for (int j = 0; j < G; ++j)
@@ -319,26 +372,20 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodePara
     for (int e = 0; e < EPL; ++e) o[j][e] = 0.f;
 
   for (int base = 0; base < cnt; base += KPI * UV) {
-    uint4 rlo[UV], rhi[UV];
+    uint4 clo[UV], chi[UV];
 #pragma unroll
     for (int u = 0; u < UV; ++u) {
-      const int key = base + u * KPI + wave * KPW + kg;
-      if (key < cnt) {
-        const char* row = vbase + (size_t)(s_begin + key) * D * sizeof(T);
-        rlo[u] = load16(row + lo_off);
-        rhi[u] = load16(row + hi_off);
-      } else {
-        rlo[u] = make_uint4(0, 0, 0, 0);
-        rhi[u] = make_uint4(0, 0, 0, 0);
-      }
+      clo[u] = vlo[u];
+      chi[u] = vhi[u];
     }
+    if (base + KPI * UV < cnt) load_v(base + KPI * UV);
 #pragma unroll
     for (int u = 0; u < UV; ++u) {
       const int key = base + u * KPI + wave * KPW + kg;
       if (key < cnt) {
         float lo[HALF], hi[HALF];
-        Elem<T>::cvt(rlo[u], lo);
-        Elem<T>::cvt(rhi[u], hi);
+        Elem<T>::cvt(clo[u], lo);
+        Elem<T>::cvt(chi[u], hi);
 #pragma unroll
         for (int j = 0; j < G; ++j) {
           const float w = xs[key * G + j];

@@ -47,7 +47,7 @@ uint64_t align256(uint64_t x) { return (x + 255u) & ~uint64_t(255); }
 bool mul_ok(uint64_t* acc, uint64_t f) { return !__builtin_mul_overflow(*acc, f, acc); }
 
 constexpr int64_t kMaxSlots = int64_t(1) << 24;
-constexpr int kTargetWorkgroups = 2048;  // decode grid size aimed for (8 per CU on 256 CUs)
+constexpr int kTargetWorkgroups = 512;  // decode grid size aimed for (2 per CU on 256 CUs)
 
 int env_int(const char* name, int dflt) {
   const char* s = std::getenv(name);
@@ -125,7 +125,9 @@ lcd_status check_config(const lcd_cache_config* c, Layout* L) {
   uint64_t aux = align256((uint64_t)c->n_layers * c->batch * c->n_kv_heads * sizeof(int32_t));
   L->off_arrive = 0;
   if (c->rope == 1) {
-    const uint64_t tab = (uint64_t)C * (c->head_dim / 2) * sizeof(float);
+    // rows 0 .. max(C, 65) - 1: the decode kernel also reads the row of its per-lane
+    // step (at most 64 positions) for angle additions
+    const uint64_t tab = (uint64_t)std::max<int64_t>(C, 65) * (c->head_dim / 2) * sizeof(float);
     L->off_cos = aux;
     aux = align256(aux + tab);
     L->off_sin = aux;
@@ -262,7 +264,8 @@ lcd_status lcd_kv_cache_init(const lcd_cache_config* cfg, void* kv_mem, uint64_t
   c->qscale = (float)(scale * 1.4426950408889634074);  // scale * log2(e), rounded once
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = lcd::launch_fill_i32(c->arrivals(0), 0, (int64_t)cfg->n_layers * cfg->batch * cfg->n_kv_heads, s);
-  if (e == hipSuccess && cfg->rope) e = lcd::launch_rope_table(c->cos_t(), c->sin_t(), L.C, cfg->head_dim, cfg->rope_base, s);
+  if (e == hipSuccess && cfg->rope)
+    e = lcd::launch_rope_table(c->cos_t(), c->sin_t(), std::max(L.C, 65), cfg->head_dim, cfg->rope_base, s);
   if (e == hipSuccess && cfg->policy == LCD_H2O) {
     const int64_t n = (int64_t)cfg->n_layers * c->per_layer_slots();
     e = lcd::launch_fill_i32(c->pos(0), -1, n, s);
