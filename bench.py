@@ -8,8 +8,10 @@ append the new token's K/V (kv_append) and attend over the cache (decode_attn).
 Inputs are synthetic (seeded, synth/) and already resident in HBM when the timed
 region starts.  Prints ONE JSON line: the headline workload (the Llama-2-7B-shaped
 layer with a 4+2044 sink + ring cache) with steps/s, the decode kernel's achieved
-HBM bandwidth against the 8 TB/s peak (HIP events around every decode_attn launch,
-on the launch stream), the SnapKV compression time, secondary decode workloads
+HBM bandwidth against the 8 TB/s peak (HIP events on the launch stream around batches
+of back-to-back decode_attn launches), the decode kernel's counter-measured HBM traffic
+when the record under profiles/ matches the current kernel sources, the SnapKV
+compression time, secondary decode workloads
 (the 16-layer GQA 32k cache, the H2O 4096 budget, the tiny fp32 stream) unless
 --only, and the fp64 CPU oracle timed on a bounded sample of the headline step.
 """
@@ -42,7 +44,111 @@ def _parse(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
+                         "'bench.py --only --copy-calibration' into the traffic record and exit (no GPU)")
     return ap.parse_args(argv)
+
+
+# HBM traffic of the headline decode kernel, from profiler counters.  The record is tied to
+# the sources that decide the kernel's memory behaviour (the kernel and its launch plan);
+# when any of them changes the record is stale and the bench reports traffic as null.
+DECODE_KERNEL = "decode_onepass_kernel"  # the decode kernel the headline shape (1 query head per KV head) runs
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_onepass_kernel_llama2_b16_c2048_traffic.md")
+TRAFFIC_SOURCES = ("long_context_decode_amd/csrc/decode.hip", "long_context_decode_amd/csrc/lcd_internal.h",
+                   "long_context_decode_amd/csrc/lcd_host.cpp")
+COPY_BYTES = 1 << 30  # the calibration copy
+
+
+def _sources_digest():
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(rel.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def _read_counter_csv(path, counter):
+    """{dispatch id: (kernel name, grid size, value in KiB)} for one counter."""
+    import csv
+
+    out = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] != counter:
+                continue
+            d = int(row["Dispatch_Id"])
+            name, grid, val = row["Kernel_Name"], int(row["Grid_Size"]), float(row["Counter_Value"])
+            if d in out:  # one row per counter instance: sum them
+                val += out[d][2]
+            out[d] = (name, grid, val)
+    return out
+
+
+def _counter_summary(fetch_csv, write_csv):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE of the decode kernel, each scaled by what the
+    counter reads for the 1 GiB calibration copy; writes the traffic record."""
+    import statistics
+
+    res = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = _read_counter_csv(path, counter)
+        # the calibration copies are the process's first three device copies
+        copies = [rows[d][2] for d in sorted(rows) if "copyBuffer" in rows[d][0]][:3]
+        if len(copies) < 3 or max(copies) > 1.05 * min(copies):
+            raise SystemExit(f"{path}: no consistent calibration copy (run the bench with --copy-calibration)")
+        copy_kib = statistics.median(copies)
+        dec = [v for (n, g, v) in rows.values() if DECODE_KERNEL in n]
+        if not dec:
+            raise SystemExit(f"{path}: no {DECODE_KERNEL} dispatch")
+        res[counter] = dict(copy_kib=copy_kib, scale=COPY_BYTES / (copy_kib * 1024.0),
+                            decode_kib=statistics.mean(dec), dispatches=len(dec))
+    f, w = res["FETCH_SIZE"], res["WRITE_SIZE"]
+    traffic = f["decode_kib"] * 1024.0 * f["scale"] + w["decode_kib"] * 1024.0 * w["scale"]
+    lines = [
+        f"# {DECODE_KERNEL} HBM traffic — Llama-2-7B-shaped layer (B=16, 32/32 heads, D=128, bf16, 4+2044)",
+        "",
+        "Two rocprofv3 counter runs of the same command, one counter each:",
+        "",
+        "```",
+        "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/p17/fetch -o run -- "
+        "python3 bench.py --only --copy-calibration --steps 64 --warmup 8 --no-cpu-baseline",
+        "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/p17/write -o run -- "
+        "python3 bench.py --only --copy-calibration --steps 64 --warmup 8 --no-cpu-baseline",
+        "python3 bench.py --counters gpurun_out/p17/fetch/run_counter_collection.csv "
+        "gpurun_out/p17/write/run_counter_collection.csv",
+        "```",
+        "",
+        "The calibration copy moves 1 GiB in each direction; each counter is scaled by "
+        "1 GiB / (its reading for that copy).",
+        "",
+        "| counter | copy reads (KiB) | scale | decode kernel, mean per dispatch (KiB) | dispatches | scaled bytes |",
+        "|---|---|---|---|---|---|",
+    ]
+    for name, r in (("FETCH_SIZE", f), ("WRITE_SIZE", w)):
+        lines.append(f"| {name} | {r['copy_kib']:.1f} | {r['scale']:.4f} | {r['decode_kib']:.1f} | "
+                     f"{r['dispatches']} | {r['decode_kib'] * 1024 * r['scale']:.0f} |")
+    lines += ["", f"traffic-bytes-per-launch: {traffic:.0f}", f"sources-sha256: {_sources_digest()}",
+              f"sources: {', '.join(TRAFFIC_SOURCES)}", ""]
+    with open(TRAFFIC_RECORD, "w") as fh:
+        fh.write("\n".join(lines))
+    print(f"traffic {traffic:.0f} B per launch -> {TRAFFIC_RECORD}")
+
+
+def _traffic():
+    """Scaled counter bytes per launch of the headline decode kernel, or None when no
+    record exists or the record was taken on other sources."""
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            kv = dict(line.split(": ", 1) for line in f.read().splitlines() if ": " in line and
+                      line.split(": ", 1)[0] in ("traffic-bytes-per-launch", "sources-sha256"))
+    except OSError:
+        return None
+    if kv.get("sources-sha256", "").strip() != _sources_digest():
+        return None
+    return int(float(kv["traffic-bytes-per-launch"]))
 
 
 def _copy_calibration():
@@ -103,15 +209,11 @@ class _Stepper:
         self.i = 0
         torch.cuda.synchronize()
 
-    def step(self, ev=None):
+    def step(self):
         i = self.i
         for l in range(self.w.n_layers):
             self.cache.append(l, self.k[l][i].unsqueeze(2), self.v[l][i].unsqueeze(2))
-            if ev is not None:
-                ev[0][l].record()
             self.cache.decode(l, self.q[l][i], self.out)
-            if ev is not None:
-                ev[1][l].record()
         self.i += 1
 
     def launch_bytes(self):
@@ -131,11 +233,10 @@ class _Stepper:
         return w.n_layers * (self.launch_bytes() + append)
 
 
-def _decode_bench(L, w, steps, warmup):
+def _decode_bench(L, w, steps, warmup, launch_batches=4, launch_batch=64):
     import torch
 
-    ev_steps = min(steps, 256)
-    st = _Stepper(L, w, warmup + steps + ev_steps)
+    st = _Stepper(L, w, warmup + steps)
     for _ in range(warmup):
         st.step()
     torch.cuda.synchronize()
@@ -147,18 +248,23 @@ def _decode_bench(L, w, steps, warmup):
     end.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
-    # the following steps with an event pair around every decode_attn launch
+    # decode kernel duration: batches of back-to-back decode_attn launches on the state the
+    # steps left (every launch reads the full cache), one event pair per batch on the
+    # launch stream
     nl = w.n_layers
-    evs = [([torch.cuda.Event(enable_timing=True) for _ in range(nl)],
-            [torch.cuda.Event(enable_timing=True) for _ in range(nl)]) for _ in range(ev_steps)]
-    for i in range(ev_steps):
-        st.step(evs[i])
-    torch.cuda.synchronize()
-    kern_ms = sorted(evs[i][0][l].elapsed_time(evs[i][1][l]) for i in range(ev_steps) for l in range(nl))
-    avg_kernel_ms = sum(kern_ms) / len(kern_ms)
+    batch_ms = []
+    for _ in range(launch_batches):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(launch_batch):
+            st.cache.decode(i % nl, st.q[i % nl][0], st.out)
+        b.record()
+        torch.cuda.synchronize()
+        batch_ms.append(a.elapsed_time(b) / launch_batch)
+    avg_kernel_ms = sum(batch_ms) / len(batch_ms)
     res = dict(steps_per_s=steps / (total_ms / 1e3), ms_per_step=total_ms / steps, avg_kernel_ms=avg_kernel_ms,
-               median_kernel_ms=kern_ms[len(kern_ms) // 2], launch_bytes=st.launch_bytes(),
-               step_bytes=st.step_bytes(), kernel_launches=len(kern_ms))
+               min_batch_kernel_ms=min(batch_ms), launch_bytes=st.launch_bytes(),
+               step_bytes=st.step_bytes(), kernel_launches=launch_batches * launch_batch)
     st.cache.close()
     del st
     torch.cuda.empty_cache()
@@ -259,6 +365,9 @@ def _cpu_baseline_streaming(w, budget_s):
 
 def main(argv=None):
     a = _parse(argv)
+    if a.counters:
+        _counter_summary(*a.counters)
+        return 0
     if a.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus_requested": a.gpus}))
@@ -297,11 +406,12 @@ def main(argv=None):
                    "cache_slots": w.n_sink + w.window if w.kind == "streaming" else w.budget},
         "hbm_tb_s": round(r["step_bytes"] * r["steps_per_s"] / 1e12, 3),
         "hbm_frac_of_peak": round(r["step_bytes"] * r["steps_per_s"] / HBM_PEAK, 4),
-        "roofline": {"bound": "hbm", "kernel": "decode_split_kernel (lcd_decode_attn)",
+        "roofline": {"bound": "hbm", "kernel": DECODE_KERNEL + " (lcd_decode_attn)",
                      "achieved": round(achieved / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK, 4),
+                     "traffic": _traffic() if a.workload == "llama2_7b_layer" else None,
                      "bytes_per_launch": r["launch_bytes"], "avg_launch_us": round(r["avg_kernel_ms"] * 1e3, 2),
-                     "median_launch_us": round(r["median_kernel_ms"] * 1e3, 2),
+                     "best_batch_launch_us": round(r["min_batch_kernel_ms"] * 1e3, 2),
                      "launches_timed": r["kernel_launches"]},
     }
     if not a.only and not a.no_snapkv:

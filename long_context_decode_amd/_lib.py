@@ -42,6 +42,11 @@ class SnapkvParams(ctypes.Structure):
 
 
 def _load():
+    # torch supplies the device memory and streams handed to the library, so the
+    # library must run on torch's HIP runtime: importing torch first makes the
+    # dynamic linker resolve liblcd's libamdhip64 dependency to torch's copy.
+    import torch  # noqa: F401
+
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is missing: build it with `python long_context_decode_amd/build.py` "

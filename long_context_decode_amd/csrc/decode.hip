@@ -8,18 +8,18 @@
 // cache is split along the sequence ([KVC] "Implementação prática em vLLM e
 // SGLang": FlashDecoding parallelises along time), so the kernel is HBM-bound.
 //
-// Per workgroup:
-//   K pass  every key of the range is loaded once (two 16-byte loads per lane,
-//           one from each half of the row), rotated in registers at its in-cache
-//           position when keys are stored un-rotated ([SINK] "como funciona"),
-//           and dotted with the G pre-rotated, pre-scaled queries; the dot is
-//           reduced across the LPK lanes that share the key.  Logits go to LDS.
-//   softmax the range maximum per query head, p = 2^(x - m) in LDS, l = sum p.
-//   V pass  every value row is loaded once and accumulated with the G weights.
-//   merge   with one split the workgroup normalises and writes the output;
-//           otherwise it publishes (o, m, l) to the workspace and the last
-//           workgroup of its (b, g) to arrive merges all splits in split order
-//           (deterministic) and, for H2O, runs the score / eviction epilogue.
+// Per workgroup, one pass over the range: every lane group of LPK lanes owns one key
+// (and its value) at a time; the lanes load one LB-byte piece from each half of the
+// row, so each lane holds whole RoPE pairs (i, i + D/2) and rotates the key in
+// registers at its in-cache position when keys are stored un-rotated ([SINK] "como
+// funciona").  The group reduces the G dot products with DPP moves and keeps its own
+// running softmax state (max m, sum l, output o) over its keys (online softmax):
+// K and V rows of the next iteration are requested before the current one's
+// arithmetic, and nothing in the loop waits for another wave.  At the end the lane
+// groups of a wave, then the 4 waves, merge their (m, l, o).  With one split the
+// workgroup normalises and writes the output; otherwise it publishes (o, m, l) to the
+// workspace and the last workgroup of its (b, g) to arrive merges all splits in split
+// order (deterministic) and, for H2O, runs the score / eviction epilogue.
 // Logits are kept in the log2 domain (the query carries scale * log2 e) so the
 // exponentials are single exp2 instructions.
 #include <hip/hip_runtime.h>
@@ -38,46 +38,101 @@ struct bf16_t {
 #define LCD_NT_KV 1
 #endif
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-__device__ inline uint4 load16(const void* p) {
-#if LCD_NT_KV
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-#else
-  const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+// Keys per lane group per iteration, chosen by measurement on MI355X: the one-pass
+// kernel (G <= 2; two iterations in flight) and the two-pass kernel's K pass
+// (G = 4 and G = 6; two iterations in flight, 2 keys for G = 8).
+#ifndef LCD_U_G2
+#define LCD_U_G2 2
 #endif
-  return make_uint4(v.x, v.y, v.z, v.w);
+#ifndef LCD_U2_G4
+#define LCD_U2_G4 4
+#endif
+#ifndef LCD_U2_G6
+#define LCD_U2_G6 2
+#endif
+#ifndef LCD_H2O_EU
+#define LCD_H2O_EU 4  // H2O epilogue: slots per thread per iteration
+#endif
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// W 32-bit words of one row piece, loaded in one instruction (W = 4: 16 bytes, W = 2: 8).
+template <int W>
+struct Words {
+  uint32_t w[W];
+};
+
+template <int W>
+__device__ inline Words<W> load_words(const void* p) {
+  Words<W> r;
+  if constexpr (W == 4) {
+#if LCD_NT_KV
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+#else
+    const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+#endif
+    r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
+  } else {
+    static_assert(W == 2, "row pieces are 8 or 16 bytes");
+#if LCD_NT_KV
+    const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+#else
+    const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+#endif
+    r.w[0] = v.x; r.w[1] = v.y;
+  }
+  return r;
 }
 
-// Element formats.  HALF elements fill one 16-byte load; cvt widens to float32.
-template <typename T>
+template <int W>
+__device__ inline Words<W> zero_words() {
+  Words<W> r;
+#pragma unroll
+  for (int i = 0; i < W; ++i) r.w[i] = 0u;
+  return r;
+}
+
+// Element formats: N elements per W-word piece, widened to float32.
+template <typename T, int W>
 struct Elem;
 
-template <>
-struct Elem<float> {
-  static constexpr int HALF = 4;
-  __device__ static inline void cvt(const uint4 v, float (&x)[4]) {
-    x[0] = __uint_as_float(v.x);
-    x[1] = __uint_as_float(v.y);
-    x[2] = __uint_as_float(v.z);
-    x[3] = __uint_as_float(v.w);
+template <int W>
+struct Elem<float, W> {
+  static constexpr int N = W;
+  __device__ static inline void cvt(const Words<W>& v, float (&x)[N]) {
+#pragma unroll
+    for (int i = 0; i < W; ++i) x[i] = __uint_as_float(v.w[i]);
   }
-  __device__ static inline void load(const void* p, float (&x)[4]) { cvt(load16(p), x); }
 };
 
-template <>
-struct Elem<bf16_t> {
-  static constexpr int HALF = 8;
-  __device__ static inline void cvt(const uint4 v, float (&x)[8]) {
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+template <int W>
+struct Elem<bf16_t, W> {
+  static constexpr int N = 2 * W;
+  __device__ static inline void cvt(const Words<W>& v, float (&x)[N]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[2 * i] = __uint_as_float(w[i] << 16);
-      x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    for (int i = 0; i < W; ++i) {
+      x[2 * i] = __uint_as_float(v.w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(v.w[i] & 0xffff0000u);
     }
   }
-  __device__ static inline void load(const void* p, float (&x)[8]) { cvt(load16(p), x); }
 };
+
+// N consecutive floats (N = 2, 4 or 8) with 8- or 16-byte loads.
+template <int N>
+__device__ inline void load_floats(const float* p, float (&x)[N]) {
+  if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int e = 0; e < N / 4; ++e) {
+      const float4 v = reinterpret_cast<const float4*>(p)[e];
+      x[4 * e] = v.x; x[4 * e + 1] = v.y; x[4 * e + 2] = v.z; x[4 * e + 3] = v.w;
+    }
+  } else {
+    static_assert(N == 2, "table pieces are 2, 4 or 8 floats");
+    const float2 v = *reinterpret_cast<const float2*>(p);
+    x[0] = v.x; x[1] = v.y;
+  }
+}
 
 // DPP lane moves inside 16-lane rows (no LDS traffic).
 constexpr int kDppXor1 = 0xB1;          // quad_perm [1,0,3,2]
@@ -90,17 +145,33 @@ __device__ inline float dpp_mov(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
 
-// Sum over aligned groups of N consecutive lanes (N a power of two <= 64); every
-// lane of the group receives the total.  Groups up to 16 lanes use DPP.
-template <int N>
-__device__ inline float group_sum(float x) {
-  if constexpr (N >= 2) x += dpp_mov<kDppXor1>(x);
-  if constexpr (N >= 4) x += dpp_mov<kDppXor2>(x);
-  if constexpr (N >= 8) x += dpp_mov<kDppRowHalfMirror>(x);
-  if constexpr (N >= 16) x += dpp_mov<kDppRowMirror>(x);
+// Sum over aligned groups of N consecutive lanes (N a power of two <= 64) of M
+// independent values, one reduction step for all of them before the next, so the DPP
+// moves of different values fill each other's hazards.  Every lane of a group receives
+// the group's total, bit-identical across the group (each step adds a commutative pair).
+template <int N, int M>
+__device__ inline void group_sum_n(float (&x)[M]) {
+  if constexpr (N >= 2) {
 #pragma unroll
-  for (int off = 16; off < N; off <<= 1) x += __shfl_xor(x, off, 64);
-  return x;
+    for (int m = 0; m < M; ++m) x[m] += dpp_mov<kDppXor1>(x[m]);
+  }
+  if constexpr (N >= 4) {
+#pragma unroll
+    for (int m = 0; m < M; ++m) x[m] += dpp_mov<kDppXor2>(x[m]);
+  }
+  if constexpr (N >= 8) {
+#pragma unroll
+    for (int m = 0; m < M; ++m) x[m] += dpp_mov<kDppRowHalfMirror>(x[m]);
+  }
+  if constexpr (N >= 16) {
+#pragma unroll
+    for (int m = 0; m < M; ++m) x[m] += dpp_mov<kDppRowMirror>(x[m]);
+  }
+#pragma unroll
+  for (int off = 16; off < N; off <<= 1) {
+#pragma unroll
+    for (int m = 0; m < M; ++m) x[m] += __shfl_xor(x[m], off, 64);
+  }
 }
 
 __device__ inline float wave_max(float x) {
@@ -127,22 +198,179 @@ __device__ inline float load_dev(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Geometry of the one-pass kernel: 16-byte pieces (W = 4 words).
+template <typename T, int D, int G>
+struct Geo {
+  static constexpr int W = 4;
+  static constexpr int HALF = Elem<T, W>::N;  // elements per piece = pairs per lane
+  static constexpr int EPL = 2 * HALF;        // elements per lane
+  static constexpr int LPK = D / EPL;         // lanes per key
+  static constexpr int KPW = 64 / LPK;        // keys per wave per sub-step
+  static constexpr int KPI = 4 * KPW;         // keys per workgroup per sub-step
+  static constexpr int U = LCD_U_G2;
+  static constexpr int STEP = KPI * U;        // keys per workgroup per iteration
+  static_assert(G <= 2, "the one-pass kernel serves up to 2 query heads per KV head");
+  static_assert(LPK >= 1 && LPK <= 64 && (64 % LPK) == 0, "lane mapping");
+};
+
+// Dynamic LDS of the one-pass kernel: the 4 waves' outputs [4][G][D], their (m, l)
+// [2][4][G], the wave weights [4][G] and the workgroup's (m, l) [2][G].
+template <int D, int G>
+constexpr size_t onepass_lds_bytes() {
+  return ((size_t)4 * G * D + 14 * G) * sizeof(float);
+}
+
+// Dynamic LDS of the two-pass kernel: the logits [chunk][G] (reused for the 4 waves'
+// outputs [4][G][D] after the V pass), cross-wave reductions [4][G] and the
+// workgroup's (m, l) [2][G].
+template <int D, int G>
+inline size_t twopass_lds_floats(int chunk) {
+  const size_t a = (size_t)chunk * G, o = (size_t)4 * G * D;
+  return (a > o ? a : o) + 6 * G;
+}
+
+// ---------------------------------------------------------------- split finish
+// The end of a decode workgroup: ored[0 .. G*D) (LDS) holds its range's unnormalised
+// output and Mh / Lh (LDS) its maximum and sum per query head.  With one split the
+// output is normalised and written; otherwise the partial is published and the last
+// workgroup of (b, g) to arrive merges every split in split order (deterministic).  In
+// logits mode the merging workgroup then runs the H2O epilogue.
+template <int D, int G, bool LOGITS>
+__device__ inline void split_finish(const DecodeParams& p, const float* ored, const float* Mh, const float* Lh,
+                                    int split, int b, int g) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const size_t bg = (size_t)b * p.Hkv + g;
+  const size_t bh0 = (size_t)b * p.Hq + g * G;
+  __shared__ float Mtot[G], Linv[G];
+  __shared__ int is_last;
+  if (p.n_splits == 1) {
+    if (threadIdx.x < G) {
+      Mtot[threadIdx.x] = Mh[threadIdx.x];
+      Linv[threadIdx.x] = 1.f / Lh[threadIdx.x];
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < G * D; idx += kDecodeThreads)
+      p.out[(bh0 + idx / D) * D + idx % D] = ored[idx] * Linv[idx / D];
+  } else {
+    // publish this split's partial, then count arrivals for (b, g)
+    const size_t BH = (size_t)p.B * p.Hq;
+    for (int idx = threadIdx.x; idx < G * D; idx += kDecodeThreads)
+      store_dev(&p.part_o[((size_t)split * BH + bh0 + idx / D) * D + idx % D], ored[idx]);
+    if (threadIdx.x < G) {
+      float* ml = p.part_ml + ((size_t)split * BH + bh0 + threadIdx.x) * 2;
+      store_dev(&ml[0], Mh[threadIdx.x]);
+      store_dev(&ml[1], Lh[threadIdx.x]);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // every store of this thread has completed
+    __syncthreads();
+    if (threadIdx.x == 0)
+      is_last = __hip_atomic_fetch_add(&p.arrivals[bg], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                p.n_splits - 1;
+    __syncthreads();
+    if (!is_last) return;
+    // last arrival: merge every split in split order (deterministic)
+    if (threadIdx.x < G) {
+      const int j = threadIdx.x;
+      float mt = -INFINITY;
+      for (int s = 0; s < p.n_splits; ++s) mt = fmaxf(mt, load_dev(&p.part_ml[((size_t)s * BH + bh0 + j) * 2]));
+      float lt = 0.f;
+      for (int s = 0; s < p.n_splits; ++s) {
+        const float* ml = p.part_ml + ((size_t)s * BH + bh0 + j) * 2;
+        lt += load_dev(&ml[1]) * exp2f(load_dev(&ml[0]) - mt);
+      }
+      Mtot[j] = mt;
+      Linv[j] = 1.f / lt;
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < G * D; idx += kDecodeThreads) {
+      const int j = idx / D, dd = idx % D;
+      float acc = 0.f;
+      for (int s = 0; s < p.n_splits; ++s)
+        acc += load_dev(&p.part_o[((size_t)s * BH + bh0 + j) * D + dd]) *
+               exp2f(load_dev(&p.part_ml[((size_t)s * BH + bh0 + j) * 2]) - Mtot[j]);
+      p.out[(bh0 + j) * D + dd] = acc * Linv[j];
+    }
+    if (threadIdx.x == 0)  // ready for the next call
+      __hip_atomic_store(&p.arrivals[bg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  if constexpr (LOGITS) {
+    // H2O: add this step's weights (summed over the group's query heads) to every
+    // filled slot's score and pick the slot the next append overwrites: the lowest
+    // score among slots with pos <= max_pos, ties evicting the higher position.
+    __shared__ unsigned long long wbest[4];
+    float* score = p.score + bg * p.C;
+    const int* pos = p.pos + bg * p.C;
+    unsigned long long best = ~0ull;
+    constexpr int EU = LCD_H2O_EU;  // slots per thread per iteration, all loads issued first
+    for (int i0 = threadIdx.x; i0 < p.n; i0 += kDecodeThreads * EU) {
+      float x[EU][G], sc[EU];
+      int ps[EU];
+#pragma unroll
+      for (int u = 0; u < EU; ++u) {
+        const int i = i0 + u * kDecodeThreads;
+        const bool in = i < p.n;
+#pragma unroll
+        for (int j = 0; j < G; ++j) x[u][j] = in ? load_dev(&p.logits[(bh0 + j) * p.C + i]) : 0.f;
+        sc[u] = in ? score[i] : 0.f;
+        ps[u] = in ? pos[i] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < EU; ++u) {
+        const int i = i0 + u * kDecodeThreads;
+        if (i >= p.n) break;
+        float a = 0.f;
+#pragma unroll
+        for (int j = 0; j < G; ++j) a += exp2f(x[u][j] - Mtot[j]) * Linv[j];
+        const float snew = sc[u] + a;
+        score[i] = snew;
+        if (p.pick_victim && (int64_t)ps[u] <= p.max_pos) {
+          const unsigned long long key = ((unsigned long long)__float_as_uint(snew) << 32) |
+                                         (unsigned long long)(0xffffffffu - (uint32_t)ps[u]);
+          best = key < best ? key : best;
+        }
+      }
+    }
+    if (p.pick_victim) {
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const unsigned long long other = __shfl_xor(best, off, 64);
+        best = other < best ? other : best;
+      }
+      if (lane == 0) wbest[wave] = best;
+      __syncthreads();
+      best = wbest[0];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) best = wbest[w] < best ? wbest[w] : best;
+      if (best != ~0ull) {
+        const int win_pos = (int)(0xffffffffu - (uint32_t)(best & 0xffffffffull));
+        for (int i = threadIdx.x; i < p.n; i += kDecodeThreads)
+          if (pos[i] == win_pos) p.victim[bg] = i;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- one-pass kernel
+// For up to 2 query heads per KV head (registers hold the queries and the outputs
+// together).
 template <typename T, int D, int G, int MODE>
-__global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodeParams p) {
+__global__ void __launch_bounds__(kDecodeThreads) decode_onepass_kernel(DecodeParams p) {
   constexpr bool ROPE = MODE == kModeRope;
   constexpr bool LOGITS = MODE == kModePlainLogits;
-  constexpr int HALF = Elem<T>::HALF;
-  constexpr int EPL = 2 * HALF;    // elements per lane (HALF pairs)
-  constexpr int LPK = D / EPL;     // lanes per key
-  constexpr int KPW = 64 / LPK;    // keys per wave per iteration
-  constexpr int KPI = 4 * KPW;     // keys per workgroup per iteration
+  using GE = Geo<T, D, G>;
+  constexpr int W = GE::W, HALF = GE::HALF, EPL = GE::EPL, LPK = GE::LPK, KPW = GE::KPW, KPI = GE::KPI;
+  constexpr int U = GE::U, STEP = GE::STEP;
   constexpr int D2 = D / 2;
-  static_assert(LPK >= 1 && LPK <= 64 && (64 % LPK) == 0, "lane mapping");
+  using E = Elem<T, W>;
 
   extern __shared__ float smem[];
-  float* xs = smem;                       // [chunk][G] logits, then weights
-  float* red = xs + p.chunk * G;          // [4][G] cross-wave reductions, then [G] sums
-  float* ored = red + 5 * G;              // [4][G][D] cross-wave output sums
+  float* ored = smem;                 // [4][G][D] the waves' outputs, then [G][D] their merge
+  float* wm = ored + 4 * G * D;       // [4][G] the waves' maxima
+  float* wl = wm + 4 * G;             // [4][G] the waves' sums
+  float* wsc = wl + 4 * G;            // [4][G] the waves' weights 2^(m_w - m)
+  float* Mh = wsc + 4 * G;            // [G] the workgroup's maxima
+  float* Lh = Mh + G;                 // [G] the workgroup's sums
 
   // Workgroups are dealt round-robin to the 8 XCDs, so linear id w runs on XCD
   // w % 8.  Give each XCD a contiguous run of (split, kv-head, batch) items, split
@@ -172,17 +400,17 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodePara
   for (int j = 0; j < G; ++j) {
     const char* qrow = reinterpret_cast<const char*>(p.q) + ((size_t)b * p.Hq + g * G + j) * D * sizeof(T);
     float lo[HALF], hi[HALF];
-    Elem<T>::load(qrow + lo_off, lo);
-    Elem<T>::load(qrow + hi_off, hi);
+    E::cvt(load_words<W>(qrow + lo_off), lo);
+    E::cvt(load_words<W>(qrow + hi_off), hi);
     if constexpr (ROPE) {
-      const float* cr = p.cos_t + (size_t)p.q_rank * D2 + i0;
-      const float* sr = p.sin_t + (size_t)p.q_rank * D2 + i0;
+      float c[HALF], s[HALF];
+      load_floats<HALF>(p.cos_t + (size_t)p.q_rank * D2 + i0, c);
+      load_floats<HALF>(p.sin_t + (size_t)p.q_rank * D2 + i0, s);
 #pragma unroll
       for (int e = 0; e < HALF; ++e) {
-        const float c = cr[e], s = sr[e];
         const float a = lo[e], bb = hi[e];
-        lo[e] = a * c - bb * s;
-        hi[e] = a * s + bb * c;
+        lo[e] = a * c[e] - bb * s[e];
+        hi[e] = a * s[e] + bb * c[e];
       }
     }
 #pragma unroll
@@ -192,24 +420,20 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodePara
     }
   }
 
-  // ---- K pass: U keys per lane group per iteration, every load issued first.
-  // With RoPE, the lane's U keys of one iteration sit KPI slots apart; where their
-  // in-cache positions are also KPI apart (everywhere except across the ring's wrap
-  // point and the sink boundary) the cos/sin of key u+1 follow from key u's by one
-  // angle addition with the per-lane constant rotation (cos, sin)(KPI * theta_i), so
-  // only one table row is read per iteration.  Waves that straddle a discontinuity
-  // read every key's row from the table instead.
-  constexpr int U = (G <= 2) ? 4 : 2;
-  float mx[G];
-#pragma unroll
-  for (int j = 0; j < G; ++j) mx[j] = -INFINITY;
+  // ---- RoPE angles of the keys.  With few query heads (G <= 2, where the kernel is
+  // far from ALU-bound) a lane group's U keys of one iteration take one table row: they
+  // sit KPI slots apart, and where their in-cache positions are also KPI apart
+  // (everywhere except across the ring's wrap point and the sink boundary) the cos/sin
+  // of key u+1 follow from key u's by one angle addition with the per-lane constant
+  // rotation (cos, sin)(KPI * theta_i).  Waves that straddle a discontinuity read every
+  // key's row.  With more query heads every key reads its own row (the split's table
+  // slice stays in its XCD's L2).
+  constexpr bool REC = ROPE && G <= 2;
+  constexpr int NCS = ROPE ? (REC ? 1 : U) : 1;  // table rows held per iteration
   float dc[HALF], ds[HALF];
-  if constexpr (ROPE) {
-#pragma unroll
-    for (int e = 0; e < HALF; ++e) {
-      dc[e] = p.cos_t[(size_t)KPI * D2 + i0 + e];
-      ds[e] = p.sin_t[(size_t)KPI * D2 + i0 + e];
-    }
+  if constexpr (REC) {
+    load_floats<HALF>(p.cos_t + (size_t)KPI * D2 + i0, dc);
+    load_floats<HALF>(p.sin_t + (size_t)KPI * D2 + i0, ds);
   }
   auto rank_of = [&](int slot) {
     int rank = slot;
@@ -221,36 +445,54 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodePara
     return rank;
   };
   auto load_cs = [&](int rank, float (&c)[HALF], float (&sn)[HALF]) {
-    const float4* cr = reinterpret_cast<const float4*>(p.cos_t + (size_t)rank * D2 + i0);
-    const float4* sr = reinterpret_cast<const float4*>(p.sin_t + (size_t)rank * D2 + i0);
-#pragma unroll
-    for (int e = 0; e < HALF / 4; ++e) {
-      const float4 c4 = cr[e], s4 = sr[e];
-      c[4 * e] = c4.x; c[4 * e + 1] = c4.y; c[4 * e + 2] = c4.z; c[4 * e + 3] = c4.w;
-      sn[4 * e] = s4.x; sn[4 * e + 1] = s4.y; sn[4 * e + 2] = s4.z; sn[4 * e + 3] = s4.w;
-    }
+    load_floats<HALF>(p.cos_t + (size_t)rank * D2 + i0, c);
+    load_floats<HALF>(p.sin_t + (size_t)rank * D2 + i0, sn);
   };
 
-  for (int base = 0; base < cnt; base += KPI * U) {
+  // one iteration's registers: the raw K and V pieces of U keys, and the table rows
+  struct Buf {
+    Words<W> klo[U], khi[U], vlo[U], vhi[U];
+    float c[NCS][HALF], sn[NCS][HALF];
+  };
+  auto load_iter = [&](int base, Buf& bf) {
     const int key0 = base + wave * KPW + kg;
-    uint4 rlo[U], rhi[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int key = key0 + u * KPI;
       if (key < cnt) {
-        const char* row = kbase + (size_t)(s_begin + key) * D * sizeof(T);
-        rlo[u] = load16(row + lo_off);
-        rhi[u] = load16(row + hi_off);
+        const size_t roff = (size_t)(s_begin + key) * D * sizeof(T);
+        bf.klo[u] = load_words<W>(kbase + roff + lo_off);
+        bf.khi[u] = load_words<W>(kbase + roff + hi_off);
+        bf.vlo[u] = load_words<W>(vbase + roff + lo_off);
+        bf.vhi[u] = load_words<W>(vbase + roff + hi_off);
       } else {
-        rlo[u] = make_uint4(0, 0, 0, 0);
-        rhi[u] = make_uint4(0, 0, 0, 0);
+        bf.klo[u] = zero_words<W>();
+        bf.khi[u] = zero_words<W>();
+        bf.vlo[u] = zero_words<W>();
+        bf.vhi[u] = zero_words<W>();
       }
     }
-    float c[HALF], sn[HALF];
-    bool stepwise = false;  // this wave straddles a rank discontinuity
-    int rank0 = 0;
     if constexpr (ROPE) {
-      rank0 = rank_of(s_begin + min(key0, cnt - 1));
+#pragma unroll
+      for (int u = 0; u < NCS; ++u) load_cs(rank_of(s_begin + min(key0 + u * KPI, cnt - 1)), bf.c[u], bf.sn[u]);
+    }
+  };
+
+  // running softmax state of this lane group (identical in its LPK lanes)
+  float m[G], l[G], o[G][EPL];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    m[j] = -INFINITY;
+    l[j] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[j][e] = 0.f;
+  }
+
+  auto compute_iter = [&](int base, Buf& bf) {
+    const int key0 = base + wave * KPW + kg;
+    bool stepwise = false;  // REC: this wave straddles a rank discontinuity
+    if constexpr (REC) {
+      const int rank0 = rank_of(s_begin + min(key0, cnt - 1));
       bool disc = false;
 #pragma unroll
       for (int u = 1; u < U; ++u) {
@@ -258,34 +500,37 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodePara
         disc |= key < cnt && rank_of(s_begin + key) != rank0 + u * KPI;
       }
       stepwise = __any(disc);
-      load_cs(rank0, c, sn);
     }
+    // dot products of the U keys with the G queries, then their lane-group sums in one
+    // interleaved pass
+    float d[U * G];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int key = key0 + u * KPI;
-      const bool valid = key < cnt;
       float kf[EPL];
       {
         float lo[HALF], hi[HALF];
-        Elem<T>::cvt(rlo[u], lo);
-        Elem<T>::cvt(rhi[u], hi);
+        E::cvt(bf.klo[u], lo);
+        E::cvt(bf.khi[u], hi);
         if constexpr (ROPE) {
-          if (u > 0) {
-            if (stepwise) {
-              load_cs(rank_of(s_begin + min(key, cnt - 1)), c, sn);
-            } else {
+          const int ci = REC ? 0 : u;
+          if constexpr (REC) {
+            if (u > 0) {
+              if (stepwise) {
+                load_cs(rank_of(s_begin + min(key0 + u * KPI, cnt - 1)), bf.c[0], bf.sn[0]);
+              } else {
 #pragma unroll
-              for (int e = 0; e < HALF; ++e) {
-                const float cc = c[e] * dc[e] - sn[e] * ds[e];
-                sn[e] = sn[e] * dc[e] + c[e] * ds[e];
-                c[e] = cc;
+                for (int e = 0; e < HALF; ++e) {
+                  const float cc = bf.c[0][e] * dc[e] - bf.sn[0][e] * ds[e];
+                  bf.sn[0][e] = bf.sn[0][e] * dc[e] + bf.c[0][e] * ds[e];
+                  bf.c[0][e] = cc;
+                }
               }
             }
           }
 #pragma unroll
           for (int e = 0; e < HALF; ++e) {
-            kf[e] = lo[e] * c[e] - hi[e] * sn[e];
-            kf[HALF + e] = lo[e] * sn[e] + hi[e] * c[e];
+            kf[e] = lo[e] * bf.c[ci][e] - hi[e] * bf.sn[ci][e];
+            kf[HALF + e] = lo[e] * bf.sn[ci][e] + hi[e] * bf.c[ci][e];
           }
         } else {
 #pragma unroll
@@ -297,35 +542,351 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodePara
       }
 #pragma unroll
       for (int j = 0; j < G; ++j) {
-        float d = 0.f;
+        float acc = 0.f;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) d = fmaf(qf[j][e], kf[e], d);
-        d = group_sum<LPK>(d);
-        if (valid) {
-          mx[j] = fmaxf(mx[j], d);
-          if (sub == 0) {
-            xs[key * G + j] = d;
-            if constexpr (LOGITS) store_dev(&p.logits[((size_t)b * p.Hq + g * G + j) * p.C + s_begin + key], d);
+        for (int e = 0; e < EPL; ++e) acc = fmaf(qf[j][e], kf[e], acc);
+        d[u * G + j] = acc;
+      }
+    }
+    group_sum_n<LPK, U * G>(d);
+
+    // mask the keys past the range, record logits (H2O), new running maxima
+    float mn[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) mn[j] = m[j];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int key = key0 + u * KPI;
+      const bool valid = key < cnt;
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        d[u * G + j] = valid ? d[u * G + j] : -INFINITY;
+        mn[j] = fmaxf(mn[j], d[u * G + j]);
+      }
+      if constexpr (LOGITS) {
+        if (valid && sub == 0) {
+#pragma unroll
+          for (int j = 0; j < G; ++j)
+            store_dev(&p.logits[((size_t)b * p.Hq + g * G + j) * p.C + s_begin + key], d[u * G + j]);
+        }
+      }
+    }
+    // rescale the running sums only when some maximum of the wave grew (rare after the
+    // first iterations); a group that has seen no key yet keeps m = -inf and scale 1
+    bool grow = false;
+#pragma unroll
+    for (int j = 0; j < G; ++j) grow |= mn[j] > m[j];
+    if (__any(grow)) {
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        const float corr = mn[j] == -INFINITY ? 1.f : exp2f(m[j] - mn[j]);
+        m[j] = mn[j];
+        l[j] *= corr;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[j][e] *= corr;
+      }
+    }
+    // weights p = 2^(x - m) (0 for masked keys) and the V accumulation
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        const float x = d[u * G + j];
+        const float pw = x == -INFINITY ? 0.f : exp2f(x - m[j]);
+        d[u * G + j] = pw;
+        l[j] += pw;
+      }
+      float lo[HALF], hi[HALF];
+      E::cvt(bf.vlo[u], lo);
+      E::cvt(bf.vhi[u], hi);
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        const float pw = d[u * G + j];
+#pragma unroll
+        for (int e = 0; e < HALF; ++e) {
+          o[j][e] = fmaf(pw, lo[e], o[j][e]);
+          o[j][HALF + e] = fmaf(pw, hi[e], o[j][HALF + e]);
+        }
+      }
+    }
+  };
+
+  // ---- the pass: two register sets alternate, the next iteration's loads are issued
+  // before this iteration's arithmetic
+  {
+    Buf A, B;
+    load_iter(0, A);
+    for (int base = 0; base < cnt; base += 2 * STEP) {
+      if (base + STEP < cnt) load_iter(base + STEP, B);
+      compute_iter(base, A);
+      if (base + STEP >= cnt) break;
+      if (base + 2 * STEP < cnt) load_iter(base + 2 * STEP, A);
+      compute_iter(base + STEP, B);
+    }
+  }
+
+  // ---- merge the lane groups of each wave at the wave's maximum, then the 4 waves
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    float mw = m[j];
+#pragma unroll
+    for (int off = LPK; off < 64; off <<= 1) mw = fmaxf(mw, __shfl_xor(mw, off, 64));
+    const float sc = m[j] == -INFINITY ? 0.f : exp2f(m[j] - mw);
+    float lw = l[j] * sc;
+#pragma unroll
+    for (int off = LPK; off < 64; off <<= 1) lw += __shfl_xor(lw, off, 64);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      float x = o[j][e] * sc;
+#pragma unroll
+      for (int off = LPK; off < 64; off <<= 1) x += __shfl_xor(x, off, 64);
+      o[j][e] = x;
+    }
+    if (lane == 0) {
+      wm[wave * G + j] = mw;
+      wl[wave * G + j] = lw;
+    }
+  }
+  if (kg == 0) {
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+#pragma unroll
+      for (int e = 0; e < HALF; ++e) {
+        ored[(wave * G + j) * D + i0 + e] = o[j][e];
+        ored[(wave * G + j) * D + D2 + i0 + e] = o[j][HALF + e];
+      }
+  }
+  __syncthreads();
+  // the workgroup's (m, l) per head and the waves' weights, then the merged output
+  if (threadIdx.x < G) {
+    const int j = threadIdx.x;
+    const float M = fmaxf(fmaxf(wm[j], wm[G + j]), fmaxf(wm[2 * G + j], wm[3 * G + j]));
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float mwv = wm[w * G + j];
+      const float s = mwv == -INFINITY ? 0.f : exp2f(mwv - M);
+      wsc[w * G + j] = s;
+      L += wl[w * G + j] * s;
+    }
+    Mh[j] = M;
+    Lh[j] = L;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * D; idx += kDecodeThreads) {  // each thread reads only its idx
+    const int j = idx / D;
+    float acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) acc += ored[w * G * D + idx] * wsc[w * G + j];
+    ored[idx] = acc;
+  }
+  __syncthreads();
+  split_finish<D, G, LOGITS>(p, ored, Mh, Lh, split, b, g);
+}
+
+// ---------------------------------------------------------------- two-pass kernel
+// For 4 or more query heads per KV head.  K pass: every key of the range is loaded
+// once, rotated, dotted with the G queries; logits go to LDS.  Softmax: the range
+// maximum per query head, p = 2^(x - m) in LDS, l = sum p.  V pass: every value row is
+// loaded once and accumulated with the G weights.  Registers then hold either the
+// queries (K pass) or the outputs (V pass), never both, which keeps G * D-sized state
+// within two waves per SIMD at 16-byte pieces.
+template <typename T, int D, int G, int MODE>
+__global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodeParams p) {
+  constexpr bool ROPE = MODE == kModeRope;
+  constexpr bool LOGITS = MODE == kModePlainLogits;
+  using E = Elem<T, 4>;
+  constexpr int HALF = E::N;
+  constexpr int EPL = 2 * HALF;    // elements per lane (HALF pairs)
+  constexpr int LPK = D / EPL;     // lanes per key
+  constexpr int KPW = 64 / LPK;    // keys per wave per sub-step
+  constexpr int KPI = 4 * KPW;     // keys per workgroup per sub-step
+  constexpr int D2 = D / 2;
+  static_assert(LPK >= 1 && LPK <= 64 && (64 % LPK) == 0, "lane mapping");
+
+  extern __shared__ float smem[];
+  const int region = (p.chunk * G > 4 * G * D ? p.chunk * G : 4 * G * D);
+  float* xs = smem;                 // [chunk][G] logits, then weights
+  float* ored = smem;               // [4][G][D] the waves' outputs (after the V pass), then [G][D]
+  float* red = smem + region;       // [4][G] cross-wave reductions
+  float* Mh = red + 4 * G;          // [G] the range's maxima
+  float* Lh = Mh + G;               // [G] the range's sums
+
+  // XCD-aware item order (see the one-pass kernel)
+  const int per_xcd = (int)((gridDim.x + 7) / 8);
+  const int item = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  const int n_bg = p.B * p.Hkv;
+  if (item >= p.n_splits * n_bg) return;  // padding of the grid to a multiple of 8
+  const int split = item / n_bg;
+  const int g = (item % n_bg) % p.Hkv, b = (item % n_bg) / p.Hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane % LPK, kg = lane / LPK;
+  const int i0 = sub * HALF;  // first pair index owned by this lane
+  const int s_begin = split * p.chunk;
+  const int cnt = min(p.n - s_begin, p.chunk);
+
+  const size_t bg = (size_t)b * p.Hkv + g;
+  const char* kbase = reinterpret_cast<const char*>(p.k) + bg * p.C * D * sizeof(T);
+  const char* vbase = reinterpret_cast<const char*>(p.v) + bg * p.C * D * sizeof(T);
+  const size_t lo_off = (size_t)i0 * sizeof(T);
+  const size_t hi_off = (size_t)(D2 + i0) * sizeof(T);
+
+  // ---- queries of the group: load, rotate at the query's position, pre-scale
+  float qf[G][EPL];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    const char* qrow = reinterpret_cast<const char*>(p.q) + ((size_t)b * p.Hq + g * G + j) * D * sizeof(T);
+    float lo[HALF], hi[HALF];
+    E::cvt(load_words<4>(qrow + lo_off), lo);
+    E::cvt(load_words<4>(qrow + hi_off), hi);
+    if constexpr (ROPE) {
+      float c[HALF], s[HALF];
+      load_floats<HALF>(p.cos_t + (size_t)p.q_rank * D2 + i0, c);
+      load_floats<HALF>(p.sin_t + (size_t)p.q_rank * D2 + i0, s);
+#pragma unroll
+      for (int e = 0; e < HALF; ++e) {
+        const float a = lo[e], bb = hi[e];
+        lo[e] = a * c[e] - bb * s[e];
+        hi[e] = a * s[e] + bb * c[e];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < HALF; ++e) {
+      qf[j][e] = lo[e] * p.qscale;
+      qf[j][HALF + e] = hi[e] * p.qscale;
+    }
+  }
+
+  // ---- K pass: U keys per lane group per iteration, every key with its own table row;
+  // for up to 6 query heads the next iteration's loads are issued before this
+  // iteration's arithmetic (two register sets alternate)
+  constexpr int U = G <= 4 ? LCD_U2_G4 : (G <= 6 ? LCD_U2_G6 : 2);
+  constexpr int NCS = ROPE ? U : 1;
+  constexpr int STEP = KPI * U;
+  auto rank_of = [&](int slot) {
+    int rank = slot;
+    if (p.full && slot >= p.S) {
+      int r = slot - p.S - p.ring_head;
+      if (r < 0) r += p.W;
+      rank = p.S + r;
+    }
+    return rank;
+  };
+  struct KBuf {
+    Words<4> lo[U], hi[U];
+    float c[NCS][HALF], sn[NCS][HALF];
+  };
+  auto load_iter = [&](int base, KBuf& bf) {
+    const int key0 = base + wave * KPW + kg;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int key = key0 + u * KPI;
+      if (key < cnt) {
+        const char* row = kbase + (size_t)(s_begin + key) * D * sizeof(T);
+        bf.lo[u] = load_words<4>(row + lo_off);
+        bf.hi[u] = load_words<4>(row + hi_off);
+      } else {
+        bf.lo[u] = zero_words<4>();
+        bf.hi[u] = zero_words<4>();
+      }
+    }
+    if constexpr (ROPE) {
+#pragma unroll
+      for (int u = 0; u < NCS; ++u) {
+        const int rank = rank_of(s_begin + min(key0 + u * KPI, cnt - 1));
+        load_floats<HALF>(p.cos_t + (size_t)rank * D2 + i0, bf.c[u]);
+        load_floats<HALF>(p.sin_t + (size_t)rank * D2 + i0, bf.sn[u]);
+      }
+    }
+  };
+  float mx[G];
+#pragma unroll
+  for (int j = 0; j < G; ++j) mx[j] = -INFINITY;
+  auto compute_iter = [&](int base, KBuf& bf) {
+    const int key0 = base + wave * KPW + kg;
+    float d[U * G];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float kf[EPL];
+      {
+        float lo[HALF], hi[HALF];
+        E::cvt(bf.lo[u], lo);
+        E::cvt(bf.hi[u], hi);
+        if constexpr (ROPE) {
+#pragma unroll
+          for (int e = 0; e < HALF; ++e) {
+            kf[e] = lo[e] * bf.c[u][e] - hi[e] * bf.sn[u][e];
+            kf[HALF + e] = lo[e] * bf.sn[u][e] + hi[e] * bf.c[u][e];
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < HALF; ++e) {
+            kf[e] = lo[e];
+            kf[HALF + e] = hi[e];
           }
         }
+      }
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc = fmaf(qf[j][e], kf[e], acc);
+        d[u * G + j] = acc;
+      }
+    }
+    group_sum_n<LPK, U * G>(d);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int key = key0 + u * KPI;
+      const bool valid = key < cnt;
+#pragma unroll
+      for (int j = 0; j < G; ++j) mx[j] = fmaxf(mx[j], valid ? d[u * G + j] : -INFINITY);
+      if (valid && sub == 0) {
+#pragma unroll
+        for (int j = 0; j < G; ++j) xs[key * G + j] = d[u * G + j];
+        if constexpr (LOGITS) {
+#pragma unroll
+          for (int j = 0; j < G; ++j)
+            store_dev(&p.logits[((size_t)b * p.Hq + g * G + j) * p.C + s_begin + key], d[u * G + j]);
+        }
+      }
+    }
+  };
+  {
+    constexpr bool KPF = G <= 6;
+    if constexpr (KPF) {
+      KBuf A, B;
+      load_iter(0, A);
+      for (int base = 0; base < cnt; base += 2 * STEP) {
+        if (base + STEP < cnt) load_iter(base + STEP, B);
+        compute_iter(base, A);
+        if (base + STEP >= cnt) break;
+        if (base + 2 * STEP < cnt) load_iter(base + 2 * STEP, A);
+        compute_iter(base + STEP, B);
+      }
+    } else {
+      for (int base = 0; base < cnt; base += STEP) {
+        KBuf A;
+        load_iter(base, A);
+        compute_iter(base, A);
       }
     }
   }
 
   // first V rows are requested before the softmax barriers (their latency overlaps them)
-  constexpr int UV = 4;
-  uint4 vlo[UV], vhi[UV];
+  constexpr int UV = G <= 6 ? 4 : 2;
+  Words<4> vlo[UV], vhi[UV];
   auto load_v = [&](int base) {
 #pragma unroll
     for (int u = 0; u < UV; ++u) {
       const int key = base + u * KPI + wave * KPW + kg;
       if (key < cnt) {
         const char* row = vbase + (size_t)(s_begin + key) * D * sizeof(T);
-        vlo[u] = load16(row + lo_off);
-        vhi[u] = load16(row + hi_off);
+        vlo[u] = load_words<4>(row + lo_off);
+        vhi[u] = load_words<4>(row + hi_off);
       } else {
-        vlo[u] = make_uint4(0, 0, 0, 0);
-        vhi[u] = make_uint4(0, 0, 0, 0);
+        vlo[u] = zero_words<4>();
+        vhi[u] = zero_words<4>();
       }
     }
   };
@@ -340,8 +901,9 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodePara
   __syncthreads();
   float M[G];
 #pragma unroll
-  for (int j = 0; j < G; ++j)
-    M[j] = fmaxf(fmaxf(red[j], red[G + j]), fmaxf(red[2 * G + j], red[3 * G + j]));
+  for (int j = 0; j < G; ++j) M[j] = fmaxf(fmaxf(red[j], red[G + j]), fmaxf(red[2 * G + j], red[3 * G + j]));
+  if (threadIdx.x < G) Mh[threadIdx.x] = fmaxf(fmaxf(red[threadIdx.x], red[G + threadIdx.x]),
+                                               fmaxf(red[2 * G + threadIdx.x], red[3 * G + threadIdx.x]));
   __syncthreads();  // red is reused below
 
   // ---- weights p = 2^(x - m) and their sums
@@ -362,6 +924,8 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodePara
     if (lane == 0) red[wave * G + j] = s;
   }
   __syncthreads();
+  if (threadIdx.x < G)
+    Lh[threadIdx.x] = red[threadIdx.x] + red[G + threadIdx.x] + red[2 * G + threadIdx.x] + red[3 * G + threadIdx.x];
 
   // ---- V pass: UV rows per lane group per iteration; the next iteration's rows are
   // requested before this iteration's arithmetic (software pipelining)
@@ -370,9 +934,8 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodePara
   for (int j = 0; j < G; ++j)
 #pragma unroll
     for (int e = 0; e < EPL; ++e) o[j][e] = 0.f;
-
   for (int base = 0; base < cnt; base += KPI * UV) {
-    uint4 clo[UV], chi[UV];
+    Words<4> clo[UV], chi[UV];
 #pragma unroll
     for (int u = 0; u < UV; ++u) {
       clo[u] = vlo[u];
@@ -384,8 +947,8 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodePara
       const int key = base + u * KPI + wave * KPW + kg;
       if (key < cnt) {
         float lo[HALF], hi[HALF];
-        Elem<T>::cvt(clo[u], lo);
-        Elem<T>::cvt(chi[u], hi);
+        E::cvt(clo[u], lo);
+        E::cvt(chi[u], hi);
 #pragma unroll
         for (int j = 0; j < G; ++j) {
           const float w = xs[key * G + j];
@@ -398,8 +961,9 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodePara
       }
     }
   }
+  __syncthreads();  // xs is reused as the waves' output buffer below
 
-  // ---- merge the key groups of the wave, then the 4 waves
+  // ---- merge the key groups of each wave, then the 4 waves
 #pragma unroll
   for (int j = 0; j < G; ++j)
 #pragma unroll
@@ -419,112 +983,10 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodePara
       }
   }
   __syncthreads();
-  const size_t bh0 = (size_t)b * p.Hq + g * G;
-  float* wsum = red + 4 * G;  // this workgroup's l per head (aliases nothing live)
-  if (threadIdx.x < G) {
-    const int j = threadIdx.x;
-    wsum[j] = red[j] + red[G + j] + red[2 * G + j] + red[3 * G + j];
-  }
-  for (int idx = threadIdx.x; idx < G * D; idx += kDecodeThreads) {
-    const int j = idx / D, d = idx % D;
-    ored[idx] = ored[(0 * G + j) * D + d] + ored[(1 * G + j) * D + d] + ored[(2 * G + j) * D + d] +
-                ored[(3 * G + j) * D + d];
-  }
+  for (int idx = threadIdx.x; idx < G * D; idx += kDecodeThreads)  // each thread reads only its idx
+    ored[idx] = ored[idx] + ored[G * D + idx] + ored[2 * G * D + idx] + ored[3 * G * D + idx];
   __syncthreads();
-  // ored[0 .. G*D) now holds this range's unnormalised output, wsum its l, M its max.
-
-  __shared__ float Mtot[G], Linv[G];
-  __shared__ int is_last;
-  if (p.n_splits == 1) {
-    if (threadIdx.x < G) {
-      Mtot[threadIdx.x] = M[threadIdx.x];
-      Linv[threadIdx.x] = 1.f / wsum[threadIdx.x];
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < G * D; idx += kDecodeThreads)
-      p.out[(bh0 + idx / D) * D + idx % D] = ored[idx] * Linv[idx / D];
-  } else {
-    // publish this split's partial, then count arrivals for (b, g)
-    const size_t BH = (size_t)p.B * p.Hq;
-    for (int idx = threadIdx.x; idx < G * D; idx += kDecodeThreads)
-      store_dev(&p.part_o[((size_t)split * BH + bh0 + idx / D) * D + idx % D], ored[idx]);
-    if (threadIdx.x < G) {
-      float* ml = p.part_ml + ((size_t)split * BH + bh0 + threadIdx.x) * 2;
-      store_dev(&ml[0], M[threadIdx.x]);
-      store_dev(&ml[1], wsum[threadIdx.x]);
-    }
-    __builtin_amdgcn_s_waitcnt(0);  // every store of this thread has completed
-    __syncthreads();
-    if (threadIdx.x == 0)
-      is_last = __hip_atomic_fetch_add(&p.arrivals[bg], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                p.n_splits - 1;
-    __syncthreads();
-    if (!is_last) return;
-    // last arrival: merge every split in split order (deterministic)
-    if (threadIdx.x < G) {
-      const int j = threadIdx.x;
-      float mt = -INFINITY;
-      for (int s = 0; s < p.n_splits; ++s) mt = fmaxf(mt, load_dev(&p.part_ml[((size_t)s * BH + bh0 + j) * 2]));
-      float lt = 0.f;
-      for (int s = 0; s < p.n_splits; ++s) {
-        const float* ml = p.part_ml + ((size_t)s * BH + bh0 + j) * 2;
-        lt += load_dev(&ml[1]) * exp2f(load_dev(&ml[0]) - mt);
-      }
-      Mtot[j] = mt;
-      Linv[j] = 1.f / lt;
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < G * D; idx += kDecodeThreads) {
-      const int j = idx / D, d = idx % D;
-      float acc = 0.f;
-      for (int s = 0; s < p.n_splits; ++s)
-        acc += load_dev(&p.part_o[((size_t)s * BH + bh0 + j) * D + d]) *
-               exp2f(load_dev(&p.part_ml[((size_t)s * BH + bh0 + j) * 2]) - Mtot[j]);
-      p.out[(bh0 + j) * D + d] = acc * Linv[j];
-    }
-    if (threadIdx.x == 0)  // ready for the next call
-      __hip_atomic_store(&p.arrivals[bg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-
-  if constexpr (LOGITS) {
-    // H2O: add this step's weights (summed over the group's query heads) to every
-    // filled slot's score and pick the slot the next append overwrites: the lowest
-    // score among slots with pos <= max_pos, ties evicting the higher position.
-    __shared__ unsigned long long wbest[4];
-    float* score = p.score + bg * p.C;
-    const int* pos = p.pos + bg * p.C;
-    unsigned long long best = ~0ull;
-    for (int i = threadIdx.x; i < p.n; i += kDecodeThreads) {
-      float a = 0.f;
-#pragma unroll
-      for (int j = 0; j < G; ++j) a += exp2f(load_dev(&p.logits[(bh0 + j) * p.C + i]) - Mtot[j]) * Linv[j];
-      const float sc = score[i] + a;
-      score[i] = sc;
-      const int ps = pos[i];
-      if (p.pick_victim && (int64_t)ps <= p.max_pos) {
-        const unsigned long long key =
-            ((unsigned long long)__float_as_uint(sc) << 32) | (unsigned long long)(0xffffffffu - (uint32_t)ps);
-        best = key < best ? key : best;
-      }
-    }
-    if (p.pick_victim) {
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const unsigned long long other = __shfl_xor(best, off, 64);
-        best = other < best ? other : best;
-      }
-      if (lane == 0) wbest[wave] = best;
-      __syncthreads();
-      best = wbest[0];
-#pragma unroll
-      for (int w = 1; w < 4; ++w) best = wbest[w] < best ? wbest[w] : best;
-      if (best != ~0ull) {
-        const int win_pos = (int)(0xffffffffu - (uint32_t)(best & 0xffffffffull));
-        for (int i = threadIdx.x; i < p.n; i += kDecodeThreads)
-          if (pos[i] == win_pos) p.victim[bg] = i;
-      }
-    }
-  }
+  split_finish<D, G, LOGITS>(p, ored, Mh, Lh, split, b, g);
 }
 
 // Victim choice for a seeded H2O layer (no decode step has run yet): the lowest score
@@ -568,21 +1030,27 @@ hipError_t launch_h2o_pick_victim(const float* score, const int* pos, int* victi
 template <typename T, int D, int G>
 static hipError_t launch_tdg(int mode, const DecodeParams& p, hipStream_t s) {
   const int items = p.n_splits * p.B * p.Hkv;
-  const dim3 grid(((items + 7) / 8) * 8);
-  const size_t lds = ((size_t)p.chunk * G + 5 * G + 4 * G * D) * sizeof(float);
-  switch (mode) {
-    case kModeRope:
-      hipLaunchKernelGGL((decode_split_kernel<T, D, G, kModeRope>), grid, dim3(kDecodeThreads), lds, s, p);
-      break;
-    case kModePlain:
-      hipLaunchKernelGGL((decode_split_kernel<T, D, G, kModePlain>), grid, dim3(kDecodeThreads), lds, s, p);
-      break;
-    case kModePlainLogits:
-      hipLaunchKernelGGL((decode_split_kernel<T, D, G, kModePlainLogits>), grid, dim3(kDecodeThreads), lds, s,
-                         p);
-      break;
-    default:
-      return hipErrorInvalidValue;
+  const dim3 grid(((items + 7) / 8) * 8), block(kDecodeThreads);
+  if constexpr (G <= 2) {
+    const size_t lds = onepass_lds_bytes<D, G>();
+    switch (mode) {
+      case kModeRope: hipLaunchKernelGGL((decode_onepass_kernel<T, D, G, kModeRope>), grid, block, lds, s, p); break;
+      case kModePlain: hipLaunchKernelGGL((decode_onepass_kernel<T, D, G, kModePlain>), grid, block, lds, s, p); break;
+      case kModePlainLogits:
+        hipLaunchKernelGGL((decode_onepass_kernel<T, D, G, kModePlainLogits>), grid, block, lds, s, p);
+        break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    const size_t lds = twopass_lds_floats<D, G>(p.chunk) * sizeof(float);
+    switch (mode) {
+      case kModeRope: hipLaunchKernelGGL((decode_twopass_kernel<T, D, G, kModeRope>), grid, block, lds, s, p); break;
+      case kModePlain: hipLaunchKernelGGL((decode_twopass_kernel<T, D, G, kModePlain>), grid, block, lds, s, p); break;
+      case kModePlainLogits:
+        hipLaunchKernelGGL((decode_twopass_kernel<T, D, G, kModePlainLogits>), grid, block, lds, s, p);
+        break;
+      default: return hipErrorInvalidValue;
+    }
   }
   return hipGetLastError();
 }
@@ -607,6 +1075,13 @@ static hipError_t launch_t(int D, int G, int mode, const DecodeParams& p, hipStr
     case 256: return launch_td<T, 256>(G, mode, p, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+int decode_chunk_cap(int G) {
+  if (G <= 2) return 1 << 24;  // the one-pass kernel keeps no per-slot state in LDS
+  // two-pass: chunk * G logits + 6 * G floats within 64 KiB, 256 bytes kept for the
+  // static shared variables
+  return (16384 - 64 - 6 * G) / G / 64 * 64;
 }
 
 bool decode_supported(int dtype, int D, int G) {

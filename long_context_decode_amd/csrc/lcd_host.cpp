@@ -47,7 +47,6 @@ uint64_t align256(uint64_t x) { return (x + 255u) & ~uint64_t(255); }
 bool mul_ok(uint64_t* acc, uint64_t f) { return !__builtin_mul_overflow(*acc, f, acc); }
 
 constexpr int64_t kMaxSlots = int64_t(1) << 24;
-constexpr int kTargetWorkgroups = 512;  // decode grid size aimed for (2 per CU on 256 CUs)
 
 int env_int(const char* name, int dflt) {
   const char* s = std::getenv(name);
@@ -61,17 +60,8 @@ struct Layout {
   uint64_t kv_bytes = 0;
   uint64_t aux_bytes = 0, off_cos = 0, off_sin = 0, off_pos = 0, off_score = 0, off_victim = 0, off_arrive = 0;
   uint64_t ws_bytes = 0, ws_off_ml = 0, ws_off_logits = 0;
-  int max_splits = 0, chunk_cap = 0, chunk_force = 0;
+  int max_splits = 0, chunk_cap = 0, chunk_force = 0, target_wgs = 0;
 };
-
-// Largest split chunk whose LDS footprint stays within 64 KiB.
-int chunk_cap_for(int G, int D) {
-  const long floats = 16384 - 4L * G - 4L * G * D;
-  long c = floats / G;
-  c = (c / 64) * 64;
-  if (c > lcd::kMaxChunk) c = lcd::kMaxChunk;
-  return (int)c;
-}
 
 lcd_status check_config(const lcd_cache_config* c, Layout* L) {
   if (!c) return fail(LCD_EINVAL, "config is NULL");
@@ -144,19 +134,24 @@ lcd_status check_config(const lcd_cache_config* c, Layout* L) {
   }
   L->aux_bytes = aux;
 
-  L->chunk_cap = chunk_cap_for(G, c->head_dim);
+  L->chunk_cap = lcd::decode_chunk_cap(G);
   const int force = env_int("LCD_DECODE_CHUNK", 0);
   L->chunk_force = (force >= 64 && force % 64 == 0 && force <= L->chunk_cap) ? force : 0;
-  const int64_t bg = (int64_t)c->batch * c->n_kv_heads;
-  const int64_t target = env_int("LCD_DECODE_TARGET_WGS", kTargetWorkgroups);
-  int64_t smax = (target + bg - 1) / bg;
-  const int64_t by_cap = (C + L->chunk_cap - 1) / L->chunk_cap;
-  if (smax < by_cap) smax = by_cap;
-  if (L->chunk_force) smax = (C + L->chunk_force - 1) / L->chunk_force;
-  const int64_t by_min = (C + 63) / 64;
-  if (smax > by_min) smax = by_min;
-  if (smax < 1) smax = 1;
-  L->max_splits = (int)smax;
+  const int target = env_int("LCD_DECODE_TARGET_WGS", lcd::kResidentWorkgroups);
+  L->target_wgs = target > 0 ? target : lcd::kResidentWorkgroups;
+  {
+    // Bound on the split count of any plan with n <= C: plan_splits never exceeds
+    // max(ceil(n / chunk_cap), 4 * target / bg) splits nor ceil(n / 64), all
+    // non-decreasing in n.
+    const int64_t bg = (int64_t)c->batch * c->n_kv_heads;
+    const int64_t by_min = (C + 63) / 64;
+    const int64_t s_cap = (C + L->chunk_cap - 1) / L->chunk_cap;
+    if (L->chunk_force)
+      L->max_splits = (int)((C + L->chunk_force - 1) / L->chunk_force);
+    else
+      L->max_splits = (int)std::min<int64_t>(by_min, std::max<int64_t>(s_cap, 4 * (int64_t)L->target_wgs / bg));
+  }
+  const int smax = L->max_splits;
 
   const uint64_t bhq = (uint64_t)c->batch * c->n_q_heads;
   uint64_t ws = align256((uint64_t)smax * bhq * c->head_dim * sizeof(float));
@@ -168,19 +163,32 @@ lcd_status check_config(const lcd_cache_config* c, Layout* L) {
   return LCD_OK;
 }
 
-// Split plan for n attended slots: chunk is a multiple of 64, splits = ceil(n / chunk).
-void plan_splits(const Layout& L, int n, int* n_splits, int* chunk) {
+// Split plan for n attended slots of bg (row, KV head) pairs.  Cost model: workgroups
+// run in rounds of target_wgs, each as long as its chunk, so a plan costs
+// rounds * chunk.  Candidates are the most splits that fit r rounds, r = 1..4, raised to
+// the fewest the chunk cap allows and capped at ceil(n / 64); the cheapest wins, ties
+// going to fewer splits.  LCD_DECODE_CHUNK forces the chunk.
+void plan_splits(const Layout& L, int n, int bg, int* n_splits, int* chunk) {
   int ch;
   if (L.chunk_force) {
     ch = L.chunk_force;
   } else {
-    int s = L.max_splits;
-    const int by_min = (n + 63) / 64;
-    if (s > by_min) s = by_min;
-    if (s < 1) s = 1;
-    ch = (n + s - 1) / s;
-    ch = ((ch + 63) / 64) * 64;
-    if (ch > L.chunk_cap) ch = L.chunk_cap;
+    const int64_t target = L.target_wgs;
+    const int64_t by_min = (n + 63) / 64;
+    const int64_t s_cap = (n + L.chunk_cap - 1) / L.chunk_cap;
+    int64_t best_ch = 0, best_cost = -1;
+    for (int64_t r = 1; r <= 4; ++r) {
+      const int64_t sp = std::min<int64_t>(by_min, std::max<int64_t>(s_cap, r * target / bg));
+      const int64_t c = ((n + sp - 1) / sp + 63) / 64 * 64;
+      if (c > L.chunk_cap) continue;
+      const int64_t wgs = (n + c - 1) / c * (int64_t)bg;
+      const int64_t cost = (wgs + target - 1) / target * c;
+      if (best_cost < 0 || cost < best_cost || (cost == best_cost && c > best_ch)) {
+        best_cost = cost;
+        best_ch = c;
+      }
+    }
+    ch = (int)best_ch;
   }
   *chunk = ch;
   *n_splits = (n + ch - 1) / ch;
@@ -396,7 +404,10 @@ lcd_status lcd_decode_attn(lcd_cache* c, int32_t layer, const void* q, float* ou
   p.Hkv = cfg.n_kv_heads;
   p.C = L.C;
   p.n = n;
-  plan_splits(L, n, &p.n_splits, &p.chunk);
+  plan_splits(L, n, cfg.batch * cfg.n_kv_heads, &p.n_splits, &p.chunk);
+  if (p.n_splits < 1 || p.n_splits > L.max_splits || p.chunk < 64 || p.chunk > L.chunk_cap)
+    return fail(LCD_ESIZE, "split plan %d x %d outside the workspace bound %d", p.n_splits, p.chunk,
+                L.max_splits);
   p.qscale = c->qscale;
   int mode = lcd::kModePlain;
   if (cfg.rope) {

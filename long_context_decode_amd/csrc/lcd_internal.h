@@ -9,8 +9,8 @@ namespace lcd {
 
 // Decode workgroup: 4 waves of 64 lanes.
 constexpr int kDecodeThreads = 256;
-// Most slots one decode workgroup reduces (bounds its LDS logit buffer).
-constexpr int kMaxChunk = 4096;
+// Decode workgroups assumed resident at once (2 per CU on 256 CUs), for the split plan.
+constexpr int kResidentWorkgroups = 512;
 
 enum DecodeMode { kModeRope = 0, kModePlain = 1, kModePlainLogits = 2 };
 
@@ -33,7 +33,7 @@ struct DecodeParams {
   int64_t max_pos;     // victim candidates have pos <= max_pos
   int B, Hq, Hkv, C;
   int n;               // attended slots 0..n-1
-  int chunk;           // slots per split (multiple of 64, <= kMaxChunk)
+  int chunk;           // slots per split (multiple of 64)
   int n_splits;
   int full;            // ring has wrapped: ranks follow the ring order
   int S, W;            // sinks and window (rope mode)
@@ -69,6 +69,8 @@ hipError_t launch_fill_i32(int* p, int value, int64_t n, hipStream_t s);
 hipError_t launch_fill_f32(float* p, float value, int64_t n, hipStream_t s);
 
 bool decode_supported(int dtype, int D, int G);
+// Most slots one decode workgroup may own for G query heads per KV head (a multiple of 64).
+int decode_chunk_cap(int G);
 
 // SnapKV
 struct SnapkvParams {

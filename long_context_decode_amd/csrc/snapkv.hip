@@ -251,7 +251,9 @@ template <int D, int RB>
 __global__ void __launch_bounds__(256) snapkv_colscore_kernel(SnapkvParams p) {
   __shared__ float sM[kMaxRows], sI[kMaxRows];
   __shared__ __attribute__((aligned(16))) char stage[4][block_lds_bytes<D>()];
-  const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // Walk K in the reverse of the row-statistics pass: the tail of K, read last by that
+  // pass, is the part most likely still held by the memory-side cache.
+  const int tile = gridDim.x - 1 - blockIdx.x, h = gridDim.y - 1 - blockIdx.y, b = gridDim.z - 1 - blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const size_t bh = (size_t)b * p.H + h;
   if (threadIdx.x < kMaxRows) {
