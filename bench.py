@@ -44,6 +44,8 @@ def _parse(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--snapkv-only", action="store_true",
+                    help="time the SnapKV compression alone and print its record (for profiling)")
     ap.add_argument("--counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
                          "'bench.py --only --copy-calibration' into the traffic record and exit (no GPU)")
@@ -87,7 +89,7 @@ def _read_counter_csv(path, counter):
     return out
 
 
-def _counter_summary(fetch_csv, write_csv):
+def _counter_summary(fetch_csv, write_csv, out=TRAFFIC_RECORD):
     """Per-dispatch FETCH_SIZE / WRITE_SIZE of the decode kernel, each scaled by what the
     counter reads for the 1 GiB calibration copy; writes the traffic record."""
     import statistics
@@ -113,12 +115,12 @@ def _counter_summary(fetch_csv, write_csv):
         "Two rocprofv3 counter runs of the same command, one counter each:",
         "",
         "```",
-        "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/p17/fetch -o run -- "
+        "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/p21/fetch -o run -- "
         "python3 bench.py --only --copy-calibration --steps 64 --warmup 8 --no-cpu-baseline",
-        "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/p17/write -o run -- "
+        "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/p21/write -o run -- "
         "python3 bench.py --only --copy-calibration --steps 64 --warmup 8 --no-cpu-baseline",
-        "python3 bench.py --counters gpurun_out/p17/fetch/run_counter_collection.csv "
-        "gpurun_out/p17/write/run_counter_collection.csv",
+        "python3 bench.py --counters gpurun_out/p21/fetch/run_counter_collection.csv "
+        "gpurun_out/p21/write/run_counter_collection.csv",
         "```",
         "",
         "The calibration copy moves 1 GiB in each direction; each counter is scaled by "
@@ -132,16 +134,17 @@ def _counter_summary(fetch_csv, write_csv):
                      f"{r['dispatches']} | {r['decode_kib'] * 1024 * r['scale']:.0f} |")
     lines += ["", f"traffic-bytes-per-launch: {traffic:.0f}", f"sources-sha256: {_sources_digest()}",
               f"sources: {', '.join(TRAFFIC_SOURCES)}", ""]
-    with open(TRAFFIC_RECORD, "w") as fh:
+    with open(out, "w") as fh:
         fh.write("\n".join(lines))
-    print(f"traffic {traffic:.0f} B per launch -> {TRAFFIC_RECORD}")
+    print(f"traffic {traffic:.0f} B per launch -> {out}")
+    return traffic
 
 
-def _traffic():
+def _traffic(record=TRAFFIC_RECORD):
     """Scaled counter bytes per launch of the headline decode kernel, or None when no
     record exists or the record was taken on other sources."""
     try:
-        with open(TRAFFIC_RECORD) as f:
+        with open(record) as f:
             kv = dict(line.split(": ", 1) for line in f.read().splitlines() if ": " in line and
                       line.split(": ", 1)[0] in ("traffic-bytes-per-launch", "sources-sha256"))
     except OSError:
@@ -380,6 +383,9 @@ def main(argv=None):
     import long_context_decode_amd as L
     from synth import WORKLOADS
 
+    if a.snapkv_only:
+        print(json.dumps(_snapkv_bench(L, WORKLOADS["snapkv_32k"])), flush=True)
+        return 0
     if a.copy_calibration:
         _copy_calibration()
     w = WORKLOADS[a.workload]

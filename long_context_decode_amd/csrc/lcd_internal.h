@@ -83,9 +83,11 @@ struct SnapkvParams {
   float* scores_out;   // [B][H][N - Lobs] or null
   float* rowstat;      // ws: [B][H][tiles][Lobs][2]
   float* rowfinal;     // ws: [B][H][Lobs][2] (max, 1/sum) log2 domain
-  float* colscore;     // ws: [B][H][N - Lobs] raw mean scores
-  float* pooled;       // ws: [B][H][N - Lobs]
+  float* colscore;     // ws: [B][H][sstride] raw mean scores (N - Lobs used)
+  float* pooled;       // ws: [B][H][sstride]
   int B, H, D, N, Lobs, ksize, k_keep, pool, out_rows, tiles;
+  int sstride;         // row stride of colscore / pooled: N - Lobs rounded up to 4
+  int h0;              // first head the scoring kernels cover (grid y covers the rest)
   float qscale;        // scale * log2(e)
 };
 size_t snapkv_ws_bytes(int B, int H, int N, int Lobs);

@@ -24,6 +24,21 @@
 
 #include "lcd_internal.h"
 
+// Memory-access knobs, chosen by measurement on MI355X: pieces per thread of the gather
+// kernel and the load / store kinds of the gather and row-statistics passes.
+#ifndef LCD_GATHER_U
+#define LCD_GATHER_U 1
+#endif
+#ifndef LCD_GATHER_NT_LOAD
+#define LCD_GATHER_NT_LOAD 0
+#endif
+#ifndef LCD_GATHER_NT_STORE
+#define LCD_GATHER_NT_STORE 0
+#endif
+#ifndef LCD_ROWSTATS_NT
+#define LCD_ROWSTATS_NT 1
+#endif
+
 namespace lcd {
 
 namespace {
@@ -68,7 +83,9 @@ constexpr int block_lds_bytes() { return 32 * lds_row_bytes<D>(); }
 template <int D>
 constexpr int chunk_pieces() { return chunk_w<D>() / 16; }  // 16-byte pieces per lane per chunk
 
-template <int D>
+// NT: non-temporal loads (the last read of these rows); otherwise plain loads, which
+// leave the rows in the caches for the second pass.
+template <int D, bool NT>
 __device__ inline void chunk_load(const uint16_t* k, int N, int key0, int c, int lane,
                                   u32x4 (&raw)[chunk_pieces<D>()]) {
   constexpr int PPR = chunk_w<D>() * 2 / 16;  // pieces per row of the chunk
@@ -77,9 +94,11 @@ __device__ inline void chunk_load(const uint16_t* k, int N, int key0, int c, int
     const int piece = i * 64 + lane;
     const int row = piece / PPR, col = piece % PPR;
     const int key = key0 + row;
-    raw[i] = key < N ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-                           k + (size_t)key * D + c * chunk_w<D>() + col * 8))
-                     : u32x4{0, 0, 0, 0};
+    const u32x4* src = reinterpret_cast<const u32x4*>(k + (size_t)key * D + c * chunk_w<D>() + col * 8);
+    if (key < N)
+      raw[i] = NT ? __builtin_nontemporal_load(src) : *src;
+    else
+      raw[i] = u32x4{0, 0, 0, 0};
   }
 }
 
@@ -115,7 +134,7 @@ template <int D, int RB>
 __global__ void __launch_bounds__(256) snapkv_rowstats_kernel(SnapkvParams p) {
   __shared__ float sm[4][kMaxRows], sl[4][kMaxRows];
   __shared__ __attribute__((aligned(16))) char stage[4][block_lds_bytes<D>()];
-  const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tile = blockIdx.x, h = p.h0 + blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const size_t bh = (size_t)b * p.H + h;
   const uint16_t* q = reinterpret_cast<const uint16_t*>(p.q_obs) + bh * p.Lobs * D;
@@ -134,7 +153,7 @@ __global__ void __launch_bounds__(256) snapkv_rowstats_kernel(SnapkvParams p) {
   constexpr int NC = D / chunk_w<D>();
   constexpr int FS = chunk_w<D>() / 16;  // fragments per chunk
   u32x4 raw[chunk_pieces<D>()];
-  chunk_load<D>(k, p.N, wkey0, 0, lane, raw);
+  chunk_load<D, LCD_ROWSTATS_NT != 0>(k, p.N, wkey0, 0, lane, raw);
   for (int blk = 0; blk < kWaveBlocks; ++blk) {
     const int key0 = wkey0 + blk * 32;
     if (key0 >= p.N) break;  // wave-uniform
@@ -145,8 +164,8 @@ __global__ void __launch_bounds__(256) snapkv_rowstats_kernel(SnapkvParams p) {
     for (int c = 0; c < NC; ++c) {
       chunk_store_lds<D>(stage[wave], lane, raw);
       // prefetch the next chunk (of this block or the next one)
-      if (c + 1 < NC) chunk_load<D>(k, p.N, key0, c + 1, lane, raw);
-      else if (blk + 1 < kWaveBlocks) chunk_load<D>(k, p.N, key0 + 32, 0, lane, raw);
+      if (c + 1 < NC) chunk_load<D, LCD_ROWSTATS_NT != 0>(k, p.N, key0, c + 1, lane, raw);
+      else if (blk + 1 < kWaveBlocks) chunk_load<D, LCD_ROWSTATS_NT != 0>(k, p.N, key0 + 32, 0, lane, raw);
       wave_lds_order();
       bf16x8 kf[FS];
       chunk_frags_lds<D>(stage[wave], lane, kf);
@@ -208,12 +227,12 @@ __global__ void __launch_bounds__(256) snapkv_rowstats_kernel(SnapkvParams p) {
 }
 
 // ---------------------------------------------------------------------------- 2. rowfinal
-// One workgroup per (row, head): threads stride over (tile, observation row) pairs,
-// then each row's partial maxima / sums are merged through LDS.
+// One workgroup per (head of the group, batch row): threads stride over (tile,
+// observation row) pairs, then each row's partial maxima / sums are merged through LDS.
 constexpr int kFinalThreads = 1024;
 __global__ void __launch_bounds__(kFinalThreads) snapkv_rowfinal_kernel(SnapkvParams p) {
   __shared__ float pm[kFinalThreads], pl[kFinalThreads];
-  const size_t bh = blockIdx.x;
+  const size_t bh = (size_t)blockIdx.y * p.H + p.h0 + blockIdx.x;
   const int rows = ((p.Lobs + 31) / 32) * 32;
   const int t = threadIdx.x % rows, part = threadIdx.x / rows, parts = kFinalThreads / rows;
   float M = -INFINITY, L = 0.f;
@@ -251,9 +270,10 @@ template <int D, int RB>
 __global__ void __launch_bounds__(256) snapkv_colscore_kernel(SnapkvParams p) {
   __shared__ float sM[kMaxRows], sI[kMaxRows];
   __shared__ __attribute__((aligned(16))) char stage[4][block_lds_bytes<D>()];
-  // Walk K in the reverse of the row-statistics pass: the tail of K, read last by that
-  // pass, is the part most likely still held by the memory-side cache.
-  const int tile = gridDim.x - 1 - blockIdx.x, h = gridDim.y - 1 - blockIdx.y, b = gridDim.z - 1 - blockIdx.z;
+  // Walk K in the reverse of the row-statistics pass: the rows read last there are the
+  // likeliest still cached.
+  const int tile = gridDim.x - 1 - blockIdx.x, h = p.h0 + (int)(gridDim.y - 1 - blockIdx.y),
+            b = gridDim.z - 1 - blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const size_t bh = (size_t)b * p.H + h;
   if (threadIdx.x < kMaxRows) {
@@ -273,7 +293,7 @@ __global__ void __launch_bounds__(256) snapkv_colscore_kernel(SnapkvParams p) {
   constexpr int NC = D / chunk_w<D>();
   constexpr int FS = chunk_w<D>() / 16;
   u32x4 raw[chunk_pieces<D>()];
-  chunk_load<D>(k, Np, wkey0, 0, lane, raw);
+  chunk_load<D, true>(k, Np, wkey0, 0, lane, raw);
   for (int blk = 0; blk < kWaveBlocks; ++blk) {
     const int key0 = wkey0 + blk * 32;
     if (key0 >= Np) break;  // wave-uniform
@@ -283,8 +303,8 @@ __global__ void __launch_bounds__(256) snapkv_colscore_kernel(SnapkvParams p) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       chunk_store_lds<D>(stage[wave], lane, raw);
-      if (c + 1 < NC) chunk_load<D>(k, Np, key0, c + 1, lane, raw);
-      else if (blk + 1 < kWaveBlocks) chunk_load<D>(k, Np, key0 + 32, 0, lane, raw);
+      if (c + 1 < NC) chunk_load<D, true>(k, Np, key0, c + 1, lane, raw);
+      else if (blk + 1 < kWaveBlocks) chunk_load<D, true>(k, Np, key0 + 32, 0, lane, raw);
       wave_lds_order();
       bf16x8 kf[FS];
       chunk_frags_lds<D>(stage[wave], lane, kf);
@@ -308,7 +328,7 @@ __global__ void __launch_bounds__(256) snapkv_colscore_kernel(SnapkvParams p) {
     }
     sc += __shfl_xor(sc, 32, 64);
     const int key = key0 + (lane & 31);
-    if (lane < 32 && key < Np) p.colscore[bh * Np + key] = sc * inv_rows;
+    if (lane < 32 && key < Np) p.colscore[bh * p.sstride + key] = sc * inv_rows;
   }
 }
 
@@ -349,7 +369,7 @@ __global__ void snapkv_pool_kernel(SnapkvParams p) {
   for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (size_t)gridDim.x * blockDim.x) {
     const size_t bh = e / Np;
     const int i = (int)(e % Np);
-    const float* s = p.colscore + bh * Np;
+    const float* s = p.colscore + bh * p.sstride;
     float acc = 0.f;  // scores are >= 0: also the identity of max
     for (int d = -rad; d <= rad; ++d) {
       const int j = i + d;
@@ -357,42 +377,117 @@ __global__ void snapkv_pool_kernel(SnapkvParams p) {
       acc = p.pool ? fmaxf(acc, s[j]) : acc + s[j];
     }
     const float v = p.pool ? acc : acc * inv_k;
-    p.pooled[e] = v;
+    p.pooled[bh * p.sstride + i] = v;
     if (p.scores_out) p.scores_out[e] = v;
   }
 }
 
 // Radix select of the k-th largest pooled score of one head, with the scores held in
-// registers: thread t owns the contiguous positions [t*PER, (t+1)*PER).  Three passes of
-// 11-bit digits (bits 31..21, 20..10, 9..0) over the float bit patterns; each pass
-// histograms the candidates that match the prefix fixed so far (4 interleaved copies
-// of the histogram cut LDS atomic conflicts), then a block scan over the bins, highest
-// digit first, finds the digit where the count of larger values reaches k.
+// registers: thread t owns the contiguous positions [t*PER, (t+1)*PER).
+//
+// With HALO = 4 the pooling is done here (kernel_size <= 9): each thread reads its raw
+// column scores with HALO neighbours on each side as 16-byte loads and pools them in
+// registers, in the same order and with the same zero padding as snapkv_pool_kernel;
+// with HALO = 0 the input is the pooled scores.
+//
+// Scores are >= 0, so their float bit patterns order like the values.  The select runs
+// on v = bits - min(bits) over the head: its bit length Lb is set by the spread of the
+// scores (a few octaves), so the first 11-bit digit already separates values that the
+// raw exponent bits would lump into a handful of bins (fewer LDS atomic conflicts).
+// Digits are taken from bit Lb down in 11-bit steps; each pass histograms the
+// candidates that match the prefix fixed so far (4 interleaved copies of the histogram
+// cut conflicts further), then a block scan over the bins, highest digit first, finds
+// the digit where the count of larger values reaches k.
 constexpr int kDigitBits = 11;
 constexpr int kBins = 1 << kDigitBits;
 constexpr int kHistCopies = 4;
 
-template <int PER>
+template <int PER, int HALO>
 __global__ void __launch_bounds__(kSelectThreads) snapkv_select_kernel(SnapkvParams p) {
+  static_assert(PER % 4 == 0 && HALO % 4 == 0, "16-byte pieces");
   __shared__ int hist[kHistCopies * kBins];
   __shared__ int warp_tot[kSelectThreads / 64];
+  __shared__ uint32_t wmin[kSelectThreads / 64], wmax[kSelectThreads / 64];
   __shared__ int total;
   __shared__ int s_digit, s_krem;
   const int h = blockIdx.x, b = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const size_t bh = (size_t)b * p.H + h;
   const int Np = p.N - p.Lobs;
-  const float* pooled = p.pooled + bh * Np;
+  const float* src = (HALO > 0 ? p.colscore : p.pooled) + bh * p.sstride;
   const int i0 = threadIdx.x * PER;
+
+  // ---- the thread's scores as bit patterns (rows are padded to a multiple of 4 floats)
   uint32_t u[PER];
+  {
+    constexpr int NW = PER + 2 * HALO;
+    float w[NW];
 #pragma unroll
-  for (int j = 0; j < PER; ++j) u[j] = i0 + j < Np ? __float_as_uint(pooled[i0 + j]) : 0u;
+    for (int q = 0; q < NW / 4; ++q) {
+      const int e0 = i0 - HALO + 4 * q;  // a multiple of 4
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (e0 >= 0 && e0 < Np) v = *reinterpret_cast<const float4*>(src + e0);
+      w[4 * q] = v.x;
+      w[4 * q + 1] = e0 + 1 < Np ? v.y : 0.f;
+      w[4 * q + 2] = e0 + 2 < Np ? v.z : 0.f;
+      w[4 * q + 3] = e0 + 3 < Np ? v.w : 0.f;
+    }
+    if constexpr (HALO > 0) {
+      const int rad = p.ksize / 2;
+      const float inv_k = 1.f / (float)p.ksize;
+      float* so = p.scores_out ? p.scores_out + bh * Np : nullptr;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        float acc = 0.f;  // scores are >= 0: also the identity of max; padding adds 0
+#pragma unroll
+        for (int d = -HALO; d <= HALO; ++d)
+          if (d >= -rad && d <= rad) acc = p.pool ? fmaxf(acc, w[j + HALO + d]) : acc + w[j + HALO + d];
+        const float sc = p.pool ? acc : acc * inv_k;
+        if (so && i0 + j < Np) so[i0 + j] = sc;
+        u[j] = __float_as_uint(sc);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < PER; ++j) u[j] = __float_as_uint(w[j]);
+    }
+  }
+  uint32_t lmin = 0xffffffffu, lmax = 0u;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    if (i0 + j < Np) {
+      lmin = min(lmin, u[j]);
+      lmax = max(lmax, u[j]);
+    }
+  }
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    lmin = min(lmin, (uint32_t)__shfl_xor((int)lmin, off, 64));
+    lmax = max(lmax, (uint32_t)__shfl_xor((int)lmax, off, 64));
+  }
+  if (lane == 0) {
+    wmin[wave] = lmin;
+    wmax[wave] = lmax;
+  }
+  __syncthreads();
+  uint32_t umin = 0xffffffffu, umax = 0u;
+#pragma unroll
+  for (int w = 0; w < kSelectThreads / 64; ++w) {
+    umin = min(umin, wmin[w]);
+    umax = max(umax, wmax[w]);
+  }
   const int k = p.k_keep;
+  const uint32_t range = umax >= umin ? umax - umin : 0u;
+  const int Lb = range ? 32 - __clz((int)range) : 0;
+  // from here on u holds v = bits - umin (order-preserving over the valid positions;
+  // positions past Np are excluded by index everywhere)
+#pragma unroll
+  for (int j = 0; j < PER; ++j) u[j] -= umin;
   uint32_t prefix = 0, mask = 0;
   int krem = k;
   if (k > 0) {
-    for (int pass = 0; pass < 3; ++pass) {
-      const int shift = 32 - kDigitBits * (pass + 1) > 0 ? 32 - kDigitBits * (pass + 1) : 0;
-      const int bits = pass < 2 ? kDigitBits : 32 - 2 * kDigitBits;
+    for (int hi = Lb; hi > 0; hi -= kDigitBits) {
+      const int shift = hi > kDigitBits ? hi - kDigitBits : 0;
+      const int bits = hi - shift;
       const uint32_t dmask = (1u << bits) - 1u;
       for (int i = threadIdx.x; i < kHistCopies * kBins; i += kSelectThreads) hist[i] = 0;
       __syncthreads();
@@ -425,7 +520,7 @@ __global__ void __launch_bounds__(kSelectThreads) snapkv_select_kernel(SnapkvPar
       __syncthreads();
     }
   }
-  const uint32_t T = prefix;                // bit pattern of the k-th largest score
+  const uint32_t T = prefix;                   // v of the k-th largest score
   const int take_eq_total = k > 0 ? krem : 0;  // how many values equal to T are kept
   int n_gt = 0, n_eq = 0;
   if (k > 0) {
@@ -457,7 +552,10 @@ __global__ void __launch_bounds__(kSelectThreads) snapkv_select_kernel(SnapkvPar
 }
 
 // ---------------------------------------------------------------------------- 5. gather
-__global__ void snapkv_gather_kernel(SnapkvParams p, int rows) {
+// Row copies of the kept K and V rows as 16-byte pieces: each thread moves kGatherU
+// pieces of K and of V per iteration, all loads issued before the stores.
+constexpr int kGatherU = LCD_GATHER_U;
+__global__ void __launch_bounds__(256) snapkv_gather_kernel(SnapkvParams p, int rows) {
   const int h = blockIdx.y, b = blockIdx.z;
   const size_t bh = (size_t)b * p.H + h;
   const int chunks = p.D * 2 / 16;  // 16-byte pieces per row
@@ -467,12 +565,36 @@ __global__ void snapkv_gather_kernel(SnapkvParams p, int rows) {
   char* ko = reinterpret_cast<char*>(p.k_out) + bh * (size_t)p.out_rows * p.D * 2;
   char* vo = reinterpret_cast<char*>(p.v_out) + bh * (size_t)p.out_rows * p.D * 2;
   const int total = rows * chunks;
-  for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < total; e += gridDim.x * blockDim.x) {
-    const int row = e / chunks, c = e % chunks;
-    const size_t src = (size_t)idx[row] * p.D * 2 + (size_t)c * 16;
-    const size_t dst = (size_t)row * p.D * 2 + (size_t)c * 16;
-    *reinterpret_cast<uint4*>(ko + dst) = *reinterpret_cast<const uint4*>(k + src);
-    *reinterpret_cast<uint4*>(vo + dst) = *reinterpret_cast<const uint4*>(v + src);
+  for (int e0 = blockIdx.x * 256 * kGatherU + threadIdx.x; e0 < total; e0 += gridDim.x * 256 * kGatherU) {
+    u32x4 kr[kGatherU], vr[kGatherU];
+#pragma unroll
+    for (int u = 0; u < kGatherU; ++u) {
+      const int e = e0 + u * 256;
+      if (e < total) {
+        const size_t src = (size_t)idx[e / chunks] * p.D * 2 + (size_t)(e % chunks) * 16;
+#if LCD_GATHER_NT_LOAD
+        kr[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k + src));
+        vr[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v + src));
+#else
+        kr[u] = *reinterpret_cast<const u32x4*>(k + src);
+        vr[u] = *reinterpret_cast<const u32x4*>(v + src);
+#endif
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kGatherU; ++u) {
+      const int e = e0 + u * 256;
+      if (e < total) {
+        const size_t dst = (size_t)(e / chunks) * p.D * 2 + (size_t)(e % chunks) * 16;
+#if LCD_GATHER_NT_STORE
+        __builtin_nontemporal_store(kr[u], reinterpret_cast<u32x4*>(ko + dst));
+        __builtin_nontemporal_store(vr[u], reinterpret_cast<u32x4*>(vo + dst));
+#else
+        *reinterpret_cast<u32x4*>(ko + dst) = kr[u];
+        *reinterpret_cast<u32x4*>(vo + dst) = vr[u];
+#endif
+      }
+    }
   }
 }
 
@@ -482,29 +604,37 @@ struct WsLayout {
   size_t rowstat, rowfinal, colscore, pooled, total;
 };
 
+// Rows of the column-score and pooled buffers are padded to a multiple of 4 floats
+// (16-byte loads in the select kernel).
+size_t score_stride(int N, int Lobs) {
+  const size_t np = (size_t)(N - Lobs);
+  return np ? (np + 3) / 4 * 4 : 4;
+}
+
 WsLayout ws_layout(int B, int H, int N, int Lobs) {
   const size_t bh = (size_t)B * H;
   const size_t tiles = (size_t)(N + kTileKeys - 1) / kTileKeys;
-  const size_t np = (size_t)(N - Lobs);
+  const size_t st = score_stride(N, Lobs);
   WsLayout w;
   w.rowstat = 0;
   w.rowfinal = align256(w.rowstat + bh * tiles * kMaxRows * 2 * sizeof(float));
   w.colscore = align256(w.rowfinal + bh * kMaxRows * 2 * sizeof(float));
-  w.pooled = align256(w.colscore + bh * (np ? np : 1) * sizeof(float));
-  w.total = align256(w.pooled + bh * (np ? np : 1) * sizeof(float));
+  w.pooled = align256(w.colscore + bh * st * sizeof(float));
+  w.total = align256(w.pooled + bh * st * sizeof(float));
   return w;
 }
 
 template <int D>
 hipError_t launch_d(SnapkvParams p, hipStream_t s) {
-  const dim3 sgrid(p.tiles, p.H, p.B);
   const bool two = p.Lobs > 32;
+  const int np = p.N - p.Lobs;
+  p.h0 = 0;
+  const dim3 sgrid(p.tiles, p.H, p.B);
   if (two)
     hipLaunchKernelGGL((snapkv_rowstats_kernel<D, 2>), sgrid, dim3(256), 0, s, p);
   else
     hipLaunchKernelGGL((snapkv_rowstats_kernel<D, 1>), sgrid, dim3(256), 0, s, p);
-  hipLaunchKernelGGL(snapkv_rowfinal_kernel, dim3(p.B * p.H), dim3(kFinalThreads), 0, s, p);
-  const int np = p.N - p.Lobs;
+  hipLaunchKernelGGL(snapkv_rowfinal_kernel, dim3(p.H, p.B), dim3(kFinalThreads), 0, s, p);
   if (np > 0) {
     const dim3 cgrid((np + kTileKeys - 1) / kTileKeys, p.H, p.B);
     if (two)
@@ -512,24 +642,34 @@ hipError_t launch_d(SnapkvParams p, hipStream_t s) {
     else
       hipLaunchKernelGGL((snapkv_colscore_kernel<D, 1>), cgrid, dim3(256), 0, s, p);
   }
-  if (np > 0) {
+  // pooling is fused into the select kernel for kernel_size <= 9
+  const bool fused = p.ksize <= 9;
+  if (np > 0 && !fused) {
     const size_t work = (size_t)p.B * p.H * np;
     const size_t blocks = (work + 255) / 256;
     hipLaunchKernelGGL(snapkv_pool_kernel, dim3(blocks < 8192 ? blocks : 8192), dim3(256), 0, s, p);
   }
   const int per = (np + kSelectThreads - 1) / kSelectThreads;
   const dim3 sel_grid(p.H, p.B);
+#define LCD_SELECT(PER)                                                                    \
+  do {                                                                                     \
+    if (fused)                                                                             \
+      hipLaunchKernelGGL((snapkv_select_kernel<PER, 4>), sel_grid, dim3(kSelectThreads), 0, s, p); \
+    else                                                                                   \
+      hipLaunchKernelGGL((snapkv_select_kernel<PER, 0>), sel_grid, dim3(kSelectThreads), 0, s, p); \
+  } while (0)
   if (per <= 8)
-    hipLaunchKernelGGL(snapkv_select_kernel<8>, sel_grid, dim3(kSelectThreads), 0, s, p);
+    LCD_SELECT(8);
   else if (per <= 16)
-    hipLaunchKernelGGL(snapkv_select_kernel<16>, sel_grid, dim3(kSelectThreads), 0, s, p);
+    LCD_SELECT(16);
   else if (per <= 32)
-    hipLaunchKernelGGL(snapkv_select_kernel<32>, sel_grid, dim3(kSelectThreads), 0, s, p);
+    LCD_SELECT(32);
   else
-    hipLaunchKernelGGL(snapkv_select_kernel<64>, sel_grid, dim3(kSelectThreads), 0, s, p);
+    LCD_SELECT(64);
+#undef LCD_SELECT
   const int rows = p.k_keep + p.Lobs;
   const int chunks = p.D * 2 / 16;
-  const int blocks_x = (rows * chunks + 255) / 256;
+  const int blocks_x = (rows * chunks + 256 * kGatherU - 1) / (256 * kGatherU);
   hipLaunchKernelGGL(snapkv_gather_kernel, dim3(blocks_x < 1024 ? blocks_x : 1024, p.H, p.B), dim3(256), 0, s, p,
                      rows);
   return hipGetLastError();
@@ -548,6 +688,7 @@ hipError_t launch_snapkv(const SnapkvParams& in, hipStream_t s) {
   p.colscore = reinterpret_cast<float*>(base + w.colscore);
   p.pooled = reinterpret_cast<float*>(base + w.pooled);
   p.tiles = (p.N + kTileKeys - 1) / kTileKeys;
+  p.sstride = (int)score_stride(p.N, p.Lobs);
   switch (p.D) {
     case 64: return launch_d<64>(p, s);
     case 128: return launch_d<128>(p, s);

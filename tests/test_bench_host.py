@@ -1,0 +1,56 @@
+"""Host logic of bench.py (no GPU): the counter-traffic record and its staleness check."""
+import csv
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+FIELDS = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id", "Thread_Id", "Grid_Size",
+          "Kernel_Id", "Kernel_Name", "Workgroup_Size", "LDS_Block_Size", "Scratch_Size", "VGPR_Count",
+          "Accum_VGPR_Count", "SGPR_Count", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+
+
+def _csv(path, counter, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=FIELDS)
+        w.writeheader()
+        for i, (name, val) in enumerate(rows, 1):
+            w.writerow({k: 0 for k in FIELDS} | {"Dispatch_Id": i, "Correlation_Id": i, "Kernel_Name": name,
+                                                  "Grid_Size": 256, "Counter_Name": counter, "Counter_Value": val})
+
+
+def test_counter_summary_scales_by_calibration_copy(tmp_path):
+    dec = f"void lcd::{bench.DECODE_KERNEL}<lcd::bf16_t, 128, 1, 0>(lcd::DecodeParams)"
+    copy = "__amd_rocclr_copyBuffer"
+    gib_kib = (1 << 30) / 1024
+    # fetch reads half the copied bytes, write all of them; a later copy of another size is ignored
+    _csv(tmp_path / "f.csv", "FETCH_SIZE", [("fill", 1.0), (copy, gib_kib / 2), (copy, gib_kib / 2),
+                                           (copy, gib_kib / 2), (dec, 1000.0), (dec, 1200.0), (copy, 7.0)])
+    _csv(tmp_path / "w.csv", "WRITE_SIZE", [(copy, gib_kib), (copy, gib_kib), (copy, gib_kib), (dec, 256.0),
+                                           (dec, 256.0)])
+    out = tmp_path / "record.md"
+    traffic = bench._counter_summary(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), out=str(out))
+    assert traffic == pytest.approx(1100.0 * 1024 * 2 + 256.0 * 1024)
+    assert bench._traffic(str(out)) == int(round(traffic))
+    # a record taken on other sources is stale
+    text = out.read_text().replace(bench._sources_digest(), "0" * 64)
+    out.write_text(text)
+    assert bench._traffic(str(out)) is None
+    assert bench._traffic(str(tmp_path / "missing.md")) is None
+
+
+def test_counter_summary_needs_the_calibration_copy(tmp_path):
+    dec = f"void lcd::{bench.DECODE_KERNEL}<lcd::bf16_t, 128, 1, 0>(lcd::DecodeParams)"
+    _csv(tmp_path / "f.csv", "FETCH_SIZE", [(dec, 1000.0)])
+    _csv(tmp_path / "w.csv", "WRITE_SIZE", [(dec, 1000.0)])
+    with pytest.raises(SystemExit):
+        bench._counter_summary(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), out=str(tmp_path / "r.md"))
+
+
+def test_more_than_one_gpu_is_refused(capsys):
+    assert bench.main(["--gpus", "2"]) == 2
+    assert "one GPU" in capsys.readouterr().out

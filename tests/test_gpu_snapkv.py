@@ -98,6 +98,8 @@ BASE = WORKLOADS["snapkv_32k"]
     dict(n_q_heads=2, n_prompt=513, l_obs=17, k_keep=0, head_dim=256),           # keep nothing
     dict(n_q_heads=1, n_prompt=200, l_obs=10, k_keep=190),                       # keep everything
     dict(batch=2, n_q_heads=2, n_prompt=2048, l_obs=32, k_keep=328),
+    dict(n_q_heads=2, n_prompt=901, l_obs=16, k_keep=120, kernel_size=11),        # pooling kernel path
+    dict(n_q_heads=1, n_prompt=40000, l_obs=8, k_keep=4000),                      # 64 scores per thread
 ])
 def test_snapkv_small(L, case):
     w = scaled(BASE, name="snapkv_small_" + "_".join(f"{k}{v}" for k, v in case.items()), **case)
@@ -105,8 +107,9 @@ def test_snapkv_small(L, case):
     _run(L, w)
 
 
-def test_snapkv_max_pool_and_out_rows(L):
-    w = scaled(BASE, name="snapkv_max", n_q_heads=2, n_prompt=700, l_obs=16, k_keep=64)
+@pytest.mark.parametrize("ksize", [5, 13])
+def test_snapkv_max_pool_and_out_rows(L, ksize):
+    w = scaled(BASE, name=f"snapkv_max_k{ksize}", n_q_heads=2, n_prompt=700, l_obs=16, k_keep=64, kernel_size=ksize)
     _run(L, w, pool=1, out_rows=100)
 
 
