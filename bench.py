@@ -324,7 +324,9 @@ def _snapkv_bench(L, w, reps=20):
 
 
 def _cpu_baseline_streaming(w, budget_s):
-    """The fp64 oracle on a bounded sample of one decode step (single thread)."""
+    """The fp64 oracle on a bounded sample of consecutive decode steps (single thread):
+    whole steps (every layer, row and KV head) until the budget is spent, the last step
+    possibly partial."""
     import numpy as np
 
     try:
@@ -333,37 +335,40 @@ def _cpu_baseline_streaming(w, budget_s):
         threadpool_limits = None
     import oracle
 
-    t = w.prefill + 7  # a decode step after the ring has wrapped
-    toks = oracle.retained_tokens(t, w.n_sink, w.window)
+    t0 = w.prefill + 7  # decode steps after the ring has wrapped
     G = w.group
     heads_per_step = w.batch * w.n_kv_heads * w.n_layers
-    done, elapsed = 0, 0.0
+    done, elapsed, t = 0, 0.0, t0
     limiter = threadpool_limits(1) if threadpool_limits else None
     try:
-        for layer in range(w.n_layers):
-            for b in range(w.batch):
-                for g in range(w.n_kv_heads):
-                    kk = w.token_block("k", layer, toks, batches=[b], heads=[g])[0]
-                    vv = w.token_block("v", layer, toks, batches=[b], heads=[g])[0]
-                    qq = w.token_block("q", layer, [t], batches=[b], heads=np.arange(g * G, g * G + G))[0, :, 0, :]
-                    t1 = time.perf_counter()
-                    oracle.streaming_decode(qq, lambda _t, kk=kk, vv=vv: (kk, vv), t, w.n_sink, w.window,
-                                            w.rope_base)
-                    elapsed += time.perf_counter() - t1
-                    done += 1
+        while elapsed < budget_s:
+            toks = oracle.retained_tokens(t, w.n_sink, w.window)
+            for layer in range(w.n_layers):
+                for b in range(w.batch):
+                    for g in range(w.n_kv_heads):
+                        kk = w.token_block("k", layer, toks, batches=[b], heads=[g])[0]
+                        vv = w.token_block("v", layer, toks, batches=[b], heads=[g])[0]
+                        qq = w.token_block("q", layer, [t], batches=[b], heads=np.arange(g * G, g * G + G))[0, :, 0, :]
+                        t1 = time.perf_counter()
+                        oracle.streaming_decode(qq, lambda _t, kk=kk, vv=vv: (kk, vv), t, w.n_sink, w.window,
+                                                w.rope_base)
+                        elapsed += time.perf_counter() - t1
+                        done += 1
+                        if elapsed >= budget_s:
+                            break
                     if elapsed >= budget_s:
                         break
                 if elapsed >= budget_s:
                     break
-            if elapsed >= budget_s:
-                break
+            t += 1
     finally:
         if limiter is not None:
             limiter.restore_original_limits()
     steps_per_s = (done / heads_per_step) / elapsed
     return {"value": steps_per_s, "unit": "decode steps/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} of the {heads_per_step} (layer, batch row, KV head) slices of decode step t={t} "
-                      f"({elapsed:.1f} s of fp64 numpy on one thread; input generation excluded)"}
+            "sample": f"{done} (layer, batch row, KV head) slices = {done / heads_per_step:.2f} decode steps from "
+                      f"t={t0} ({heads_per_step} slices per step; {elapsed:.1f} s of fp64 numpy on one thread; "
+                      f"input generation excluded)"}
 
 
 def main(argv=None):
