@@ -243,6 +243,22 @@ lcd_status lcd_snapkv_compress(const lcd_snapkv_params* p, const void* q_obs, co
                                void* k_out, void* v_out, int32_t* idx_out, float* scores_out, void* ws,
                                uint64_t ws_bytes, void* stream);
 
+/* PyramidKV per-layer budgets ---------------------------------------------------
+ * [KVC] "Alocação piramidal com o PyramidKV": the budget of layer l falls linearly
+ * with depth, B_l = b_base + dB * (n_layers - 1 - l) / (n_layers - 1), and the
+ * budgets meet the global target, sum B_l = n_layers * b_target, which fixes
+ * dB = 2 * (b_target - b_base).  Whole tokens: each B_l is rounded down and the
+ * tokens that rounding lost (fewer than n_layers) go one each to the lowest layers
+ * 0, 1, ..., so the sum is exact; one layer gets b_target.  Layer 0 is the lowest.
+ * A budget counts every row a layer keeps per head: with SnapKV, k_keep = B_l - l_obs.
+ *   n_layers     1 .. 4096
+ *   b_base       budget of the top layer, 0 .. 2^24
+ *   b_target     mean budget, 0 .. 2^24
+ *   budgets_out  host int32 [n_layers], written on success only
+ * Host-only (no device work, no stream).  LCD_EINVAL for a null pointer, values out
+ * of range, or a layer budget that would be negative (b_base > 2 * b_target). */
+lcd_status lcd_pyramid_budgets(int32_t n_layers, int32_t b_base, int32_t b_target, int32_t* budgets_out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,6 +28,7 @@ from ._lib import (  # noqa: F401
     kv_set_filled,
     kv_slot_of,
     kv_tokens,
+    pyramid_budgets,
     last_error,
     lib,
     snapkv_compress,

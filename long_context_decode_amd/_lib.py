@@ -80,6 +80,7 @@ _SIGS = {
     "lcd_kv_set_filled": (_S, [_P, _I32, _I32, _I64, _P]),
     "lcd_snapkv_sizes": (_S, [ctypes.POINTER(SnapkvParams), ctypes.POINTER(_U64)]),
     "lcd_snapkv_compress": (_S, [ctypes.POINTER(SnapkvParams), _P, _P, _P, _P, _P, _P, _P, _P, _U64, _P]),
+    "lcd_pyramid_budgets": (_S, [_I32, _I32, _I32, ctypes.POINTER(_I32)]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(lib, _name)
@@ -196,6 +197,13 @@ def snapkv_sizes(p: SnapkvParams) -> int:
 def snapkv_compress(p: SnapkvParams, q_obs, k, v, k_out, v_out, idx_out, scores_out, ws, ws_bytes, stream=None):
     _check(lib.lcd_snapkv_compress(ctypes.byref(p), _ptr(q_obs), _ptr(k), _ptr(v), _ptr(k_out), _ptr(v_out),
                                    _ptr(idx_out), _ptr(scores_out), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def pyramid_budgets(n_layers, b_base, b_target):
+    """Per-layer PyramidKV budgets (layer 0 lowest), computed by the library."""
+    out = (_I32 * max(n_layers, 1))()
+    _check(lib.lcd_pyramid_budgets(n_layers, b_base, b_target, out))
+    return list(out[:n_layers])
 
 
 class KVCache:

@@ -579,3 +579,32 @@ extern "C" lcd_status lcd_snapkv_compress(const lcd_snapkv_params* p, const void
   if (e != hipSuccess) return hip_fail(e, "snapkv launch");
   return ok();
 }
+
+// ------------------------------------------------------------------ PyramidKV budgets
+extern "C" lcd_status lcd_pyramid_budgets(int32_t n_layers, int32_t b_base, int32_t b_target, int32_t* out) {
+  if (!out) return fail(LCD_EINVAL, "budgets_out is NULL");
+  if (n_layers < 1 || n_layers > 4096) return fail(LCD_EINVAL, "n_layers %d outside 1..4096", n_layers);
+  const int32_t kMaxBudget = int32_t(1) << 24;
+  if (b_base < 0 || b_base > kMaxBudget || b_target < 0 || b_target > kMaxBudget)
+    return fail(LCD_EINVAL, "budgets must lie in 0..2^24");
+  std::vector<int64_t> b(n_layers);
+  if (n_layers == 1) {
+    b[0] = b_target;
+  } else {
+    // B_l = b_base + floor(2 * (b_target - b_base) * (n_layers - 1 - l) / (n_layers - 1))
+    const int64_t den = n_layers - 1;
+    int64_t sum = 0;
+    for (int32_t l = 0; l < n_layers; ++l) {
+      const int64_t num = 2 * (int64_t)(b_target - b_base) * (n_layers - 1 - l);
+      const int64_t q = num >= 0 ? num / den : -((-num + den - 1) / den);  // floor division
+      b[l] = b_base + q;
+      sum += b[l];
+    }
+    const int64_t lost = (int64_t)n_layers * b_target - sum;  // 0 <= lost < n_layers
+    for (int64_t l = 0; l < lost; ++l) b[l] += 1;
+  }
+  for (int32_t l = 0; l < n_layers; ++l)
+    if (b[l] < 0) return fail(LCD_EINVAL, "layer %d budget would be negative (b_base > 2 * b_target)", l);
+  for (int32_t l = 0; l < n_layers; ++l) out[l] = (int32_t)b[l];
+  return ok();
+}

@@ -120,3 +120,21 @@ def test_destroy_null_is_ignored(L):
     L.lib.lcd_kv_cache_destroy(None)
     assert isinstance(L.last_error(), str)
     assert ctypes.sizeof(L._lib.CacheConfig) == 12 * 4 + 2 * 8
+
+
+# ---------------------------------------------------------------- PyramidKV budgets (host-only)
+@pytest.mark.parametrize("n_layers,b_base,b_target", [
+    (1, 10, 77), (2, 0, 3), (4, 64, 128), (32, 128, 2048), (32, 0, 1000), (7, 100, 100), (80, 512, 5275),
+    (3, 9, 7), (4096, 1 << 24, 1 << 24), (4096, 0, 1 << 24), (97, 5, 1 << 20),
+])
+def test_pyramid_budgets_match_oracle(L, n_layers, b_base, b_target):
+    assert L.pyramid_budgets(n_layers, b_base, b_target) == oracle.pyramid_budgets(n_layers, b_base, b_target)
+
+
+@pytest.mark.parametrize("args", [(0, 1, 1), (4097, 1, 1), (3, -1, 4), (3, 4, -1), (3, 300, 100),
+                                  (2, (1 << 24) + 1, 5)])
+def test_pyramid_budgets_rejects(L, args):
+    with pytest.raises(L.LcdError):
+        L.pyramid_budgets(*args)
+    import ctypes
+    assert L.lib.lcd_pyramid_budgets(3, 1, 2, None) == 1  # LCD_EINVAL for a null output

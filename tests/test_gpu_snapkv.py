@@ -159,3 +159,19 @@ def test_decode_over_compressed_cache(L):
             err = np.abs(got[h] - ref).max()
             assert err <= 2e-3, f"step {s} head {h}: {err:.2e}"
     assert L.kv_filled(cache.handle, 0) == K + Lo + steps
+
+
+def test_pyramid_budgets_feed_snapkv(L):
+    """PyramidKV: budgets from the library ([KVC] "Alocação piramidal com o PyramidKV"),
+    then one SnapKV compress per layer keeping k_l = B_l - L_obs prefix rows plus the
+    window; every layer checked against the oracle, the kept rows summing to the target."""
+    n_layers, lo, b_base, b_target = 4, 16, 48, 96
+    budgets = L.pyramid_budgets(n_layers, b_base, b_target)
+    assert budgets == oracle.pyramid_budgets(n_layers, b_base, b_target)
+    kept = 0
+    for layer, b_l in enumerate(budgets):
+        w = scaled(BASE, name=f"pyramid_layer{layer}", n_q_heads=2, n_prompt=600, l_obs=lo, k_keep=b_l - lo)
+        print(f"[pyramid] layer {layer} budget {b_l}", flush=True)
+        _run(L, w)
+        kept += b_l
+    assert kept == n_layers * b_target
