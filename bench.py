@@ -12,7 +12,8 @@ HBM bandwidth against the 8 TB/s peak (HIP events on the launch stream around ba
 of back-to-back decode_attn launches), the decode kernel's counter-measured HBM traffic
 when the record under profiles/ matches the current kernel sources, the SnapKV
 compression time, secondary decode workloads
-(the 16-layer GQA 32k cache, the H2O 4096 budget, the tiny fp32 stream) unless
+(the 16-layer GQA 32k cache, the H2O 4096 budget, the DuoAttention 128k mixed-head
+layer, the tiny fp32 stream) unless
 --only, and the fp64 CPU oracle timed on a bounded sample of the headline step.
 """
 from __future__ import annotations
@@ -29,7 +30,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK = 8.0e12  # B/s, MI355X HBM3E
 MFMA_BF16_PEAK = 2.5e15  # flop/s, dense
 METRIC = "decode steps/s + achieved HBM TB/s (% of peak); SnapKV compress ms"
-DEFAULTS = {"llama2_7b_layer": (8192, 64), "gqa_long": (64, 4), "h2o_128k": (1024, 32), "tiny_streaming": (448, 64)}
+DEFAULTS = {"llama2_7b_layer": (8192, 64), "gqa_long": (64, 4), "h2o_128k": (1024, 32), "duo_128k": (192, 16),
+            "tiny_streaming": (448, 64)}
 
 
 def _parse(argv=None):
@@ -115,12 +117,12 @@ def _counter_summary(fetch_csv, write_csv, out=TRAFFIC_RECORD):
         "Two rocprofv3 counter runs of the same command, one counter each:",
         "",
         "```",
-        "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/p21/fetch -o run -- "
+        "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/p26/fetch -o run -- "
         "python3 bench.py --only --copy-calibration --steps 64 --warmup 8 --no-cpu-baseline",
-        "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/p21/write -o run -- "
+        "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/p26/write -o run -- "
         "python3 bench.py --only --copy-calibration --steps 64 --warmup 8 --no-cpu-baseline",
-        "python3 bench.py --counters gpurun_out/p21/fetch/run_counter_collection.csv "
-        "gpurun_out/p21/write/run_counter_collection.csv",
+        "python3 bench.py --counters gpurun_out/p26/fetch/run_counter_collection.csv "
+        "gpurun_out/p26/write/run_counter_collection.csv",
         "```",
         "",
         "The calibration copy moves 1 GiB in each direction; each counter is scaled by "
@@ -188,6 +190,20 @@ class _Stepper:
                     del k, v
             self.t0 = w.prefill
             self.slots = w.n_sink + w.window
+        elif w.kind == "duo":
+            cfg = L.cache_config(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, dt, L.LCD_DUO,
+                                 n_layers=w.n_layers, n_sink=w.n_sink, window=w.window, capacity=w.capacity,
+                                 retrieval=w.retrieval)
+            self.cache = L.KVCache(cfg, device=dev)
+            for layer in range(w.n_layers):
+                for a in range(0, w.prefill, 8192):
+                    e = min(w.prefill, a + 8192)
+                    k = w.token_block_torch("k", layer, a, e, dev)
+                    v = w.token_block_torch("v", layer, a, e, dev)
+                    self.cache.append(layer, k, v)
+                    del k, v
+            self.t0 = w.prefill
+            self.slots = w.prefill  # grows by one per step; launch_bytes counts the state at the end
         else:  # h2o
             from synth.workloads import h2o_state_torch
 
@@ -222,8 +238,16 @@ class _Stepper:
     def launch_bytes(self):
         """Algorithmic bytes of one decode_attn launch (one layer)."""
         w = self.w
-        kv = 2 * w.batch * w.n_kv_heads * self.slots * w.head_dim * w.esize
         io = w.batch * w.n_q_heads * w.head_dim * (w.esize + 4)  # q in, fp32 out
+        if w.kind == "duo":
+            n = self.t0 + self.i  # tokens held now (retrieval heads attend all of them)
+            per_layer = []
+            for gam in w.retrieval:
+                r = sum(gam)
+                slots = r * n + (w.n_kv_heads - r) * min(n, w.n_sink + w.window)
+                per_layer.append(2 * w.batch * slots * w.head_dim * w.esize + io)
+            return sum(per_layer) // len(per_layer)
+        kv = 2 * w.batch * w.n_kv_heads * self.slots * w.head_dim * w.esize
         if w.kind == "h2o":
             logits = 2 * w.batch * w.n_q_heads * self.slots * 4  # written then read
             state = w.batch * w.n_kv_heads * self.slots * (4 + 4 + 4)  # score read+write, pos read
@@ -429,7 +453,7 @@ def main(argv=None):
         line["snapkv"] = _snapkv_bench(L, WORKLOADS["snapkv_32k"])
     if not a.only:
         others = []
-        for name in ("gqa_long", "h2o_128k", "tiny_streaming"):
+        for name in ("gqa_long", "h2o_128k", "duo_128k", "tiny_streaming"):
             if name == a.workload:
                 continue
             s2, w2 = DEFAULTS[name]

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define LCD_ABI_VERSION 1
+#define LCD_ABI_VERSION 2
 
 typedef enum lcd_status {
   LCD_OK = 0,
@@ -74,8 +74,15 @@ typedef enum lcd_dtype { LCD_F32 = 0, LCD_BF16 = 1 } lcd_dtype;
  *                among tokens older than the n_recent newest (ties evict the newer
  *                token).  decode_attn adds the step's attention weights (summed
  *                over the query heads sharing the KV head) to the scores and picks
- *                the next victim. */
-typedef enum lcd_policy { LCD_SINK_RING = 0, LCD_APPEND = 1, LCD_H2O = 2 } lcd_policy;
+ *                the next victim.
+ * LCD_DUO        [KVC] "Decomposição funcional com o DuoAttention".  Each KV head of
+ *                each layer is a retrieval head (full history: APPEND rows in order
+ *                up to `capacity`, never evicted) or a streaming head (the 4 sinks +
+ *                64 recent tokens of the page, in general n_sink sinks + a ring of
+ *                `window` slots exactly as LCD_SINK_RING), as `retrieval` says.
+ *                Both kinds are served by one decode launch.  Keys are used as given
+ *                (rope = 0). */
+typedef enum lcd_policy { LCD_SINK_RING = 0, LCD_APPEND = 1, LCD_H2O = 2, LCD_DUO = 3 } lcd_policy;
 
 typedef struct lcd_cache_config {
   int32_t batch;       /* B >= 1 (all rows advance in lockstep)                   */
@@ -85,9 +92,11 @@ typedef struct lcd_cache_config {
   int32_t head_dim;    /* D in {64, 128, 256}                                      */
   int32_t dtype;       /* lcd_dtype of K, V and q                                  */
   int32_t policy;      /* lcd_policy                                               */
-  int32_t n_sink;      /* SINK_RING: sink slots S >= 0                             */
-  int32_t window;      /* SINK_RING: ring slots W >= 1; capacity C = S + W          */
-  int32_t capacity;    /* APPEND, H2O: slots C >= 1 per (layer, batch row, KV head) */
+  int32_t n_sink;      /* SINK_RING, DUO streaming heads: sink slots S >= 0         */
+  int32_t window;      /* SINK_RING, DUO streaming heads: ring slots W >= 1;
+                          SINK_RING capacity C = S + W                              */
+  int32_t capacity;    /* APPEND, H2O: slots C >= 1 per (layer, batch row, KV head);
+                          DUO: slots of a retrieval head                            */
   int32_t n_recent;    /* H2O: protected newest tokens, 1 <= n_recent <= capacity;
                           includes the token being decoded                          */
   int32_t rope;        /* SINK_RING only: 1 = keys are stored un-rotated and q and
@@ -98,6 +107,10 @@ typedef struct lcd_cache_config {
                           pair i by position * rope_base^(-2i/D).                  */
   double rope_base;    /* > 1 when rope = 1                                        */
   double scale;        /* logit scale; 0 selects 1/sqrt(head_dim)                  */
+  const int32_t* retrieval; /* DUO: host int32 [n_layers][n_kv_heads], 1 = retrieval
+                          head, 0 = streaming head (n_kv_heads <= 128); read during
+                          lcd_cache_sizes / lcd_kv_cache_init only (the handle keeps
+                          a copy).  Ignored by the other policies (may be NULL).    */
 } lcd_cache_config;
 
 typedef struct lcd_cache lcd_cache; /* opaque host handle */
@@ -116,6 +129,10 @@ const char* lcd_last_error(void);
  *              contextos longos" and [KVL] "01 · Conceito" with C retained slots.
  *              Layout: for layer l, K at l*2*P and V at (l*2+1)*P bytes, each
  *              [batch][n_kv_heads][C][head_dim], P = kv_bytes / (2 * n_layers).
+ *              DUO: per layer l with R_l retrieval and T_l streaming heads, K then
+ *              V, each [batch][R_l][capacity][head_dim] (retrieval heads in head
+ *              order) followed by [batch][T_l][n_sink + window][head_dim]
+ *              (streaming heads in head order); layers follow each other.
  *   aux_bytes  Per-cache state: int32 arrival counters of the split merge (one
  *              per layer, batch row and KV head), the float32 cos/sin table of
  *              the in-cache positions (SINK_RING with rope), per-slot token
@@ -148,9 +165,12 @@ void lcd_kv_cache_destroy(lcd_cache* cache);
  *   n_new  >= 1.  SINK_RING writes only the tokens that survive (the sinks among
  *          them and the newest `window`), exactly as n_new single appends would.
  *          APPEND requires tokens + n_new <= capacity (else LCD_ECAPACITY).  H2O
- *          requires n_new == 1 (bulk state goes through lcd_kv_load); when the
- *          cache is full the row overwrites the victim slot chosen on the device
- *          by the previous lcd_decode_attn of this layer.
+ *          requires n_new == 1 (bulk state goes through lcd_kv_layer_view and
+ *          lcd_kv_set_filled); when the cache is full the row overwrites the
+ *          victim slot chosen on the device by the previous lcd_decode_attn of
+ *          this layer.  DUO writes every row of a retrieval head in order
+ *          (tokens + n_new <= capacity, else LCD_ECAPACITY) and, for a streaming
+ *          head, the rows that survive as SINK_RING does; one launch for both.
  * Advances the layer's token counter by n_new. */
 lcd_status lcd_kv_append(lcd_cache* cache, int32_t layer, const void* k, const void* v, int32_t n_new,
                          void* stream);
@@ -166,16 +186,19 @@ lcd_status lcd_kv_append(lcd_cache* cache, int32_t layer, const void* k, const v
  * Attends all retained tokens of the layer, including the newest.  SINK_RING with
  * rope rotates q and every key at its in-cache position.  H2O also adds the step's
  * attention weights to the slot scores and selects the next victim; call it once
- * after each append.  LCD_EINVAL if the layer holds no token. */
+ * after each append.  DUO: retrieval heads attend every appended token, streaming
+ * heads their sinks and window, in the same launch.  LCD_EINVAL if the layer
+ * holds no token. */
 lcd_status lcd_decode_attn(lcd_cache* cache, int32_t layer, const void* q, float* out, void* ws,
                            uint64_t ws_bytes, void* stream);
 
 /* Host-side queries (pure host functions, no HIP call; -1 on invalid arguments).
  *   lcd_kv_tokens   tokens appended so far to `layer` (int64 counter).
- *   lcd_kv_filled   slots currently holding a token (<= capacity).
+ *   lcd_kv_filled   slots currently holding a token (<= capacity; DUO: of a
+ *                   retrieval head).
  *   lcd_kv_slot_of  SINK_RING: slot that holds / held token `token`; APPEND:
- *                   the row index of the token-th appended row; H2O: -1 (the slot
- *                   is chosen on the device).
+ *                   the row index of the token-th appended row; H2O, DUO: -1 (the
+ *                   slot depends on the head).
  *   lcd_kv_rank_of  SINK_RING: in-cache position of the token in `slot` right now
  *                   (-1 if the slot is empty); others: -1. */
 int64_t lcd_kv_tokens(const lcd_cache* cache, int32_t layer);
@@ -186,14 +209,15 @@ int64_t lcd_kv_rank_of(const lcd_cache* cache, int32_t layer, int64_t slot);
 /* Device addresses of one layer's state, for callers that fill a cache in place
  * (e.g. SnapKV output written straight into an APPEND cache).  k/v point at
  * [batch][n_kv_heads][C][head_dim]; pos (int32) and score (float32) at
- * [batch][n_kv_heads][C] (H2O only, else NULL).  Any output may be NULL. */
+ * [batch][n_kv_heads][C] (H2O only, else NULL).  Any output may be NULL.
+ * DUO: LCD_EUNSUPPORTED (heads of a layer have two layouts; see lcd_cache_sizes). */
 lcd_status lcd_kv_layer_view(const lcd_cache* cache, int32_t layer, void** k, void** v, int32_t** pos,
                              float** score);
 
 /* Seed a layer whose first n rows (per batch row and KV head) were already
  * written in place through lcd_kv_layer_view: sets the fill count to n and the
  * token counter to next_token (the position of the next appended token).  APPEND
- * and H2O only (n <= capacity).  For H2O the caller has also written pos (distinct
+ * and H2O only (n <= capacity; others LCD_EUNSUPPORTED).  For H2O the caller has also written pos (distinct
  * token positions < next_token) and score of those rows; when n == capacity the
  * victim of the next append is chosen on `stream` from those scores (lowest score
  * among positions <= next_token - n_recent, ties evicting the higher position).

@@ -11,6 +11,7 @@ from ._lib import (  # noqa: F401
     LCD_BF16,
     LCD_F32,
     LCD_H2O,
+    LCD_DUO,
     LCD_SINK_RING,
     LIB_PATH,
     KVCache,

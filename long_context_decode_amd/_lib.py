@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("LCD_LIB_PATH") or os.path.join(PKG, "liblcd.so")
 
 LCD_F32, LCD_BF16 = 0, 1
-LCD_SINK_RING, LCD_APPEND, LCD_H2O = 0, 1, 2
+LCD_SINK_RING, LCD_APPEND, LCD_H2O, LCD_DUO = 0, 1, 2, 3
 
 _STATUS = {0: "LCD_OK", 1: "LCD_EINVAL", 2: "LCD_ESHAPE", 3: "LCD_EALIGN", 4: "LCD_ECAPACITY",
            5: "LCD_ESIZE", 6: "LCD_EHIP", 7: "LCD_EUNSUPPORTED"}
@@ -31,7 +31,8 @@ class CacheConfig(ctypes.Structure):
                 ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("policy", ctypes.c_int32), ("n_sink", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("capacity", ctypes.c_int32), ("n_recent", ctypes.c_int32), ("rope", ctypes.c_int32),
-                ("rope_base", ctypes.c_double), ("scale", ctypes.c_double)]
+                ("rope_base", ctypes.c_double), ("scale", ctypes.c_double),
+                ("retrieval", ctypes.POINTER(ctypes.c_int32))]
 
 
 class SnapkvParams(ctypes.Structure):
@@ -125,9 +126,17 @@ def _stream(stream):
 
 
 def cache_config(batch, n_q_heads, n_kv_heads, head_dim, dtype=LCD_BF16, policy=LCD_SINK_RING, n_layers=1,
-                 n_sink=0, window=0, capacity=0, n_recent=0, rope=0, rope_base=10000.0, scale=0.0):
-    return CacheConfig(batch, n_layers, n_q_heads, n_kv_heads, head_dim, dtype, policy, n_sink, window,
-                       capacity, n_recent, rope, rope_base, scale)
+                 n_sink=0, window=0, capacity=0, n_recent=0, rope=0, rope_base=10000.0, scale=0.0,
+                 retrieval=None):
+    """``retrieval``: DUO head kinds, [n_layers][n_kv_heads] of 0/1 (any nested sequence)."""
+    cfg = CacheConfig(batch, n_layers, n_q_heads, n_kv_heads, head_dim, dtype, policy, n_sink, window,
+                      capacity, n_recent, rope, rope_base, scale, None)
+    if retrieval is not None:
+        flat = [int(x) for row in retrieval for x in row]
+        arr = (ctypes.c_int32 * len(flat))(*flat)
+        cfg._retrieval_keepalive = arr  # the library reads it during sizes / init only
+        cfg.retrieval = ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32))
+    return cfg
 
 
 def cache_sizes(cfg: CacheConfig):
@@ -230,18 +239,21 @@ class KVCache:
         decode_attn(self.handle, layer, q, out, self.ws, self.ws_bytes, stream)
 
     def layer_tensors(self, layer):
-        """(K, V) views of one layer as [B][H_kv][C][D] torch tensors."""
+        """(K, V) views of one layer as [B][H_kv][C][D] torch tensors, at the addresses
+        lcd_kv_layer_view reports (LcdError for a mixed-head layer)."""
         import torch
 
         c = self.cfg
+        k, v, _, _ = kv_layer_view(self.handle, layer)
         C = c.n_sink + c.window if c.policy == LCD_SINK_RING else c.capacity
         dt = torch.float32 if c.dtype == LCD_F32 else torch.bfloat16
         es = 4 if c.dtype == LCD_F32 else 2
         per = c.batch * c.n_kv_heads * C * c.head_dim
-        base = layer * 2 * per * es
-        kv = self.kv_mem[base: base + 2 * per * es].view(dt)
-        return kv[:per].view(c.batch, c.n_kv_heads, C, c.head_dim), kv[per:].view(c.batch, c.n_kv_heads, C,
-                                                                                   c.head_dim)
+        base = self.kv_mem.data_ptr()
+        ko, vo = k - base, v - base
+        K = self.kv_mem[ko: ko + per * es].view(dt).view(c.batch, c.n_kv_heads, C, c.head_dim)
+        V = self.kv_mem[vo: vo + per * es].view(dt).view(c.batch, c.n_kv_heads, C, c.head_dim)
+        return K, V
 
     def h2o_tensors(self, layer):
         """(positions int32, scores float32) views of one H2O layer as [B][H_kv][C]."""

@@ -44,6 +44,12 @@ struct bf16_t {
 #ifndef LCD_U_G2
 #define LCD_U_G2 2
 #endif
+#ifndef LCD_ONEPASS_MAXG
+#define LCD_ONEPASS_MAXG 2  // largest G served by the one-pass kernel
+#endif
+#ifndef LCD_U_OP_BIG
+#define LCD_U_OP_BIG 1  // one-pass keys per lane group per iteration for G > 2
+#endif
 #ifndef LCD_U2_G4
 #define LCD_U2_G4 4
 #endif
@@ -207,9 +213,8 @@ struct Geo {
   static constexpr int LPK = D / EPL;         // lanes per key
   static constexpr int KPW = 64 / LPK;        // keys per wave per sub-step
   static constexpr int KPI = 4 * KPW;         // keys per workgroup per sub-step
-  static constexpr int U = LCD_U_G2;
+  static constexpr int U = G <= 2 ? LCD_U_G2 : LCD_U_OP_BIG;
   static constexpr int STEP = KPI * U;        // keys per workgroup per iteration
-  static_assert(G <= 2, "the one-pass kernel serves up to 2 query heads per KV head");
   static_assert(LPK >= 1 && LPK <= 64 && (64 % LPK) == 0, "lane mapping");
 };
 
@@ -229,6 +234,56 @@ inline size_t twopass_lds_floats(int chunk) {
   return (a > o ? a : o) + 6 * G;
 }
 
+// The work item of linear index `item` (split, KV head g, batch row b), split slowest;
+// split = -1 past the end.  Mixed heads: retrieval items first, then streaming ones.
+struct WorkItem {
+  int split, g, b;
+};
+
+__device__ inline WorkItem work_item(const DecodeParams& p, int item) {
+  if (p.duo) {
+    const int nr = p.B * p.Hret, ns = p.B * p.Hstr;
+    const int items_ret = p.ret_splits * nr;
+    if (item < items_ret) {
+      const int r = item % nr;
+      return {item / nr, p.duo_ret[r % p.Hret], r / p.Hret};
+    }
+    item -= items_ret;
+    if (item >= p.str_splits * ns) return {-1, 0, 0};
+    const int r = item % ns;
+    return {item / ns, p.duo_str[r % p.Hstr], r / p.Hstr};
+  }
+  const int n_bg = p.B * p.Hkv;
+  if (item >= p.n_splits * n_bg) return {-1, 0, 0};
+  const int r = item % n_bg;
+  return {item / n_bg, r % p.Hkv, r / p.Hkv};
+}
+
+// The cache rows one workgroup's (b, g) reads: K / V bases and attended slot count.
+// Uniform caches: [B][Hkv][C][D] and n.  Mixed retrieval / streaming heads: the
+// retrieval or streaming region of the head, each with its own count.
+struct HeadView {
+  const char* k;
+  const char* v;
+  int n;
+};
+
+template <typename T, int D>
+__device__ inline HeadView head_view(const DecodeParams& p, int b, int g) {
+  constexpr size_t row = (size_t)D * sizeof(T);
+  if (p.duo) {
+    const int m = p.duo_map[g];
+    if (m >= 0) {
+      const size_t off = ((size_t)b * p.Hret + m) * p.C * row;
+      return {reinterpret_cast<const char*>(p.k) + off, reinterpret_cast<const char*>(p.v) + off, p.n};
+    }
+    const size_t off = ((size_t)b * p.Hstr + (-1 - m)) * p.C2 * row;
+    return {reinterpret_cast<const char*>(p.k2) + off, reinterpret_cast<const char*>(p.v2) + off, p.n2};
+  }
+  const size_t off = ((size_t)b * p.Hkv + g) * p.C * row;
+  return {reinterpret_cast<const char*>(p.k) + off, reinterpret_cast<const char*>(p.v) + off, p.n};
+}
+
 // ---------------------------------------------------------------- split finish
 // The end of a decode workgroup: ored[0 .. G*D) (LDS) holds its range's unnormalised
 // output and Mh / Lh (LDS) its maximum and sum per query head.  With one split the
@@ -237,13 +292,13 @@ inline size_t twopass_lds_floats(int chunk) {
 // logits mode the merging workgroup then runs the H2O epilogue.
 template <int D, int G, bool LOGITS>
 __device__ inline void split_finish(const DecodeParams& p, const float* ored, const float* Mh, const float* Lh,
-                                    int split, int b, int g) {
+                                    int split, int n_splits, int b, int g) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const size_t bg = (size_t)b * p.Hkv + g;
   const size_t bh0 = (size_t)b * p.Hq + g * G;
   __shared__ float Mtot[G], Linv[G];
   __shared__ int is_last;
-  if (p.n_splits == 1) {
+  if (n_splits == 1) {
     if (threadIdx.x < G) {
       Mtot[threadIdx.x] = Mh[threadIdx.x];
       Linv[threadIdx.x] = 1.f / Lh[threadIdx.x];
@@ -265,16 +320,16 @@ __device__ inline void split_finish(const DecodeParams& p, const float* ored, co
     __syncthreads();
     if (threadIdx.x == 0)
       is_last = __hip_atomic_fetch_add(&p.arrivals[bg], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                p.n_splits - 1;
+                n_splits - 1;
     __syncthreads();
     if (!is_last) return;
     // last arrival: merge every split in split order (deterministic)
     if (threadIdx.x < G) {
       const int j = threadIdx.x;
       float mt = -INFINITY;
-      for (int s = 0; s < p.n_splits; ++s) mt = fmaxf(mt, load_dev(&p.part_ml[((size_t)s * BH + bh0 + j) * 2]));
+      for (int s = 0; s < n_splits; ++s) mt = fmaxf(mt, load_dev(&p.part_ml[((size_t)s * BH + bh0 + j) * 2]));
       float lt = 0.f;
-      for (int s = 0; s < p.n_splits; ++s) {
+      for (int s = 0; s < n_splits; ++s) {
         const float* ml = p.part_ml + ((size_t)s * BH + bh0 + j) * 2;
         lt += load_dev(&ml[1]) * exp2f(load_dev(&ml[0]) - mt);
       }
@@ -285,7 +340,7 @@ __device__ inline void split_finish(const DecodeParams& p, const float* ored, co
     for (int idx = threadIdx.x; idx < G * D; idx += kDecodeThreads) {
       const int j = idx / D, dd = idx % D;
       float acc = 0.f;
-      for (int s = 0; s < p.n_splits; ++s)
+      for (int s = 0; s < n_splits; ++s)
         acc += load_dev(&p.part_o[((size_t)s * BH + bh0 + j) * D + dd]) *
                exp2f(load_dev(&p.part_ml[((size_t)s * BH + bh0 + j) * 2]) - Mtot[j]);
       p.out[(bh0 + j) * D + dd] = acc * Linv[j];
@@ -377,20 +432,19 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_onepass_kernel(DecodePa
   // slowest: the workgroups resident on one XCD then share a slot range and its
   // slice of the position table stays in that XCD's L2.
   const int per_xcd = (int)((gridDim.x + 7) / 8);
-  const int item = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
-  const int n_bg = p.B * p.Hkv;
-  if (item >= p.n_splits * n_bg) return;  // padding of the grid to a multiple of 8
-  const int split = item / n_bg;
-  const int g = (item % n_bg) % p.Hkv, b = (item % n_bg) / p.Hkv;
+  const WorkItem wi = work_item(p, (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8));
+  if (wi.split < 0) return;  // padding of the grid to a multiple of 8
+  const int split = wi.split, g = wi.g, b = wi.b;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane % LPK, kg = lane / LPK;
   const int i0 = sub * HALF;  // first pair index owned by this lane
+  const HeadView hv = head_view<T, D>(p, b, g);
   const int s_begin = split * p.chunk;
-  const int cnt = min(p.n - s_begin, p.chunk);
-
-  const size_t bg = (size_t)b * p.Hkv + g;
-  const char* kbase = reinterpret_cast<const char*>(p.k) + bg * p.C * D * sizeof(T);
-  const char* vbase = reinterpret_cast<const char*>(p.v) + bg * p.C * D * sizeof(T);
+  if (s_begin >= hv.n) return;  // never taken: every listed item holds at least one slot
+  const int n_splits = (hv.n + p.chunk - 1) / p.chunk;
+  const int cnt = min(hv.n - s_begin, p.chunk);
+  const char* kbase = hv.k;
+  const char* vbase = hv.v;
   const size_t lo_off = (size_t)i0 * sizeof(T);
   const size_t hi_off = (size_t)(D2 + i0) * sizeof(T);
 
@@ -681,7 +735,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_onepass_kernel(DecodePa
     ored[idx] = acc;
   }
   __syncthreads();
-  split_finish<D, G, LOGITS>(p, ored, Mh, Lh, split, b, g);
+  split_finish<D, G, LOGITS>(p, ored, Mh, Lh, split, n_splits, b, g);
 }
 
 // ---------------------------------------------------------------- two-pass kernel
@@ -714,20 +768,19 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
 
   // XCD-aware item order (see the one-pass kernel)
   const int per_xcd = (int)((gridDim.x + 7) / 8);
-  const int item = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
-  const int n_bg = p.B * p.Hkv;
-  if (item >= p.n_splits * n_bg) return;  // padding of the grid to a multiple of 8
-  const int split = item / n_bg;
-  const int g = (item % n_bg) % p.Hkv, b = (item % n_bg) / p.Hkv;
+  const WorkItem wi = work_item(p, (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8));
+  if (wi.split < 0) return;  // padding of the grid to a multiple of 8
+  const int split = wi.split, g = wi.g, b = wi.b;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane % LPK, kg = lane / LPK;
   const int i0 = sub * HALF;  // first pair index owned by this lane
+  const HeadView hv = head_view<T, D>(p, b, g);
   const int s_begin = split * p.chunk;
-  const int cnt = min(p.n - s_begin, p.chunk);
-
-  const size_t bg = (size_t)b * p.Hkv + g;
-  const char* kbase = reinterpret_cast<const char*>(p.k) + bg * p.C * D * sizeof(T);
-  const char* vbase = reinterpret_cast<const char*>(p.v) + bg * p.C * D * sizeof(T);
+  if (s_begin >= hv.n) return;  // never taken: every listed item holds at least one slot
+  const int n_splits = (hv.n + p.chunk - 1) / p.chunk;
+  const int cnt = min(hv.n - s_begin, p.chunk);
+  const char* kbase = hv.k;
+  const char* vbase = hv.v;
   const size_t lo_off = (size_t)i0 * sizeof(T);
   const size_t hi_off = (size_t)(D2 + i0) * sizeof(T);
 
@@ -986,7 +1039,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
   for (int idx = threadIdx.x; idx < G * D; idx += kDecodeThreads)  // each thread reads only its idx
     ored[idx] = ored[idx] + ored[G * D + idx] + ored[2 * G * D + idx] + ored[3 * G * D + idx];
   __syncthreads();
-  split_finish<D, G, LOGITS>(p, ored, Mh, Lh, split, b, g);
+  split_finish<D, G, LOGITS>(p, ored, Mh, Lh, split, n_splits, b, g);
 }
 
 // Victim choice for a seeded H2O layer (no decode step has run yet): the lowest score
@@ -1029,9 +1082,10 @@ hipError_t launch_h2o_pick_victim(const float* score, const int* pos, int* victi
 // ---------------------------------------------------------------------------- dispatch
 template <typename T, int D, int G>
 static hipError_t launch_tdg(int mode, const DecodeParams& p, hipStream_t s) {
-  const int items = p.n_splits * p.B * p.Hkv;
+  const int items = p.duo ? p.ret_splits * p.B * p.Hret + p.str_splits * p.B * p.Hstr
+                         : p.n_splits * p.B * p.Hkv;
   const dim3 grid(((items + 7) / 8) * 8), block(kDecodeThreads);
-  if constexpr (G <= 2) {
+  if constexpr (G <= LCD_ONEPASS_MAXG) {
     const size_t lds = onepass_lds_bytes<D, G>();
     switch (mode) {
       case kModeRope: hipLaunchKernelGGL((decode_onepass_kernel<T, D, G, kModeRope>), grid, block, lds, s, p); break;
@@ -1078,7 +1132,7 @@ static hipError_t launch_t(int D, int G, int mode, const DecodeParams& p, hipStr
 }
 
 int decode_chunk_cap(int G) {
-  if (G <= 2) return 1 << 24;  // the one-pass kernel keeps no per-slot state in LDS
+  if (G <= LCD_ONEPASS_MAXG) return 1 << 24;  // the one-pass kernel keeps no per-slot state in LDS
   // two-pass: chunk * G logits + 6 * G floats within 64 KiB, 256 bytes kept for the
   // static shared variables
   return (16384 - 64 - 6 * G) / G / 64 * 64;

@@ -52,6 +52,43 @@ __global__ void append_h2o_kernel(AppendParams p) {
   }
 }
 
+// Mixed retrieval / streaming heads ([KVC] "Decomposição funcional com o
+// DuoAttention"): input row r of (b, g) is token a = t0 + r.  A retrieval head keeps
+// every token in slot a; a streaming head keeps its sinks (a < S, slot a) and the
+// tokens of the final window (a >= a_first, slot S + (a - S) mod W), exactly the rows
+// a sink + window cache holds after these tokens, each written once.
+__global__ void append_duo_kernel(AppendParams p) {
+  const int chunks = p.row_bytes / 16;
+  const int64_t total = (int64_t)p.BHkv * p.n_new * chunks;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int c = (int)(i % chunks);
+    const int64_t rr = i / chunks;
+    const int r = (int)(rr % p.n_new);
+    const int bh = (int)(rr / p.n_new);
+    const int b = bh / p.Hkv, g = bh % p.Hkv;
+    const int64_t a = p.t0 + r;
+    const int m = p.duo_map[g];
+    char* kc;
+    char* vc;
+    size_t dst;
+    if (m >= 0) {
+      dst = (((size_t)b * p.Hret + m) * p.C + (size_t)a) * p.row_bytes;
+      kc = p.k_cache;
+      vc = p.v_cache;
+    } else {
+      if (a >= p.S && a < p.a_first) continue;  // evicted by a later row of this call
+      const int64_t slot = a < p.S ? a : p.S + (a - p.S) % p.W;
+      dst = (((size_t)b * p.Hstr + (-1 - m)) * p.C2 + (size_t)slot) * p.row_bytes;
+      kc = p.k2_cache;
+      vc = p.v2_cache;
+    }
+    const size_t src = ((size_t)bh * p.n_new + r) * p.row_bytes + (size_t)c * 16;
+    *reinterpret_cast<uint4*>(kc + dst + (size_t)c * 16) = *reinterpret_cast<const uint4*>(p.k_in + src);
+    *reinterpret_cast<uint4*>(vc + dst + (size_t)c * 16) = *reinterpret_cast<const uint4*>(p.v_in + src);
+  }
+}
+
 // cos/sin of (position * base^(-2i/D)) for every in-cache position and pair,
 // evaluated in float64 and rounded to float32.
 __global__ void rope_table_kernel(float* cos_t, float* sin_t, int C, int D, double base) {
@@ -87,6 +124,9 @@ static int grid_for(int64_t work, int threads) {
 hipError_t launch_append(const AppendParams& p, hipStream_t s) {
   if (p.h2o) {
     hipLaunchKernelGGL(append_h2o_kernel, dim3(p.BHkv), dim3(64), 0, s, p);
+  } else if (p.duo) {
+    const int64_t work = (int64_t)p.BHkv * p.n_new * (p.row_bytes / 16);
+    hipLaunchKernelGGL(append_duo_kernel, dim3(grid_for(work, 256)), dim3(256), 0, s, p);
   } else {
     const int64_t work = (int64_t)p.BHkv * p.n_rows * (p.row_bytes / 16);
     hipLaunchKernelGGL(append_rows_kernel, dim3(grid_for(work, 256)), dim3(256), 0, s, p);

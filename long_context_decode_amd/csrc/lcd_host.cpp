@@ -61,6 +61,13 @@ struct Layout {
   uint64_t aux_bytes = 0, off_cos = 0, off_sin = 0, off_pos = 0, off_score = 0, off_victim = 0, off_arrive = 0;
   uint64_t ws_bytes = 0, ws_off_ml = 0, ws_off_logits = 0;
   int max_splits = 0, chunk_cap = 0, chunk_force = 0, target_wgs = 0;
+  // mixed retrieval / streaming heads (DUO): streaming capacity, per-layer retrieval
+  // head count, byte offset of each layer's K block and size of its K (= V) block,
+  // and the per-layer head map (>= 0 retrieval index, < 0: -1 - streaming index)
+  int C2 = 0;
+  std::vector<int> duo_hret;
+  std::vector<uint64_t> duo_off, duo_bytes;
+  std::vector<int16_t> duo_map;
 };
 
 lcd_status check_config(const lcd_cache_config* c, Layout* L) {
@@ -88,6 +95,17 @@ lcd_status check_config(const lcd_cache_config* c, Layout* L) {
       if (c->policy == LCD_H2O && (c->n_recent < 1 || c->n_recent > c->capacity))
         return fail(LCD_ESHAPE, "H2O needs 1 <= n_recent <= capacity");
       break;
+    case LCD_DUO:
+      if (c->capacity < 1) return fail(LCD_ESHAPE, "capacity must be >= 1");
+      if (c->n_sink < 0 || c->window < 1) return fail(LCD_ESHAPE, "need n_sink >= 0 and window >= 1");
+      if (!c->retrieval) return fail(LCD_EINVAL, "DUO needs the retrieval head map");
+      if (c->n_kv_heads > lcd::kMaxDuoHeads)
+        return fail(LCD_EUNSUPPORTED, "DUO supports up to %d KV heads per layer", lcd::kMaxDuoHeads);
+      for (int64_t i = 0; i < (int64_t)c->n_layers * c->n_kv_heads; ++i)
+        if (c->retrieval[i] != 0 && c->retrieval[i] != 1) return fail(LCD_EINVAL, "retrieval flags must be 0 or 1");
+      C = c->capacity;
+      if ((int64_t)c->n_sink + c->window > kMaxSlots) return fail(LCD_ESHAPE, "n_sink + window exceeds the slot limit");
+      break;
     default:
       return fail(LCD_EINVAL, "unknown policy %d", c->policy);
   }
@@ -95,6 +113,7 @@ lcd_status check_config(const lcd_cache_config* c, Layout* L) {
   if (c->rope != 0 && c->rope != 1) return fail(LCD_EINVAL, "rope must be 0 or 1");
   if (c->rope == 1 && c->policy != LCD_SINK_RING)
     return fail(LCD_EUNSUPPORTED, "rotation at in-cache positions is defined for the sink + window cache only");
+  const bool duo = c->policy == LCD_DUO;
   if (c->rope == 1 && !(std::isfinite(c->rope_base) && c->rope_base > 1.0))
     return fail(LCD_EINVAL, "rope_base must be finite and > 1");
   if (!(std::isfinite(c->scale) && c->scale >= 0.0)) return fail(LCD_EINVAL, "scale must be finite and >= 0");
@@ -110,6 +129,31 @@ lcd_status check_config(const lcd_cache_config* c, Layout* L) {
   if (!mul_ok(&kv, 2) || !mul_ok(&kv, c->n_layers)) return fail(LCD_ESIZE, "cache size overflows 64 bits");
   L->layer_bytes = lb;
   L->kv_bytes = kv;
+  if (duo) {
+    // per layer: K = [B][R_l][C][D] then [B][T_l][S + W][D]; V the same; layers in order
+    L->C2 = c->n_sink + c->window;
+    L->duo_hret.assign(c->n_layers, 0);
+    L->duo_off.assign(c->n_layers, 0);
+    L->duo_bytes.assign(c->n_layers, 0);
+    L->duo_map.assign((size_t)c->n_layers * c->n_kv_heads, 0);
+    const uint64_t row = (uint64_t)c->head_dim * L->esize;
+    uint64_t off = 0;
+    for (int l = 0; l < c->n_layers; ++l) {
+      int r = 0, t = 0;
+      for (int g = 0; g < c->n_kv_heads; ++g) {
+        const bool ret = c->retrieval[(size_t)l * c->n_kv_heads + g] != 0;
+        L->duo_map[(size_t)l * c->n_kv_heads + g] = (int16_t)(ret ? r++ : -1 - t++);
+      }
+      L->duo_hret[l] = r;
+      // the slot counts fit 2^24 and heads 128, so (r*C + t*C2) < 2^32; times B*row below
+      uint64_t blk = (uint64_t)r * C + (uint64_t)t * L->C2;
+      if (!mul_ok(&blk, c->batch) || !mul_ok(&blk, row)) return fail(LCD_ESIZE, "cache size overflows 64 bits");
+      L->duo_off[l] = off;
+      L->duo_bytes[l] = blk;
+      if (__builtin_add_overflow(off, 2 * blk, &off)) return fail(LCD_ESIZE, "cache size overflows 64 bits");
+    }
+    L->kv_bytes = off;
+  }
 
   // arrival counters of the split merge: one per (layer, batch row, KV head)
   uint64_t aux = align256((uint64_t)c->n_layers * c->batch * c->n_kv_heads * sizeof(int32_t));
@@ -142,12 +186,13 @@ lcd_status check_config(const lcd_cache_config* c, Layout* L) {
   {
     // Bound on the split count of any plan with n <= C: plan_splits never exceeds
     // max(ceil(n / chunk_cap), 4 * target / bg) splits nor ceil(n / 64), all
-    // non-decreasing in n.
-    const int64_t bg = (int64_t)c->batch * c->n_kv_heads;
-    const int64_t by_min = (C + 63) / 64;
-    const int64_t s_cap = (C + L->chunk_cap - 1) / L->chunk_cap;
+    // non-decreasing in n.  Mixed heads plan over C or S + W with bg >= batch.
+    const int64_t Cp = duo ? std::max<int64_t>(C, L->C2) : C;
+    const int64_t bg = duo ? (int64_t)c->batch : (int64_t)c->batch * c->n_kv_heads;
+    const int64_t by_min = (Cp + 63) / 64;
+    const int64_t s_cap = (Cp + L->chunk_cap - 1) / L->chunk_cap;
     if (L->chunk_force)
-      L->max_splits = (int)((C + L->chunk_force - 1) / L->chunk_force);
+      L->max_splits = (int)((Cp + L->chunk_force - 1) / L->chunk_force);
     else
       L->max_splits = (int)std::min<int64_t>(by_min, std::max<int64_t>(s_cap, 4 * (int64_t)L->target_wgs / bg));
   }
@@ -205,8 +250,14 @@ struct lcd_cache {
   std::vector<int64_t> filled;  // slots holding a token per layer
   float qscale = 0.f;
 
-  char* k_layer(int l) const { return kv + (uint64_t)l * 2 * L.layer_bytes; }
-  char* v_layer(int l) const { return k_layer(l) + L.layer_bytes; }
+  char* k_layer(int l) const {
+    return cfg.policy == LCD_DUO ? kv + L.duo_off[l] : kv + (uint64_t)l * 2 * L.layer_bytes;
+  }
+  char* v_layer(int l) const { return k_layer(l) + (cfg.policy == LCD_DUO ? L.duo_bytes[l] : L.layer_bytes); }
+  // DUO: start of the streaming heads inside a layer's K (or V) block
+  uint64_t duo_str_off(int l) const {
+    return (uint64_t)cfg.batch * L.duo_hret[l] * L.C * cfg.head_dim * L.esize;
+  }
   float* cos_t() const { return cfg.rope ? reinterpret_cast<float*>(aux + L.off_cos) : nullptr; }
   float* sin_t() const { return cfg.rope ? reinterpret_cast<float*>(aux + L.off_sin) : nullptr; }
   uint64_t per_layer_slots() const { return (uint64_t)cfg.batch * cfg.n_kv_heads * L.C; }
@@ -263,6 +314,7 @@ lcd_status lcd_kv_cache_init(const lcd_cache_config* cfg, void* kv_mem, uint64_t
   lcd_cache* c = new (std::nothrow) lcd_cache();
   if (!c) return fail(LCD_EINVAL, "out of host memory");
   c->cfg = *cfg;
+  c->cfg.retrieval = nullptr;  // the head map lives in the layout (caller memory is read once)
   c->L = L;
   c->kv = static_cast<char*>(kv_mem);
   c->aux = static_cast<char*>(aux_mem);
@@ -358,6 +410,24 @@ lcd_status lcd_kv_append(lcd_cache* c, int32_t layer, const void* k, const void*
     const hipError_t e = lcd::launch_append(p, s);
     if (e != hipSuccess) return hip_fail(e, "kv_append launch");
     new_filled = c->filled[layer] + n_new;
+  } else if (cfg.policy == LCD_DUO) {
+    if (c->filled[layer] + n_new > C)
+      return fail(LCD_ECAPACITY, "append of %d rows to %lld filled retrieval slots of capacity %d", n_new,
+                  (long long)c->filled[layer], C);
+    const int64_t S = cfg.n_sink, W = cfg.window;
+    p.duo = 1;
+    p.Hkv = cfg.n_kv_heads;
+    p.Hret = c->L.duo_hret[layer];
+    p.Hstr = cfg.n_kv_heads - p.Hret;
+    p.C2 = c->L.C2;
+    p.t0 = t0;
+    p.a_first = std::max<int64_t>(S, t0 + n_new - W);  // oldest token of the final window
+    p.k2_cache = p.k_cache + c->duo_str_off(layer);
+    p.v2_cache = p.v_cache + c->duo_str_off(layer);
+    for (int g = 0; g < cfg.n_kv_heads; ++g) p.duo_map[g] = c->L.duo_map[(size_t)layer * cfg.n_kv_heads + g];
+    const hipError_t e = lcd::launch_append(p, s);
+    if (e != hipSuccess) return hip_fail(e, "kv_append launch");
+    new_filled = c->filled[layer] + n_new;
   } else {  // H2O
     if (n_new != 1) return fail(LCD_EINVAL, "H2O appends one token per call (got %d)", n_new);
     if (t0 > INT32_MAX) return fail(LCD_ECAPACITY, "H2O token positions are int32");
@@ -404,7 +474,32 @@ lcd_status lcd_decode_attn(lcd_cache* c, int32_t layer, const void* q, float* ou
   p.Hkv = cfg.n_kv_heads;
   p.C = L.C;
   p.n = n;
-  plan_splits(L, n, cfg.batch * cfg.n_kv_heads, &p.n_splits, &p.chunk);
+  if (cfg.policy == LCD_DUO) {
+    // retrieval heads attend the n appended rows, streaming heads min(tokens, S + W);
+    // the plan follows the retrieval heads (the bulk of the bytes) unless there are none
+    p.duo = 1;
+    p.Hret = L.duo_hret[layer];
+    p.Hstr = cfg.n_kv_heads - p.Hret;
+    p.C2 = L.C2;
+    p.n2 = (int)std::min<int64_t>(c->tokens[layer], L.C2);
+    p.k2 = c->k_layer(layer) + c->duo_str_off(layer);
+    p.v2 = c->v_layer(layer) + c->duo_str_off(layer);
+    for (int g = 0; g < cfg.n_kv_heads; ++g) {
+      const int m = L.duo_map[(size_t)layer * cfg.n_kv_heads + g];
+      p.duo_map[g] = (int16_t)m;
+      if (m >= 0)
+        p.duo_ret[m] = (int16_t)g;
+      else
+        p.duo_str[-1 - m] = (int16_t)g;
+    }
+    const int n_plan = p.Hret > 0 ? n : p.n2;
+    plan_splits(L, n_plan, cfg.batch * (p.Hret > 0 ? p.Hret : cfg.n_kv_heads), &p.n_splits, &p.chunk);
+    p.ret_splits = p.Hret > 0 ? (n + p.chunk - 1) / p.chunk : 0;
+    p.str_splits = p.Hstr > 0 ? (p.n2 + p.chunk - 1) / p.chunk : 0;
+    p.n_splits = std::max(p.ret_splits, p.str_splits);
+  } else {
+    plan_splits(L, n, cfg.batch * cfg.n_kv_heads, &p.n_splits, &p.chunk);
+  }
   if (p.n_splits < 1 || p.n_splits > L.max_splits || p.chunk < 64 || p.chunk > L.chunk_cap)
     return fail(LCD_ESIZE, "split plan %d x %d outside the workspace bound %d", p.n_splits, p.chunk,
                 L.max_splits);
@@ -474,6 +569,8 @@ int64_t lcd_kv_rank_of(const lcd_cache* c, int32_t layer, int64_t slot) {
 lcd_status lcd_kv_layer_view(const lcd_cache* c, int32_t layer, void** k, void** v, int32_t** pos, float** score) {
   lcd_status st = check_layer(c, layer);
   if (st) return st;
+  if (c->cfg.policy == LCD_DUO)
+    return fail(LCD_EUNSUPPORTED, "a mixed-head layer has no single [batch][heads][C][D] view");
   if (k) *k = c->k_layer(layer);
   if (v) *v = c->v_layer(layer);
   if (pos) *pos = c->pos(layer);
@@ -484,7 +581,7 @@ lcd_status lcd_kv_layer_view(const lcd_cache* c, int32_t layer, void** k, void**
 lcd_status lcd_kv_set_filled(lcd_cache* c, int32_t layer, int32_t n, int64_t next_token, void* stream) {
   lcd_status st = check_layer(c, layer);
   if (st) return st;
-  if (c->cfg.policy == LCD_SINK_RING)
+  if (c->cfg.policy == LCD_SINK_RING || c->cfg.policy == LCD_DUO)
     return fail(LCD_EUNSUPPORTED, "set_filled applies to APPEND and H2O caches");
   if (n < 0 || n > c->L.C) return fail(LCD_ECAPACITY, "n=%d outside [0, %d]", n, c->L.C);
   if (next_token < n) return fail(LCD_EINVAL, "next_token must be >= n");

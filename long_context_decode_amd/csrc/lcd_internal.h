@@ -14,6 +14,10 @@ constexpr int kResidentWorkgroups = 512;
 
 enum DecodeMode { kModeRope = 0, kModePlain = 1, kModePlainLogits = 2 };
 
+// Most KV heads per layer of a mixed retrieval / streaming (DuoAttention) cache: the
+// per-head map travels in the kernel arguments.
+constexpr int kMaxDuoHeads = 128;
+
 struct DecodeParams {
   const void* k;       // layer K [B][Hkv][C][D] (cache dtype)
   const void* v;       // layer V
@@ -37,6 +41,19 @@ struct DecodeParams {
   int n_splits;
   int full;            // ring has wrapped: ranks follow the ring order
   int S, W;            // sinks and window (rope mode)
+  // mixed heads (duo = 1): duo_map[g] >= 0 is KV head g's index among the Hret
+  // retrieval heads (k / v, [B][Hret][C][D], n attended slots); duo_map[g] < 0 is
+  // -1 - its index among the Hstr streaming heads (k2 / v2, [B][Hstr][C2][D], n2
+  // attended slots).  n_splits is the larger split count of the two kinds.
+  // The grid lists only real work: ret_splits x B x Hret retrieval items, then
+  // str_splits x B x Hstr streaming items; duo_ret / duo_str give the KV head of each
+  // retrieval / streaming index.
+  int duo, Hret, Hstr, C2, n2, ret_splits, str_splits;
+  const void* k2;
+  const void* v2;
+  int16_t duo_map[kMaxDuoHeads];
+  int16_t duo_ret[kMaxDuoHeads];
+  int16_t duo_str[kMaxDuoHeads];
   int ring_head;       // ring index of the oldest window token (rope mode, full)
   int q_rank;          // in-cache position of the query (rope mode)
   float qscale;        // logit scale * log2(e)
@@ -54,6 +71,13 @@ struct AppendParams {
   int r0, n_rows, r_split, slot_lin, ring_off, S, W;
   // H2O: one row per (b, kv head), slot = fill < C ? fill : victim[bh]
   int h2o, fill;
+  // mixed heads (duo = 1): rows of input token a = t0 + r go to a retrieval head's
+  // slot a, or to a streaming head's sink / ring slot when a < S or a >= a_first
+  int duo, Hkv, Hret, Hstr, C2;
+  int64_t t0, a_first;
+  char* k2_cache;
+  char* v2_cache;
+  int16_t duo_map[kMaxDuoHeads];
   const int* victim;
   int* pos;
   float* score;

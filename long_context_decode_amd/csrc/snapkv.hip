@@ -334,6 +334,10 @@ __global__ void __launch_bounds__(256) snapkv_colscore_kernel(SnapkvParams p) {
 
 // ---------------------------------------------------------------------------- 4. select
 // Exclusive prefix sum over the 1024 threads of the block; *total receives the sum.
+// Each wave scans its lanes with DPP-free shuffles, publishes its total, and after one
+// barrier every wave adds the totals of the waves before it itself (16 broadcast LDS
+// reads, no serial pass).  warp_tot must not be reused before every thread has
+// returned: callers alternate two buffers.
 __device__ int block_exclusive_scan(int v, int* warp_tot, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int x = v;
@@ -344,19 +348,15 @@ __device__ int block_exclusive_scan(int v, int* warp_tot, int* total) {
   }
   if (lane == 63) warp_tot[wave] = x;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int acc = 0;
-    for (int w = 0; w < kSelectThreads / 64; ++w) {
-      const int t = warp_tot[w];
-      warp_tot[w] = acc;
-      acc += t;
-    }
-    *total = acc;
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kSelectThreads / 64; ++w) {
+    const int t = warp_tot[w];
+    before += w < wave ? t : 0;
+    all += t;
   }
-  __syncthreads();
-  const int r = warp_tot[wave] + x - v;
-  __syncthreads();
-  return r;
+  *total = all;
+  return before + x - v;
 }
 
 // Pooling of the prefix scores: centred window of kernel_size, zero padding; the
@@ -406,9 +406,9 @@ template <int PER, int HALO>
 __global__ void __launch_bounds__(kSelectThreads) snapkv_select_kernel(SnapkvParams p) {
   static_assert(PER % 4 == 0 && HALO % 4 == 0, "16-byte pieces");
   __shared__ int hist[kHistCopies * kBins];
-  __shared__ int warp_tot[kSelectThreads / 64];
+  __shared__ int warp_tot[2][kSelectThreads / 64];  // alternated between consecutive scans
   __shared__ uint32_t wmin[kSelectThreads / 64], wmax[kSelectThreads / 64];
-  __shared__ int total;
+  int total;
   __shared__ int s_digit, s_krem;
   const int h = blockIdx.x, b = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -507,7 +507,7 @@ __global__ void __launch_bounds__(kSelectThreads) snapkv_select_kernel(SnapkvPar
           for (int q = 0; q < kHistCopies; ++q) v += hist[q * kBins + bin];
         c[e] = v;
       }
-      const int before = block_exclusive_scan(c[0] + c[1], warp_tot, &total);
+      const int before = block_exclusive_scan(c[0] + c[1], warp_tot[0], &total);
       if (before < krem && before + c[0] + c[1] >= krem) {
         const int e = before + c[0] >= krem ? 0 : 1;
         s_digit = nb - 1 - (2 * (int)threadIdx.x + e);
@@ -531,9 +531,9 @@ __global__ void __launch_bounds__(kSelectThreads) snapkv_select_kernel(SnapkvPar
       n_eq += in && u[j] == T;
     }
   }
-  const int eq_before = block_exclusive_scan(n_eq, warp_tot, &total);
+  const int eq_before = block_exclusive_scan(n_eq, warp_tot[1], &total);
   const int take_eq = max(0, min(n_eq, take_eq_total - eq_before));
-  const int off = block_exclusive_scan(n_gt + take_eq, warp_tot, &total);
+  const int off = block_exclusive_scan(n_gt + take_eq, warp_tot[0], &total);
   int* idx = p.idx_out + bh * p.out_rows;
   if (k > 0) {
     int o = off, seen = 0;

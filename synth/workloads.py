@@ -1,8 +1,9 @@
-"""The five synthetic workloads and their seeded tensors.
+"""The six synthetic workloads and their seeded tensors.
 
 Shapes follow the decode configurations of the pages' examples (a tiny streaming
 case, a Llama-2-7B-shaped layer with a 4+2044 cache, a Qwen-like 24/4-head GQA
-model with 16 attention layers, a 32k SnapKV prompt and a 128k H2O budget).
+model with 16 attention layers, a 32k SnapKV prompt, a 128k H2O budget and a 128k
+DuoAttention mixed-head layer).
 Tensors are virtual: each is a :class:`synth.gen.NormalStream` over a fixed
 logical shape, so any slice can be produced on the CPU (numpy) or on the GPU
 (torch) with identical bits.
@@ -23,7 +24,7 @@ SEED = 0
 class Workload:
     name: str
     title: str
-    kind: str  # "streaming" | "snapkv" | "h2o"
+    kind: str  # "streaming" | "snapkv" | "h2o" | "duo"
     batch: int
     n_q_heads: int
     n_kv_heads: int
@@ -47,6 +48,9 @@ class Workload:
     # h2o
     budget: int = 0
     n_recent: int = 0
+    # duo: per layer, per KV head, 1 = retrieval head (full history), 0 = streaming
+    # head (n_sink sinks + window recent tokens)
+    retrieval: tuple = ()
     seed: int = SEED
 
     @property
@@ -59,6 +63,8 @@ class Workload:
             return self.n_sink + self.window
         if self.kind == "h2o":
             return self.budget
+        if self.kind == "duo":
+            return self.prefill + self.steps
         return self.k_keep + self.l_obs
 
     @property
@@ -295,6 +301,13 @@ WORKLOADS = {
               "avg pool 5, keep 5243 per head + the observation window; 2% of keys x3",
         kind="snapkv", batch=1, n_q_heads=32, n_kv_heads=32, head_dim=128, dtype="bf16",
         n_prompt=32768, l_obs=32, kernel_size=5, k_keep=5243, plant_frac=0.02, plant_scale=3.0),
+    "duo_128k": Workload(
+        name="duo_128k",
+        title="DuoAttention mixed-head decode: B=16, 32 q / 8 kv heads, D=128, bf16, per layer 2 retrieval "
+              "heads (full history) + 6 streaming heads (4 sinks + 64 recent), prefilled to 131072 then "
+              "256 decode steps",
+        kind="duo", batch=16, n_q_heads=32, n_kv_heads=8, head_dim=128, dtype="bf16",
+        n_sink=4, window=64, prefill=131072, steps=256, retrieval=((1, 0, 0, 0, 0, 1, 0, 0),)),
     "h2o_128k": Workload(
         name="h2o_128k",
         title="H2O budgeted decode: B=16, 32 q / 8 kv heads, D=128, bf16, 131072-token prompt held in "

@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported(L):
     for name in declared:
         assert hasattr(L.lib, name), name
     assert set(declared) == set(L._lib.EXPORTED)
-    assert L.abi_version() == 1
+    assert L.abi_version() == 2
 
 
 def test_sizes_follow_the_kv_size_model(L):
@@ -116,10 +116,55 @@ def test_snapkv_param_validation(L):
         assert e.value.name == status
 
 
+def test_duo_sizes_follow_the_mixed_layout(L):
+    """DuoAttention caches: per layer, R_l retrieval heads of `capacity` slots and T_l
+    streaming heads of n_sink + window slots, K and V each."""
+    B, Hq, Hkv, D, C, S, W = 3, 16, 8, 128, 1000, 4, 64
+    gamma = [[1, 0, 0, 0, 0, 1, 0, 0], [0] * 8, [1] * 8]
+    cfg = L.cache_config(B, Hq, Hkv, D, L.LCD_BF16, L.LCD_DUO, n_layers=3, n_sink=S, window=W, capacity=C,
+                         retrieval=gamma)
+    kv, aux, ws = L.cache_sizes(cfg)
+    want = sum(2 * B * (sum(r) * C + (Hkv - sum(r)) * (S + W)) * D * 2 for r in gamma)
+    assert kv == want
+    assert aux >= 3 * B * Hkv * 4 and ws > 0
+    # the 128k workload: 2 of 8 heads keep the whole history
+    from synth import WORKLOADS
+
+    w = WORKLOADS["duo_128k"]
+    cfg = L.cache_config(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, L.LCD_BF16, L.LCD_DUO,
+                         n_sink=w.n_sink, window=w.window, capacity=w.capacity, retrieval=w.retrieval)
+    full = oracle.kv_cache_bytes(1, w.n_kv_heads, w.head_dim, w.capacity, 2, batch=w.batch)
+    assert L.cache_sizes(cfg)[0] == 2 * w.batch * (2 * w.capacity + 6 * 68) * w.head_dim * 2 < full / 3
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(retrieval=None), "LCD_EINVAL"),
+    (dict(retrieval=[[1, 2]]), "LCD_EINVAL"),
+    (dict(capacity=0), "LCD_ESHAPE"),
+    (dict(window=0), "LCD_ESHAPE"),
+    (dict(rope=1), "LCD_EUNSUPPORTED"),
+])
+def test_duo_config_validation(L, kw, status):
+    base = dict(batch=2, n_q_heads=4, n_kv_heads=2, head_dim=128, dtype=1, policy=L.LCD_DUO, n_sink=4, window=64,
+                capacity=100, retrieval=[[1, 0]])
+    base.update(kw)
+    with pytest.raises(L.LcdError) as e:
+        L.cache_sizes(L.cache_config(**base))
+    assert e.value.name == status
+
+
+def test_duo_too_many_heads(L):
+    cfg = L.cache_config(1, 129, 129, 64, 0, L.LCD_DUO, n_sink=4, window=64, capacity=10,
+                         retrieval=[[0] * 129])
+    with pytest.raises(L.LcdError) as e:
+        L.cache_sizes(cfg)
+    assert e.value.name == "LCD_EUNSUPPORTED"
+
+
 def test_destroy_null_is_ignored(L):
     L.lib.lcd_kv_cache_destroy(None)
     assert isinstance(L.last_error(), str)
-    assert ctypes.sizeof(L._lib.CacheConfig) == 12 * 4 + 2 * 8
+    assert ctypes.sizeof(L._lib.CacheConfig) == 12 * 4 + 2 * 8 + 8  # + the DUO head-map pointer
 
 
 # ---------------------------------------------------------------- PyramidKV budgets (host-only)
