@@ -267,6 +267,49 @@ lcd_status lcd_snapkv_compress(const lcd_snapkv_params* p, const void* q_obs, co
                                void* k_out, void* v_out, int32_t* idx_out, float* scores_out, void* ws,
                                uint64_t ws_bytes, void* stream);
 
+/* H2O prompt-phase compression -------------------------------------------------
+ * [KVC] "Heavy-Hitter Oracle (H2O) e a esparsidade de cauda pesada": token j's score
+ * is the attention it receives, s_j = sum over steps t of alpha_{t,j}; when the budget
+ * is reached the cache keeps a recent partition (the n_recent newest tokens) and the
+ * heavy hitters (the highest s among the older tokens).  Applied to a whole prompt:
+ * s_j = sum over the query heads h of the KV head's group and over the prompt rows
+ * t >= j of the causal softmax weight alpha_{h,t,j} (row t attends keys 0..t, logit
+ * scale * <q_{h,t}, k_j>); the cache keeps the budget - n_recent highest s_j among
+ * j < N - n_recent (ties to the lower position, decided on float32 s) in ascending
+ * position order, then the n_recent newest tokens.  The output is the state of a full
+ * LCD_H2O layer: k_out / v_out / pos_out / score_out can be the arrays
+ * lcd_kv_layer_view returns (capacity = budget), followed by
+ * lcd_kv_set_filled(layer, min(budget, N), N). */
+typedef struct lcd_h2o_prompt_params {
+  int32_t batch;       /* >= 1                                                      */
+  int32_t n_q_heads;   /* H_q, a multiple of n_kv_heads                             */
+  int32_t n_kv_heads;  /* H_kv >= 1                                                 */
+  int32_t head_dim;    /* D in {64, 128, 256}                                       */
+  int32_t n_prompt;    /* N, 1 .. 262144                                            */
+  int32_t budget;      /* kept rows per (batch row, KV head), n_recent <= budget;
+                          a budget >= N keeps every token                          */
+  int32_t n_recent;    /* >= 1                                                      */
+  int32_t dtype;       /* LCD_BF16 (the score contractions run on bf16 MFMA)        */
+  double scale;        /* logit scale; 0 selects 1/sqrt(head_dim)                   */
+} lcd_h2o_prompt_params;
+
+/* Workspace bytes lcd_h2o_prompt_compress needs for these parameters. */
+lcd_status lcd_h2o_prompt_sizes(const lcd_h2o_prompt_params* p, uint64_t* ws_bytes);
+
+/* h2o_prompt_compress:
+ *   q           device [batch][n_q_heads][N][head_dim] prompt queries (as given)
+ *   k, v        device [batch][n_kv_heads][N][head_dim]
+ *   k_out,v_out device [batch][n_kv_heads][budget][head_dim]: kept rows; with
+ *               budget > N rows N .. budget-1 are left untouched
+ *   pos_out     device int32 [batch][n_kv_heads][budget]: kept prompt positions
+ *   score_out   device float32 [batch][n_kv_heads][budget]: s of each kept token
+ *   scores_all  device float32 [batch][n_kv_heads][N]: s of every token, or NULL
+ *   ws          device workspace of ws_bytes >= lcd_h2o_prompt_sizes
+ * All buffers distinct. */
+lcd_status lcd_h2o_prompt_compress(const lcd_h2o_prompt_params* p, const void* q, const void* k, const void* v,
+                                   void* k_out, void* v_out, int32_t* pos_out, float* score_out,
+                                   float* scores_all, void* ws, uint64_t ws_bytes, void* stream);
+
 /* PyramidKV per-layer budgets ---------------------------------------------------
  * [KVC] "Alocação piramidal com o PyramidKV": the budget of layer l falls linearly
  * with depth, B_l = b_base + dB * (n_layers - 1 - l) / (n_layers - 1), and the

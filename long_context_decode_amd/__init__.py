@@ -30,6 +30,9 @@ from ._lib import (  # noqa: F401
     kv_slot_of,
     kv_tokens,
     pyramid_budgets,
+    h2o_prompt_params,
+    h2o_prompt_sizes,
+    h2o_prompt_compress,
     last_error,
     lib,
     snapkv_compress,

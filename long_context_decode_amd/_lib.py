@@ -42,6 +42,12 @@ class SnapkvParams(ctypes.Structure):
                 ("out_rows", ctypes.c_int32), ("scale", ctypes.c_double)]
 
 
+class H2oPromptParams(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("n_prompt", ctypes.c_int32), ("budget", ctypes.c_int32),
+                ("n_recent", ctypes.c_int32), ("dtype", ctypes.c_int32), ("scale", ctypes.c_double)]
+
+
 def _load():
     # torch supplies the device memory and streams handed to the library, so the
     # library must run on torch's HIP runtime: importing torch first makes the
@@ -82,6 +88,9 @@ _SIGS = {
     "lcd_snapkv_sizes": (_S, [ctypes.POINTER(SnapkvParams), ctypes.POINTER(_U64)]),
     "lcd_snapkv_compress": (_S, [ctypes.POINTER(SnapkvParams), _P, _P, _P, _P, _P, _P, _P, _P, _U64, _P]),
     "lcd_pyramid_budgets": (_S, [_I32, _I32, _I32, ctypes.POINTER(_I32)]),
+    "lcd_h2o_prompt_sizes": (_S, [ctypes.POINTER(H2oPromptParams), ctypes.POINTER(_U64)]),
+    "lcd_h2o_prompt_compress": (_S, [ctypes.POINTER(H2oPromptParams), _P, _P, _P, _P, _P, _P, _P, _P, _P, _U64,
+                                     _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(lib, _name)
@@ -206,6 +215,24 @@ def snapkv_sizes(p: SnapkvParams) -> int:
 def snapkv_compress(p: SnapkvParams, q_obs, k, v, k_out, v_out, idx_out, scores_out, ws, ws_bytes, stream=None):
     _check(lib.lcd_snapkv_compress(ctypes.byref(p), _ptr(q_obs), _ptr(k), _ptr(v), _ptr(k_out), _ptr(v_out),
                                    _ptr(idx_out), _ptr(scores_out), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def h2o_prompt_params(batch, n_q_heads, n_kv_heads, head_dim, n_prompt, budget, n_recent, dtype=LCD_BF16,
+                      scale=0.0):
+    return H2oPromptParams(batch, n_q_heads, n_kv_heads, head_dim, n_prompt, budget, n_recent, dtype, scale)
+
+
+def h2o_prompt_sizes(p: H2oPromptParams) -> int:
+    ws = _U64()
+    _check(lib.lcd_h2o_prompt_sizes(ctypes.byref(p), ctypes.byref(ws)))
+    return ws.value
+
+
+def h2o_prompt_compress(p: H2oPromptParams, q, k, v, k_out, v_out, pos_out, score_out, scores_all, ws, ws_bytes,
+                        stream=None):
+    _check(lib.lcd_h2o_prompt_compress(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(k_out), _ptr(v_out),
+                                       _ptr(pos_out), _ptr(score_out), _ptr(scores_all), _ptr(ws), ws_bytes,
+                                       _stream(stream)))
 
 
 def pyramid_budgets(n_layers, b_base, b_target):

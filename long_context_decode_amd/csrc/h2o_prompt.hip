@@ -1,0 +1,552 @@
+// H2O prompt-phase compression for gfx950 ([KVC] "Heavy-Hitter Oracle (H2O) e a
+// esparsidade de cauda pesada"): every prompt token's accumulated attention
+// s_j = sum over the group's query heads h and rows t >= j of the causal softmax
+// weight alpha_{h,t,j}, then the recent partition plus the heavy hitters, gathered
+// into the layout of a full H2O cache.
+//
+// The score is a dense causal Q K^T over the whole prompt (N^2/2 * D * 2 flop per query
+// head, twice: once for the row statistics, once for the column sums), so it runs on
+// MFMA (v_mfma_f32_32x32x16_bf16) and is compute-bound: both kernels take the K tile as
+// the A operand and the Q tile as the B operand, so the 32x32 result C[key][row] gives
+// each lane 16 keys of one row (lane % 32), and the per-row softmax statistics of pass 1
+// and the per-key sums of pass 2 need no cross-lane work inside the loop.
+//
+//   1. h2o_rowstats_kernel  per (block of RB prompt rows, query head): Q rows held in
+//                           registers, K streamed through LDS in 32-key tiles (double
+//                           buffered) over keys 0 .. last row; running (max, sum of
+//                           2^(x - max)) per row -> (M_t, 1/L_t).
+//   2. h2o_colsum_kernel    per (block of 128 .. 512 keys, KV head): K rows in registers,
+//                           Q tiles of the group's heads and their row statistics
+//                           streamed through LDS over rows t >= first key; weights
+//                           2^(x - M_t) / L_t summed per key in a fixed order -> s_j.
+//   3. h2o_topk_kernel      per (batch row, KV head): exact selection of the heavy
+//                           hitters on float32 s (radix select over range-relative
+//                           bits, candidates streamed from memory), then an ascending,
+//                           stable compaction by wave ballots; the recent tokens follow.
+//   4. h2o_gather_kernel    kept K / V rows, positions and scores.
+#include <hip/hip_runtime.h>
+
+#include "lcd_internal.h"
+
+namespace lcd {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kThreads = 256;
+constexpr int kTopkThreads = 1024;
+constexpr int kTopkWaves = kTopkThreads / 64;
+constexpr int kMaxChunks = 256;  // prompt chunks of kTopkThreads positions: N <= 262144
+constexpr int kDigitBits = 11;
+constexpr int kBins = 1 << kDigitBits;
+constexpr int kHistCopies = 4;
+
+__device__ inline bf16x8 frag_global(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+}
+
+__device__ inline bf16x8 frag_zero() { return __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0)); }
+
+// LDS tile of 32 rows x D bf16, rows padded by 16 bytes (fragment reads, one row per
+// lane, spread over the banks).
+template <int D>
+constexpr int tile_row_bytes() { return 2 * D + 16; }
+template <int D>
+constexpr int tile_bytes() { return 32 * tile_row_bytes<D>(); }
+template <int D>
+constexpr int tile_pieces_per_thread() { return 32 * D * 2 / 16 / kThreads; }  // 16-byte pieces
+
+// Global -> registers for one 32-row tile (rows past n read as zero).
+template <int D>
+__device__ inline void tile_load(const uint16_t* base, int row0, int n, uint4 (&r)[tile_pieces_per_thread<D>()]) {
+  constexpr int PPR = D * 2 / 16;  // pieces per row
+#pragma unroll
+  for (int i = 0; i < tile_pieces_per_thread<D>(); ++i) {
+    const int piece = i * kThreads + (int)threadIdx.x;
+    const int row = piece / PPR, col = piece % PPR;
+    r[i] = row0 + row < n ? *reinterpret_cast<const uint4*>(base + (size_t)(row0 + row) * D + col * 8)
+                          : make_uint4(0, 0, 0, 0);
+  }
+}
+
+template <int D>
+__device__ inline void tile_store(char* lds, const uint4 (&r)[tile_pieces_per_thread<D>()]) {
+  constexpr int PPR = D * 2 / 16;
+#pragma unroll
+  for (int i = 0; i < tile_pieces_per_thread<D>(); ++i) {
+    const int piece = i * kThreads + (int)threadIdx.x;
+    *reinterpret_cast<uint4*>(lds + (piece / PPR) * tile_row_bytes<D>() + (piece % PPR) * 16) = r[i];
+  }
+}
+
+// Fragment of k-step s: row lane % 32, elements 16 s + 8 (lane / 32) .. + 7.
+template <int D>
+__device__ inline bf16x8 frag_lds(const char* lds, int s, int lane) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(lds + (lane & 31) * tile_row_bytes<D>() +
+                                                                    32 * s + 16 * (lane >> 5)));
+}
+
+// C register r of a 32x32 MFMA result: A-row 8 (r / 4) + 4 (lane / 32) + r % 4 (the key),
+// B-column lane % 32 (the prompt row).
+__device__ inline int c_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+
+// Row tiles per wave in pass 1: the Q fragments of TPW tiles stay in registers.
+template <int D>
+constexpr int rows_tiles_per_wave() { return D == 64 ? 4 : (D == 128 ? 2 : 1); }
+
+// ------------------------------------------------------------------ 1. row statistics
+template <int D>
+__global__ void __launch_bounds__(kThreads) h2o_rowstats_kernel(H2oPromptParams p) {
+  constexpr int TPW = rows_tiles_per_wave<D>();
+  constexpr int RB = 4 * TPW * 32;  // prompt rows per workgroup
+  constexpr int KS = D / 16;        // MFMA k-steps
+  __shared__ __attribute__((aligned(16))) char ktile[2][tile_bytes<D>()];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int blk = (int)gridDim.x - 1 - (int)blockIdx.x;  // longest causal ranges first
+  const int h = blockIdx.y, b = blockIdx.z, g = h / (p.Hq / p.Hkv);
+  const int P0 = blk * RB;
+  const uint16_t* Q = reinterpret_cast<const uint16_t*>(p.q) + ((size_t)b * p.Hq + h) * p.N * D;
+  const uint16_t* K = reinterpret_cast<const uint16_t*>(p.k) + ((size_t)b * p.Hkv + g) * p.N * D;
+
+  bf16x8 qf[TPW][KS];
+  float m[TPW], l[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int row = P0 + (wave * TPW + i) * 32 + (lane & 31);
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      qf[i][s] = row < p.N ? frag_global(Q + (size_t)row * D + 16 * s + 8 * (lane >> 5)) : frag_zero();
+    m[i] = -INFINITY;
+    l[i] = 0.f;
+  }
+  const int n_keys = min(p.N, P0 + RB);
+  const int n_tiles = (n_keys + 31) / 32;
+  uint4 raw[tile_pieces_per_thread<D>()];
+  tile_load<D>(K, 0, p.N, raw);
+  tile_store<D>(ktile[0], raw);
+  for (int kt = 0; kt < n_tiles; ++kt) {
+    if (kt + 1 < n_tiles) tile_load<D>(K, (kt + 1) * 32, p.N, raw);
+    __syncthreads();  // tile kt is in ktile[kt & 1]; every wave is done with tile kt - 1
+    const char* kl = ktile[kt & 1];
+    // row tiles that see some key of this tile (wave-uniform)
+    bool act[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int r0 = P0 + (wave * TPW + i) * 32;
+      act[i] = kt * 32 <= r0 + 31 && r0 < p.N;
+    }
+    f32x16 acc[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) acc[i] = f32x16{};
+    // each K fragment is read from LDS once and used for every row tile
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const bf16x8 a = frag_lds<D>(kl, s, lane);
+#pragma unroll
+      for (int i = 0; i < TPW; ++i)
+        if (act[i]) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[i][s], acc[i], 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      if (!act[i]) continue;
+      const int r0 = P0 + (wave * TPW + i) * 32;
+      // keys past N sit in the tile only when the tile holds the last key, which is
+      // the diagonal case; there key <= row < N masks them too
+      const bool full = kt * 32 + 31 <= r0;  // every key <= every row (wave-uniform)
+      const int dlt = r0 + (lane & 31) - kt * 32;
+      float x[16], bm = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        x[r] = full || c_row(r, lane) <= dlt ? acc[i][r] * p.qscale : -INFINITY;
+        bm = fmaxf(bm, x[r]);
+      }
+      const float mn = fmaxf(m[i], bm);
+      if (mn > -INFINITY) {
+        float add = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) add += exp2f(x[r] - mn);
+        l[i] = l[i] * exp2f(m[i] - mn) + add;
+        m[i] = mn;
+      }
+    }
+    if (kt + 1 < n_tiles) tile_store<D>(ktile[(kt + 1) & 1], raw);
+  }
+  // lanes l and l ^ 32 hold the same row (the two halves of every key tile)
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const float mo = __shfl_xor(m[i], 32, 64), lo = __shfl_xor(l[i], 32, 64);
+    const float M = fmaxf(m[i], mo);
+    const float L = (m[i] > -INFINITY ? l[i] * exp2f(m[i] - M) : 0.f) + (mo > -INFINITY ? lo * exp2f(mo - M) : 0.f);
+    const int row = P0 + (wave * TPW + i) * 32 + (lane & 31);
+    if (lane < 32 && row < p.N) {
+      float2* st = reinterpret_cast<float2*>(p.rowstat) + ((size_t)b * p.Hq + h) * p.N + row;
+      *st = make_float2(M, 1.f / L);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ 2. column sums
+// Key tiles per wave in pass 2: the K fragments of KT tiles stay in registers, and each
+// Q fragment read from LDS serves all of them.
+template <int D>
+constexpr int key_tiles_per_wave() { return D == 64 ? 4 : (D == 128 ? 2 : 1); }
+template <int D>
+constexpr int col_keys() { return 4 * 32 * key_tiles_per_wave<D>(); }  // keys per workgroup
+
+template <int D>
+__global__ void __launch_bounds__(kThreads, 2) h2o_colsum_kernel(H2oPromptParams p) {
+  constexpr int KS = D / 16;
+  __shared__ __attribute__((aligned(16))) char qtile[2][tile_bytes<D>()];
+  __shared__ float2 qstat[2][32];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int kb = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int G = p.Hq / p.Hkv;
+  constexpr int KT = key_tiles_per_wave<D>();
+  const int kblk0 = kb * col_keys<D>();
+  const int key0 = kblk0 + wave * KT * 32;  // the wave's first key
+  const uint16_t* K = reinterpret_cast<const uint16_t*>(p.k) + ((size_t)b * p.Hkv + g) * p.N * D;
+  bf16x8 kf[KT][KS];
+#pragma unroll
+  for (int t = 0; t < KT; ++t) {
+    const int key = key0 + t * 32 + (lane & 31);
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      kf[t][s] = key < p.N ? frag_global(K + (size_t)key * D + 16 * s + 8 * (lane >> 5)) : frag_zero();
+  }
+  float col[KT][16];
+#pragma unroll
+  for (int t = 0; t < KT; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) col[t][r] = 0.f;
+
+  // work units: (row tile, head) for row tiles from the block's first key to the end
+  const int t_first = kblk0 / 32;
+  const int n_rt = (p.N + 31) / 32;
+  const int units = (n_rt - t_first) * G;
+  auto unit_src = [&](int u, const uint16_t** q, const float2** st, int* row0) {
+    const int rt = t_first + u / G, j = u % G;
+    const size_t bh = (size_t)b * p.Hq + g * G + j;
+    *q = reinterpret_cast<const uint16_t*>(p.q) + bh * p.N * D;
+    *st = reinterpret_cast<const float2*>(p.rowstat) + bh * p.N;
+    *row0 = rt * 32;
+  };
+  uint4 raw[tile_pieces_per_thread<D>()];
+  float2 sraw = make_float2(0.f, 0.f);
+  {
+    const uint16_t* q;
+    const float2* st;
+    int row0;
+    unit_src(0, &q, &st, &row0);
+    tile_load<D>(q, row0, p.N, raw);
+    if (threadIdx.x < 32) sraw = row0 + (int)threadIdx.x < p.N ? st[row0 + threadIdx.x] : make_float2(0.f, 0.f);
+    tile_store<D>(qtile[0], raw);
+    if (threadIdx.x < 32) qstat[0][threadIdx.x] = sraw;
+  }
+  for (int u = 0; u < units; ++u) {
+    const uint16_t* qn = nullptr;
+    const float2* stn = nullptr;
+    int row0n = 0;
+    if (u + 1 < units) {
+      unit_src(u + 1, &qn, &stn, &row0n);
+      tile_load<D>(qn, row0n, p.N, raw);
+      if (threadIdx.x < 32) sraw = row0n + (int)threadIdx.x < p.N ? stn[row0n + threadIdx.x] : make_float2(0.f, 0.f);
+    }
+    __syncthreads();  // unit u is in buffer u & 1; every wave is done with unit u - 1
+    const int row0 = (t_first + u / G) * 32;
+    const char* ql = qtile[u & 1];
+    bool act[KT];
+#pragma unroll
+    for (int t = 0; t < KT; ++t) act[t] = row0 + 31 >= key0 + t * 32 && key0 + t * 32 < p.N;
+    f32x16 acc[KT];
+#pragma unroll
+    for (int t = 0; t < KT; ++t) acc[t] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const bf16x8 bq = frag_lds<D>(ql, s, lane);
+#pragma unroll
+      for (int t = 0; t < KT; ++t)
+        if (act[t]) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t][s], bq, acc[t], 0, 0, 0);
+    }
+    const float2 st = qstat[u & 1][lane & 31];  // rows past N carry (0, 0): weight 0
+#pragma unroll
+    for (int t = 0; t < KT; ++t) {
+      if (!act[t]) continue;
+      if (row0 >= key0 + t * 32 + 31) {  // every key of the tile is <= every row (wave-uniform)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) col[t][r] += exp2f(acc[t][r] * p.qscale - st.x) * st.y;
+      } else {  // the diagonal tile: key <= row <=> c_row <= row - first key
+        const int dlt = row0 + (lane & 31) - (key0 + t * 32);
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          col[t][r] += c_row(r, lane) <= dlt ? exp2f(acc[t][r] * p.qscale - st.x) * st.y : 0.f;
+      }
+    }
+    if (u + 1 < units) {
+      tile_store<D>(qtile[(u + 1) & 1], raw);
+      if (threadIdx.x < 32) qstat[(u + 1) & 1][threadIdx.x] = sraw;
+    }
+  }
+  // lanes of one half (lane / 32 fixed) hold the same 16 keys for different rows
+#pragma unroll
+  for (int t = 0; t < KT; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float x = col[t][r];
+#pragma unroll
+      for (int off = 1; off < 32; off <<= 1) x += __shfl_xor(x, off, 64);
+      col[t][r] = x;
+    }
+  if ((lane & 31) == 0) {
+    float* s = p.scores + ((size_t)b * p.Hkv + g) * p.N;
+#pragma unroll
+    for (int t = 0; t < KT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + t * 32 + c_row(r, lane);
+        if (key < p.N) s[key] = col[t][r];
+      }
+  }
+}
+
+// ------------------------------------------------------------------ 3. selection
+// Exclusive scan over the 1024 threads (per-wave shuffles, one barrier, every wave
+// adds the totals of the waves before it); *total receives the sum.  Callers alternate
+// the two halves of `buf` between consecutive scans.
+__device__ inline int topk_scan(int v, int* buf, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) buf[wave] = x;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; ++w) {
+    const int t = buf[w];
+    before += w < wave ? t : 0;
+    all += t;
+  }
+  *total = all;
+  return before + x - v;
+}
+
+// One workgroup per (batch row, KV head).  Candidates are positions [0, Np); chunk c
+// covers positions c * 1024 .. c * 1024 + 1023 with position c * 1024 + threadIdx.x
+// per thread, so every pass over the scores reads them coalesced.  Selection: the
+// k-th largest float32 score T by radix select over v = bits - min(bits) (scores are
+// >= 0, so bits order like values); kept = v > T plus the first positions with v == T
+// up to k.  Compaction: per (chunk, wave) counts of both kinds, one scan over them,
+// then ballots place each wave's kept positions in ascending order.
+__global__ void __launch_bounds__(kTopkThreads) h2o_topk_kernel(H2oPromptParams p) {
+  // the radix histogram, then (once the threshold is known) the per-piece counts
+  static_assert(2 * kMaxChunks * kTopkWaves <= kHistCopies * kBins, "counts overlay the histogram");
+  __shared__ int hist[kHistCopies * kBins];
+  __shared__ int scan_buf[2][kTopkWaves];
+  __shared__ uint32_t wmin[kTopkWaves], wmax[kTopkWaves];
+  __shared__ int s_digit, s_krem;
+  int* cnt_gt = hist;
+  int* cnt_eq = hist + kMaxChunks * kTopkWaves;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const size_t bg = blockIdx.x;
+  const float* sc = p.scores + bg * p.N;
+  int* idx = p.pos_out + bg * p.budget;
+  const int N = p.N;
+  const int kept_rows = min(p.budget, N);
+  const int n_recent = min(p.n_recent, kept_rows);
+  const int Np = N - n_recent;              // candidates of the heavy partition
+  const int k = kept_rows - n_recent;       // heavy hitters kept (<= Np)
+  const int chunks = (Np + kTopkThreads - 1) / kTopkThreads;
+  int total;
+
+  if (k >= Np) {  // every candidate is kept
+    for (int i = threadIdx.x; i < Np; i += kTopkThreads) idx[i] = i;
+  } else if (k > 0) {
+    uint32_t lmin = 0xffffffffu, lmax = 0u;
+    for (int c = 0; c < chunks; ++c) {
+      const int i = c * kTopkThreads + threadIdx.x;
+      if (i < Np) {
+        const uint32_t u = __float_as_uint(sc[i]);
+        lmin = min(lmin, u);
+        lmax = max(lmax, u);
+      }
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      lmin = min(lmin, (uint32_t)__shfl_xor((int)lmin, off, 64));
+      lmax = max(lmax, (uint32_t)__shfl_xor((int)lmax, off, 64));
+    }
+    if (lane == 0) {
+      wmin[wave] = lmin;
+      wmax[wave] = lmax;
+    }
+    __syncthreads();
+    uint32_t umin = 0xffffffffu, umax = 0u;
+#pragma unroll
+    for (int w = 0; w < kTopkWaves; ++w) {
+      umin = min(umin, wmin[w]);
+      umax = max(umax, wmax[w]);
+    }
+    const uint32_t range = umax - umin;
+    const int Lb = range ? 32 - __clz((int)range) : 0;
+    uint32_t prefix = 0, mask = 0;
+    int krem = k;
+    for (int hi = Lb; hi > 0; hi -= kDigitBits) {
+      const int shift = hi > kDigitBits ? hi - kDigitBits : 0;
+      const int bits = hi - shift;
+      const uint32_t dmask = (1u << bits) - 1u;
+      for (int i = threadIdx.x; i < kHistCopies * kBins; i += kTopkThreads) hist[i] = 0;
+      __syncthreads();
+      int* hcopy = hist + (threadIdx.x & (kHistCopies - 1)) * kBins;
+      for (int c = 0; c < chunks; ++c) {
+        const int i = c * kTopkThreads + threadIdx.x;
+        if (i < Np) {
+          const uint32_t v = __float_as_uint(sc[i]) - umin;
+          if ((v & mask) == prefix) atomicAdd(&hcopy[(v >> shift) & dmask], 1);
+        }
+      }
+      __syncthreads();
+      const int nb = 1 << bits;
+      int cb[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int bin = nb - 1 - (2 * (int)threadIdx.x + e);
+        int v = 0;
+        if (bin >= 0)
+          for (int q = 0; q < kHistCopies; ++q) v += hist[q * kBins + bin];
+        cb[e] = v;
+      }
+      const int before = topk_scan(cb[0] + cb[1], scan_buf[0], &total);
+      if (before < krem && before + cb[0] + cb[1] >= krem) {
+        const int e = before + cb[0] >= krem ? 0 : 1;
+        s_digit = nb - 1 - (2 * (int)threadIdx.x + e);
+        s_krem = krem - before - (e ? cb[0] : 0);
+      }
+      __syncthreads();
+      prefix |= (uint32_t)s_digit << shift;
+      mask |= dmask << shift;
+      krem = s_krem;
+      __syncthreads();
+    }
+    const uint32_t T = prefix;  // v of the k-th largest score
+    const int take_eq = krem;   // values equal to T that are kept
+    // per (chunk, wave) counts of v > T and v == T
+    for (int c = 0; c < chunks; ++c) {
+      const int i = c * kTopkThreads + threadIdx.x;
+      uint32_t v = 0;
+      bool in = i < Np;
+      if (in) v = __float_as_uint(sc[i]) - umin;
+      const unsigned long long bgt = __ballot(in && v > T), beq = __ballot(in && v == T);
+      if (lane == 0) {
+        cnt_gt[c * kTopkWaves + wave] = __popcll(bgt);
+        cnt_eq[c * kTopkWaves + wave] = __popcll(beq);
+      }
+    }
+    __syncthreads();
+    // exclusive prefix of both counts over (chunk, wave) in order: each thread sums a
+    // contiguous run of the entries, then one scan over the threads
+    const int n_ent = chunks * kTopkWaves;
+    const int per = (n_ent + kTopkThreads - 1) / kTopkThreads;
+    const int e0 = threadIdx.x * per;
+    int sg = 0, se = 0;
+    for (int e = e0; e < min(e0 + per, n_ent); ++e) {
+      sg += cnt_gt[e];
+      se += cnt_eq[e];
+    }
+    int run_eq = topk_scan(se, scan_buf[1], &total);
+    int run_gt = topk_scan(sg, scan_buf[0], &total);
+    __syncthreads();
+    // turn the counts into the output offset of each (chunk, wave) piece: kept before
+    // it = gt before + min(eq before, take_eq)
+    for (int e = e0; e < min(e0 + per, n_ent); ++e) {
+      const int g_here = cnt_gt[e], e_here = cnt_eq[e];
+      cnt_gt[e] = run_gt + min(run_eq, take_eq);  // output offset of the piece
+      cnt_eq[e] = run_eq;                          // equal values before the piece
+      run_gt += g_here;
+      run_eq += e_here;
+    }
+    __syncthreads();
+    for (int c = 0; c < chunks; ++c) {
+      const int i = c * kTopkThreads + threadIdx.x;
+      uint32_t v = 0;
+      bool in = i < Np;
+      if (in) v = __float_as_uint(sc[i]) - umin;
+      const bool gt = in && v > T, eq = in && v == T;
+      const unsigned long long beq = __ballot(eq);
+      const int eq_rank = cnt_eq[c * kTopkWaves + wave] + __popcll(beq & ((1ull << lane) - 1ull));
+      const bool keep = gt || (eq && eq_rank < take_eq);
+      const unsigned long long bk = __ballot(keep);
+      if (keep) idx[cnt_gt[c * kTopkWaves + wave] + __popcll(bk & ((1ull << lane) - 1ull))] = i;
+    }
+  }
+  for (int t = threadIdx.x; t < n_recent; t += kTopkThreads) idx[k + t] = Np + t;
+}
+
+// ------------------------------------------------------------------ 4. gather
+template <int D>
+__global__ void __launch_bounds__(kThreads) h2o_gather_kernel(H2oPromptParams p) {
+  const size_t bg = blockIdx.y;
+  const int rows = min(p.budget, p.N);
+  constexpr int PPR = D * 2 / 16;
+  const int* idx = p.pos_out + bg * p.budget;
+  const char* k = reinterpret_cast<const char*>(p.k) + bg * p.N * D * 2;
+  const char* v = reinterpret_cast<const char*>(p.v) + bg * p.N * D * 2;
+  char* ko = reinterpret_cast<char*>(p.k_out) + bg * p.budget * D * 2;
+  char* vo = reinterpret_cast<char*>(p.v_out) + bg * p.budget * D * 2;
+  const int total = rows * PPR;
+  for (int e = blockIdx.x * kThreads + threadIdx.x; e < total; e += gridDim.x * kThreads) {
+    const int row = e / PPR, c = e % PPR;
+    const int src = idx[row];
+    const size_t so = (size_t)src * D * 2 + (size_t)c * 16, dst = (size_t)row * D * 2 + (size_t)c * 16;
+    *reinterpret_cast<uint4*>(ko + dst) = *reinterpret_cast<const uint4*>(k + so);
+    *reinterpret_cast<uint4*>(vo + dst) = *reinterpret_cast<const uint4*>(v + so);
+    if (c == 0) {
+      const float s = p.scores[bg * p.N + src];
+      p.score_out[bg * p.budget + row] = s;
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_d(const H2oPromptParams& p, hipStream_t s) {
+  constexpr int RB = 4 * rows_tiles_per_wave<D>() * 32;
+  hipLaunchKernelGGL(h2o_rowstats_kernel<D>, dim3((p.N + RB - 1) / RB, p.Hq, p.B), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL(h2o_colsum_kernel<D>, dim3((p.N + col_keys<D>() - 1) / col_keys<D>(), p.Hkv, p.B),
+                     dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL(h2o_topk_kernel, dim3(p.B * p.Hkv), dim3(kTopkThreads), 0, s, p);
+  const int rows = p.budget < p.N ? p.budget : p.N;
+  const int blocks = (rows * (D * 2 / 16) + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL(h2o_gather_kernel<D>, dim3(blocks < 1024 ? blocks : 1024, p.B * p.Hkv), dim3(kThreads), 0, s,
+                     p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+static size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t h2o_prompt_ws_bytes(int B, int Hq, int Hkv, int N) {
+  const size_t stats = round256((size_t)B * Hq * N * 2 * sizeof(float));
+  const size_t scores = round256((size_t)B * Hkv * N * sizeof(float));
+  return stats + scores;
+}
+
+hipError_t launch_h2o_prompt(const H2oPromptParams& in, void* ws, float* scores_all, hipStream_t s) {
+  H2oPromptParams p = in;
+  char* w = static_cast<char*>(ws);
+  p.rowstat = reinterpret_cast<float*>(w);
+  p.scores = scores_all ? scores_all
+                        : reinterpret_cast<float*>(w + round256((size_t)p.B * p.Hq * p.N * 2 * sizeof(float)));
+  switch (p.D) {
+    case 64: return launch_d<64>(p, s);
+    case 128: return launch_d<128>(p, s);
+    case 256: return launch_d<256>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace lcd

@@ -677,6 +677,72 @@ extern "C" lcd_status lcd_snapkv_compress(const lcd_snapkv_params* p, const void
   return ok();
 }
 
+// ------------------------------------------------------------------ H2O prompt phase
+namespace {
+
+lcd_status check_h2o_prompt(const lcd_h2o_prompt_params* p) {
+  if (!p) return fail(LCD_EINVAL, "params is NULL");
+  if (p->batch < 1 || p->n_kv_heads < 1 || p->n_q_heads < 1) return fail(LCD_ESHAPE, "batch and heads must be >= 1");
+  if (p->n_q_heads % p->n_kv_heads)
+    return fail(LCD_ESHAPE, "n_q_heads (%d) must be a multiple of n_kv_heads (%d)", p->n_q_heads, p->n_kv_heads);
+  if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 256)
+    return fail(LCD_ESHAPE, "head_dim %d not in {64, 128, 256}", p->head_dim);
+  if (p->n_prompt < 1 || p->n_prompt > 262144) return fail(LCD_ESHAPE, "n_prompt %d outside [1, 262144]", p->n_prompt);
+  if (p->n_recent < 1 || p->budget < p->n_recent) return fail(LCD_ESHAPE, "need 1 <= n_recent <= budget");
+  if (p->dtype != LCD_BF16) return fail(LCD_EUNSUPPORTED, "the prompt-phase scores run on bf16 MFMA (dtype must be bf16)");
+  if (!(std::isfinite(p->scale) && p->scale >= 0.0)) return fail(LCD_EINVAL, "scale must be finite and >= 0");
+  uint64_t e = (uint64_t)p->batch;
+  if (!mul_ok(&e, p->n_q_heads) || !mul_ok(&e, p->n_prompt) || !mul_ok(&e, p->head_dim) || e > (uint64_t)1 << 40)
+    return fail(LCD_ESIZE, "prompt tensors too large");
+  return LCD_OK;
+}
+
+}  // namespace
+
+extern "C" lcd_status lcd_h2o_prompt_sizes(const lcd_h2o_prompt_params* p, uint64_t* ws_bytes) {
+  const lcd_status st = check_h2o_prompt(p);
+  if (st) return st;
+  if (ws_bytes) *ws_bytes = lcd::h2o_prompt_ws_bytes(p->batch, p->n_q_heads, p->n_kv_heads, p->n_prompt);
+  return ok();
+}
+
+extern "C" lcd_status lcd_h2o_prompt_compress(const lcd_h2o_prompt_params* p, const void* q, const void* k,
+                                              const void* v, void* k_out, void* v_out, int32_t* pos_out,
+                                              float* score_out, float* scores_all, void* ws, uint64_t ws_bytes,
+                                              void* stream) {
+  lcd_status st = check_h2o_prompt(p);
+  if (st) return st;
+  if (!q || !k || !v || !k_out || !v_out || !pos_out || !score_out || !ws)
+    return fail(LCD_EINVAL, "a required buffer is NULL");
+  const void* bufs[] = {q, k, v, k_out, v_out, pos_out, score_out, ws};
+  for (const void* b : bufs)
+    if (!aligned16(b)) return fail(LCD_EALIGN, "buffers must be 16-byte aligned");
+  if (scores_all && !aligned16(scores_all)) return fail(LCD_EALIGN, "scores_all must be 16-byte aligned");
+  const uint64_t need = lcd::h2o_prompt_ws_bytes(p->batch, p->n_q_heads, p->n_kv_heads, p->n_prompt);
+  if (ws_bytes < need)
+    return fail(LCD_ESIZE, "ws_bytes %llu < required %llu", (unsigned long long)ws_bytes, (unsigned long long)need);
+  lcd::H2oPromptParams h{};
+  h.q = q;
+  h.k = k;
+  h.v = v;
+  h.k_out = k_out;
+  h.v_out = v_out;
+  h.pos_out = pos_out;
+  h.score_out = score_out;
+  h.B = p->batch;
+  h.Hq = p->n_q_heads;
+  h.Hkv = p->n_kv_heads;
+  h.D = p->head_dim;
+  h.N = p->n_prompt;
+  h.budget = p->budget;
+  h.n_recent = p->n_recent;
+  const double scale = p->scale > 0 ? p->scale : 1.0 / std::sqrt((double)p->head_dim);
+  h.qscale = (float)(scale * 1.4426950408889634074);
+  const hipError_t e = lcd::launch_h2o_prompt(h, ws, scores_all, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "h2o prompt launch");
+  return ok();
+}
+
 // ------------------------------------------------------------------ PyramidKV budgets
 extern "C" lcd_status lcd_pyramid_budgets(int32_t n_layers, int32_t b_base, int32_t b_target, int32_t* out) {
   if (!out) return fail(LCD_EINVAL, "budgets_out is NULL");

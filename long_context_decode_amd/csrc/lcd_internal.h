@@ -117,4 +117,21 @@ struct SnapkvParams {
 size_t snapkv_ws_bytes(int B, int H, int N, int Lobs);
 hipError_t launch_snapkv(const SnapkvParams& p, hipStream_t s);
 
+// H2O prompt-phase compression (see h2o_prompt.hip).
+struct H2oPromptParams {
+  const void* q;       // [B][Hq][N][D] bf16
+  const void* k;       // [B][Hkv][N][D]
+  const void* v;
+  void* k_out;         // [B][Hkv][budget][D]
+  void* v_out;
+  int* pos_out;        // [B][Hkv][budget]
+  float* score_out;    // [B][Hkv][budget]
+  float* rowstat;      // ws: [B][Hq][N] (max, 1/sum), log2 domain
+  float* scores;       // [B][Hkv][N] accumulated scores (ws or the caller's buffer)
+  int B, Hq, Hkv, D, N, budget, n_recent;
+  float qscale;        // scale * log2(e)
+};
+size_t h2o_prompt_ws_bytes(int B, int Hq, int Hkv, int N);
+hipError_t launch_h2o_prompt(const H2oPromptParams& p, void* ws, float* scores_all, hipStream_t s);
+
 }  // namespace lcd

@@ -1,9 +1,9 @@
-"""The six synthetic workloads and their seeded tensors.
+"""The synthetic workloads and their seeded tensors.
 
 Shapes follow the decode configurations of the pages' examples (a tiny streaming
 case, a Llama-2-7B-shaped layer with a 4+2044 cache, a Qwen-like 24/4-head GQA
-model with 16 attention layers, a 32k SnapKV prompt, a 128k H2O budget and a 128k
-DuoAttention mixed-head layer).
+model with 16 attention layers, a 32k SnapKV prompt, a 128k H2O budget, its
+128k prompt phase and a 128k DuoAttention mixed-head layer).
 Tensors are virtual: each is a :class:`synth.gen.NormalStream` over a fixed
 logical shape, so any slice can be produced on the CPU (numpy) or on the GPU
 (torch) with identical bits.
@@ -24,7 +24,7 @@ SEED = 0
 class Workload:
     name: str
     title: str
-    kind: str  # "streaming" | "snapkv" | "h2o" | "duo"
+    kind: str  # "streaming" | "snapkv" | "h2o" | "duo" | "h2o_prompt"
     batch: int
     n_q_heads: int
     n_kv_heads: int
@@ -190,6 +190,32 @@ class Workload:
                     out[b, h, p] = st.torch_stored(idx[p], self.plant_scale)
         return out
 
+    # ------------------------------------------------------------------ h2o prompt phase
+    def prompt_tensor(self, tensor: str, b: int, h: int, *, f64=True):
+        """[N][d] prompt block of one head: "q" (query head h) or "k" / "v" (KV head h)."""
+        heads = self.n_q_heads if tensor == "q" else self.n_kv_heads
+        base = (b * heads + h) * self.n_prompt * self.head_dim
+        idx = base + np.arange(self.n_prompt * self.head_dim, dtype=np.int64).reshape(self.n_prompt, self.head_dim)
+        st = NormalStream(self.seed, f"{self.name}/prompt/{tensor}", self.dtype)
+        return st.values(idx) if f64 else st.stored(idx)
+
+    def prompt_tensor_torch(self, tensor: str, device):
+        """The whole [B][H][N][D] prompt tensor on ``device`` (H = query or KV heads)."""
+        import torch
+
+        heads = self.n_q_heads if tensor == "q" else self.n_kv_heads
+        B, N, D = self.batch, self.n_prompt, self.head_dim
+        st = NormalStream(self.seed, f"{self.name}/prompt/{tensor}", self.dtype)
+        out = torch.empty((B, heads, N, D), device=device,
+                          dtype=torch.float32 if self.dtype == "f32" else torch.bfloat16)
+        per = N * D
+        for b in range(B):
+            for h in range(heads):
+                base = (b * heads + h) * per
+                out[b, h] = st.torch_stored(torch.arange(base, base + per, device=device,
+                                                         dtype=torch.int64)).view(N, D)
+        return out
+
     # ------------------------------------------------------------------ h2o
     def h2o_initial_state(self, b: int, g: int):
         """Seeded post-compression H2O state of one (batch row, kv head).
@@ -308,6 +334,12 @@ WORKLOADS = {
               "256 decode steps",
         kind="duo", batch=16, n_q_heads=32, n_kv_heads=8, head_dim=128, dtype="bf16",
         n_sink=4, window=64, prefill=131072, steps=256, retrieval=((1, 0, 0, 0, 0, 1, 0, 0),)),
+    "h2o_prompt_128k": Workload(
+        name="h2o_prompt_128k",
+        title="H2O prompt-phase compression: B=16, 32 q / 8 kv heads, D=128, bf16, 131072-token prompt "
+              "scored by its full causal attention, kept in a 4096 budget (512 recent + 3584 heavy)",
+        kind="h2o_prompt", batch=16, n_q_heads=32, n_kv_heads=8, head_dim=128, dtype="bf16",
+        n_prompt=131072, budget=4096, n_recent=512),
     "h2o_128k": Workload(
         name="h2o_128k",
         title="H2O budgeted decode: B=16, 32 q / 8 kv heads, D=128, bf16, 131072-token prompt held in "

@@ -183,3 +183,17 @@ def test_pyramid_budgets_rejects(L, args):
         L.pyramid_budgets(*args)
     import ctypes
     assert L.lib.lcd_pyramid_budgets(3, 1, 2, None) == 1  # LCD_EINVAL for a null output
+
+
+def test_h2o_prompt_param_validation(L):
+    ok = dict(batch=16, n_q_heads=32, n_kv_heads=8, head_dim=128, n_prompt=131072, budget=4096, n_recent=512)
+    assert L.h2o_prompt_sizes(L.h2o_prompt_params(**ok)) > 16 * 32 * 131072 * 8
+    for kw, status in [(dict(n_q_heads=12, n_kv_heads=8), "LCD_ESHAPE"), (dict(head_dim=96), "LCD_ESHAPE"),
+                       (dict(n_prompt=262145), "LCD_ESHAPE"), (dict(n_recent=0), "LCD_ESHAPE"),
+                       (dict(budget=100, n_recent=200), "LCD_ESHAPE"), (dict(dtype=0), "LCD_EUNSUPPORTED"),
+                       (dict(scale=-1.0), "LCD_EINVAL")]:
+        p = dict(ok)
+        p.update(kw)
+        with pytest.raises(L.LcdError) as e:
+            L.h2o_prompt_sizes(L.h2o_prompt_params(**p))
+        assert e.value.name == status, kw
