@@ -11,7 +11,8 @@ layer with a 4+2044 sink + ring cache) with steps/s, the decode kernel's achieve
 HBM bandwidth against the 8 TB/s peak (HIP events on the launch stream around batches
 of back-to-back decode_attn launches), the decode kernel's counter-measured HBM traffic
 when the record under profiles/ matches the current kernel sources, the SnapKV
-compression time, secondary decode workloads
+compression time, the H2O prompt-phase compression time and MFMA rate, secondary decode
+workloads
 (the 16-layer GQA 32k cache, the H2O 4096 budget, the DuoAttention 128k mixed-head
 layer, the tiny fp32 stream) unless
 --only, and the fp64 CPU oracle timed on a bounded sample of the headline step.
@@ -42,6 +43,7 @@ def _parse(argv=None):
     ap.add_argument("--workload", default="llama2_7b_layer", choices=sorted(DEFAULTS))
     ap.add_argument("--only", action="store_true", help="skip the secondary workloads and SnapKV")
     ap.add_argument("--no-snapkv", action="store_true", help="skip the SnapKV compression timing")
+    ap.add_argument("--no-h2o-prompt", action="store_true", help="skip the H2O prompt-phase compression timing")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="bound of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -347,6 +349,40 @@ def _snapkv_bench(L, w, reps=20):
             "mfma_frac_bf16": round(flops / (ms / 1e3) / MFMA_BF16_PEAK, 5)}
 
 
+def _h2o_prompt_bench(L, w, reps=2):
+    """H2O prompt-phase compression of the 128k prompt: ms per compress (best of ``reps``
+    after one warm-up) and the MFMA rate of its two causal score contractions."""
+    import torch
+
+    B, Hq, Hkv, D, N, C = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_prompt, w.budget
+    dev = "cuda"
+    p = L.h2o_prompt_params(B, Hq, Hkv, D, N, C, w.n_recent)
+    wsb = L.h2o_prompt_sizes(p)
+    q, k, v = (w.prompt_tensor_torch(t, dev) for t in ("q", "k", "v"))
+    ko = torch.empty((B, Hkv, C, D), dtype=torch.bfloat16, device=dev)
+    vo = torch.empty_like(ko)
+    pos = torch.empty((B, Hkv, C), dtype=torch.int32, device=dev)
+    sco = torch.empty((B, Hkv, C), dtype=torch.float32, device=dev)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    L.h2o_prompt_compress(p, q, k, v, ko, vo, pos, sco, None, ws, wsb)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        L.h2o_prompt_compress(p, q, k, v, ko, vo, pos, sco, None, ws, wsb)
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    ms = min(times)
+    flops = 2 * B * Hq * (N * (N + 1) // 2) * D * 2  # two causal Q K^T passes
+    del q, k, v, ko, vo, ws
+    torch.cuda.empty_cache()
+    return {"workload": w.title, "compress_ms": round(ms, 2), "reps": reps, "flops": flops,
+            "tflops": round(flops / (ms / 1e3) / 1e12, 1),
+            "mfma_frac_bf16": round(flops / (ms / 1e3) / MFMA_BF16_PEAK, 4)}
+
+
 def _cpu_baseline_streaming(w, budget_s):
     """The fp64 oracle on a bounded sample of consecutive decode steps (single thread):
     whole steps (every layer, row and KV head) until the budget is spent, the last step
@@ -451,6 +487,8 @@ def main(argv=None):
     }
     if not a.only and not a.no_snapkv:
         line["snapkv"] = _snapkv_bench(L, WORKLOADS["snapkv_32k"])
+    if not a.only and not a.no_h2o_prompt:
+        line["h2o_prompt"] = _h2o_prompt_bench(L, WORKLOADS["h2o_prompt_128k"])
     if not a.only:
         others = []
         for name in ("gqa_long", "h2o_128k", "duo_128k", "tiny_streaming"):

@@ -11,12 +11,12 @@
 // each lane 16 keys of one row (lane % 32), and the per-row softmax statistics of pass 1
 // and the per-key sums of pass 2 need no cross-lane work inside the loop.
 //
-//   1. h2o_rowstats_kernel  per (block of RB prompt rows, query head): Q rows held in
-//                           registers, K streamed through LDS in 32-key tiles (double
-//                           buffered) over keys 0 .. last row; running (max, sum of
-//                           2^(x - max)) per row -> (M_t, 1/L_t).
-//   2. h2o_colsum_kernel    per (block of 128 .. 512 keys, KV head): K rows in registers,
-//                           Q tiles of the group's heads and their row statistics
+//   1. h2o_rowstats_kernel  per (256 prompt rows, query head): Q rows held in registers,
+//                           K streamed through LDS in blocks of 128 (D = 256: 64) keys,
+//                           double buffered, over keys 0 .. last row; running (max, sum
+//                           of 2^(x - max)) per row -> (M_t, 1/L_t).
+//   2. h2o_colsum_kernel    per (256 keys, KV head): K rows in registers, blocks of 128
+//                           (64) rows of the group's query heads and their statistics
 //                           streamed through LDS over rows t >= first key; weights
 //                           2^(x - M_t) / L_t summed per key in a fixed order -> s_j.
 //   3. h2o_topk_kernel      per (batch row, KV head): exact selection of the heavy
@@ -35,6 +35,13 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+#ifndef LCD_H2OP_TW
+#define LCD_H2OP_TW 1  // register tiles per wave at D <= 128
+#endif
+#ifndef LCD_H2OP_BT
+#define LCD_H2OP_BT 2  // 32-row tiles per staged block at D <= 128
+#endif
+
 constexpr int kThreads = 256;
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / 64;
@@ -42,6 +49,11 @@ constexpr int kMaxChunks = 256;  // prompt chunks of kTopkThreads positions: N <
 constexpr int kDigitBits = 11;
 constexpr int kBins = 1 << kDigitBits;
 constexpr int kHistCopies = 4;
+
+// 2^x with the hardware instruction (v_exp_f32).  Arguments here are <= 0 (logit minus
+// its row maximum); results below 2^-126, which the instruction may flush to zero, are
+// negligible against the row sums they join.
+__device__ inline float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ inline bf16x8 frag_global(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
@@ -55,31 +67,6 @@ template <int D>
 constexpr int tile_row_bytes() { return 2 * D + 16; }
 template <int D>
 constexpr int tile_bytes() { return 32 * tile_row_bytes<D>(); }
-template <int D>
-constexpr int tile_pieces_per_thread() { return 32 * D * 2 / 16 / kThreads; }  // 16-byte pieces
-
-// Global -> registers for one 32-row tile (rows past n read as zero).
-template <int D>
-__device__ inline void tile_load(const uint16_t* base, int row0, int n, uint4 (&r)[tile_pieces_per_thread<D>()]) {
-  constexpr int PPR = D * 2 / 16;  // pieces per row
-#pragma unroll
-  for (int i = 0; i < tile_pieces_per_thread<D>(); ++i) {
-    const int piece = i * kThreads + (int)threadIdx.x;
-    const int row = piece / PPR, col = piece % PPR;
-    r[i] = row0 + row < n ? *reinterpret_cast<const uint4*>(base + (size_t)(row0 + row) * D + col * 8)
-                          : make_uint4(0, 0, 0, 0);
-  }
-}
-
-template <int D>
-__device__ inline void tile_store(char* lds, const uint4 (&r)[tile_pieces_per_thread<D>()]) {
-  constexpr int PPR = D * 2 / 16;
-#pragma unroll
-  for (int i = 0; i < tile_pieces_per_thread<D>(); ++i) {
-    const int piece = i * kThreads + (int)threadIdx.x;
-    *reinterpret_cast<uint4*>(lds + (piece / PPR) * tile_row_bytes<D>() + (piece % PPR) * 16) = r[i];
-  }
-}
 
 // Fragment of k-step s: row lane % 32, elements 16 s + 8 (lane / 32) .. + 7.
 template <int D>
@@ -92,220 +79,294 @@ __device__ inline bf16x8 frag_lds(const char* lds, int s, int lane) {
 // B-column lane % 32 (the prompt row).
 __device__ inline int c_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
-// Row tiles per wave in pass 1: the Q fragments of TPW tiles stay in registers.
+// Keys (pass 1) or rows (pass 2) staged per iteration: four 32-row tiles for D = 64, two
+// otherwise (LDS buffers within 2 x 34 KiB, prefetch registers within 32 VGPRs).  With
+// two register tiles per wave (D <= 128) every iteration gives each wave 32 MFMAs (16
+// at D = 256, each twice as long), enough to cover the global loads issued one
+// iteration ahead.
 template <int D>
-constexpr int rows_tiles_per_wave() { return D == 64 ? 4 : (D == 128 ? 2 : 1); }
+constexpr int block_tiles() { return D == 256 ? 2 : LCD_H2OP_BT; }
+template <int D>
+constexpr int block_rows() { return 32 * block_tiles<D>(); }
+template <int D>
+constexpr int block_bytes() { return block_rows<D>() * tile_row_bytes<D>(); }
+template <int D>
+constexpr int block_pieces_per_thread() { return block_rows<D>() * D * 2 / 16 / kThreads; }
+
+// Global -> registers for one block of rows (rows past n read as zero).
+template <int D>
+__device__ inline void block_load(const uint16_t* base, int row0, int n, uint4 (&r)[block_pieces_per_thread<D>()]) {
+  constexpr int PPR = D * 2 / 16;  // pieces per row
+#pragma unroll
+  for (int i = 0; i < block_pieces_per_thread<D>(); ++i) {
+    const int piece = i * kThreads + (int)threadIdx.x;
+    const int row = piece / PPR, col = piece % PPR;
+    r[i] = row0 + row < n ? *reinterpret_cast<const uint4*>(base + (size_t)(row0 + row) * D + col * 8)
+                          : make_uint4(0, 0, 0, 0);
+  }
+}
+
+template <int D>
+__device__ inline void block_store(char* lds, const uint4 (&r)[block_pieces_per_thread<D>()]) {
+  constexpr int PPR = D * 2 / 16;
+#pragma unroll
+  for (int i = 0; i < block_pieces_per_thread<D>(); ++i) {
+    const int piece = i * kThreads + (int)threadIdx.x;
+    *reinterpret_cast<uint4*>(lds + (piece / PPR) * tile_row_bytes<D>() + (piece % PPR) * 16) = r[i];
+  }
+}
+
+// Row (pass 1) or key (pass 2) tiles a wave keeps in registers: every fragment read from
+// LDS then feeds that many MFMAs, which keeps the LDS reads below the MFMA rate.
+template <int D>
+constexpr int wave_tiles() { return D == 256 ? 1 : LCD_H2OP_TW; }
 
 // ------------------------------------------------------------------ 1. row statistics
+// Workgroup: 4 * 32 * TW prompt rows of one query head (Q fragments in registers).
+// Iteration: a block of keys staged in LDS; each wave multiplies its rows with every key
+// tile of the block (MFMA), then folds each tile into its rows' running (max, sum).
 template <int D>
-__global__ void __launch_bounds__(kThreads) h2o_rowstats_kernel(H2oPromptParams p) {
-  constexpr int TPW = rows_tiles_per_wave<D>();
-  constexpr int RB = 4 * TPW * 32;  // prompt rows per workgroup
-  constexpr int KS = D / 16;        // MFMA k-steps
-  __shared__ __attribute__((aligned(16))) char ktile[2][tile_bytes<D>()];
+__global__ void __launch_bounds__(kThreads, 2) h2o_rowstats_kernel(H2oPromptParams p) {
+  constexpr int KS = D / 16;  // MFMA k-steps
+  constexpr int BT = block_tiles<D>(), BR = block_rows<D>();
+  constexpr int TW = wave_tiles<D>();
+  constexpr int WR = 4 * 32 * TW;  // rows per workgroup
+  __shared__ __attribute__((aligned(16))) char kblk[2][block_bytes<D>()];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int blk = (int)gridDim.x - 1 - (int)blockIdx.x;  // longest causal ranges first
   const int h = blockIdx.y, b = blockIdx.z, g = h / (p.Hq / p.Hkv);
-  const int P0 = blk * RB;
+  const int r0 = blk * WR + wave * 32 * TW;  // the wave's first row
   const uint16_t* Q = reinterpret_cast<const uint16_t*>(p.q) + ((size_t)b * p.Hq + h) * p.N * D;
   const uint16_t* K = reinterpret_cast<const uint16_t*>(p.k) + ((size_t)b * p.Hkv + g) * p.N * D;
 
-  bf16x8 qf[TPW][KS];
-  float m[TPW], l[TPW];
+  bf16x8 qf[TW][KS];
+  float m[TW], l[TW];
 #pragma unroll
-  for (int i = 0; i < TPW; ++i) {
-    const int row = P0 + (wave * TPW + i) * 32 + (lane & 31);
+  for (int i = 0; i < TW; ++i) {
+    const int row = r0 + i * 32 + (lane & 31);
 #pragma unroll
     for (int s = 0; s < KS; ++s)
       qf[i][s] = row < p.N ? frag_global(Q + (size_t)row * D + 16 * s + 8 * (lane >> 5)) : frag_zero();
     m[i] = -INFINITY;
     l[i] = 0.f;
   }
-  const int n_keys = min(p.N, P0 + RB);
-  const int n_tiles = (n_keys + 31) / 32;
-  uint4 raw[tile_pieces_per_thread<D>()];
-  tile_load<D>(K, 0, p.N, raw);
-  tile_store<D>(ktile[0], raw);
-  for (int kt = 0; kt < n_tiles; ++kt) {
-    if (kt + 1 < n_tiles) tile_load<D>(K, (kt + 1) * 32, p.N, raw);
-    __syncthreads();  // tile kt is in ktile[kt & 1]; every wave is done with tile kt - 1
-    const char* kl = ktile[kt & 1];
-    // row tiles that see some key of this tile (wave-uniform)
-    bool act[TPW];
+  const int n_keys = min(p.N, blk * WR + WR);
+  const int n_blocks = (n_keys + BR - 1) / BR;
+  // blocks are loaded two iterations ahead into alternating register sets (named, so
+  // they stay in registers), stored to LDS one iteration ahead
+  uint4 rawA[block_pieces_per_thread<D>()], rawB[block_pieces_per_thread<D>()];
+  auto step = [&](int kb, uint4 (&load_into)[block_pieces_per_thread<D>()],
+                  const uint4 (&store_from)[block_pieces_per_thread<D>()]) {
+    if (kb + 2 < n_blocks) block_load<D>(K, (kb + 2) * BR, p.N, load_into);
+    __syncthreads();  // block kb is in kblk[kb & 1]; every wave is done with block kb - 1
+    const char* kl = kblk[kb & 1];
+    const int k0 = kb * BR;
+    // (key tile, row tile) pairs the wave computes: some key of the tile is <= some row
+    bool act[BT][TW];
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      const int r0 = P0 + (wave * TPW + i) * 32;
-      act[i] = kt * 32 <= r0 + 31 && r0 < p.N;
-    }
-    f32x16 acc[TPW];
+    for (int t = 0; t < BT; ++t)
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) acc[i] = f32x16{};
-    // each K fragment is read from LDS once and used for every row tile
+      for (int i = 0; i < TW; ++i) act[t][i] = r0 + i * 32 < p.N && k0 + t * 32 <= r0 + i * 32 + 31;
+    // every MFMA of the block first (independent accumulators), then the folds
+    f32x16 acc[BT][TW];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const bf16x8 a = frag_lds<D>(kl, s, lane);
+    for (int t = 0; t < BT; ++t)
 #pragma unroll
-      for (int i = 0; i < TPW; ++i)
-        if (act[i]) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[i][s], acc[i], 0, 0, 0);
-    }
+      for (int i = 0; i < TW; ++i) acc[t][i] = f32x16{};
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      if (!act[i]) continue;
-      const int r0 = P0 + (wave * TPW + i) * 32;
-      // keys past N sit in the tile only when the tile holds the last key, which is
-      // the diagonal case; there key <= row < N masks them too
-      const bool full = kt * 32 + 31 <= r0;  // every key <= every row (wave-uniform)
-      const int dlt = r0 + (lane & 31) - kt * 32;
-      float x[16], bm = -INFINITY;
+    for (int s = 0; s < KS; ++s)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        x[r] = full || c_row(r, lane) <= dlt ? acc[i][r] * p.qscale : -INFINITY;
-        bm = fmaxf(bm, x[r]);
+      for (int t = 0; t < BT; ++t) {
+        if (!(act[t][0] || act[t][TW - 1])) continue;
+        const bf16x8 a = frag_lds<D>(kl + t * tile_bytes<D>(), s, lane);
+#pragma unroll
+        for (int i = 0; i < TW; ++i)
+          if (act[t][i]) acc[t][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[i][s], acc[t][i], 0, 0, 0);
       }
-      const float mn = fmaxf(m[i], bm);
+    // fold the block into each row's (max, sum): the maximum on the raw products (the
+    // scale is positive), masked keys set to -inf, then 2^(acc * scale - max)
+#pragma unroll
+    for (int i = 0; i < TW; ++i) {
+      const int ri = r0 + i * 32;
+      float bm = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < BT; ++t) {
+        if (!act[t][i]) continue;
+        const int kt0 = k0 + t * 32;
+        if (kt0 + 31 > ri) {  // the diagonal tile: key <= row <=> c_row <= row - first key
+          const int dlt = ri + (lane & 31) - kt0;
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (c_row(r, lane) > dlt) acc[t][i][r] = -INFINITY;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) bm = fmaxf(bm, acc[t][i][r]);
+      }
+      const float mn = fmaxf(m[i], bm * p.qscale);
       if (mn > -INFINITY) {
         float add = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) add += exp2f(x[r] - mn);
-        l[i] = l[i] * exp2f(m[i] - mn) + add;
+        for (int t = 0; t < BT; ++t) {
+          if (!act[t][i]) continue;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) add += exp2_hw(fmaf(acc[t][i][r], p.qscale, -mn));
+        }
+        l[i] = l[i] * exp2_hw(m[i] - mn) + add;
         m[i] = mn;
       }
     }
-    if (kt + 1 < n_tiles) tile_store<D>(ktile[(kt + 1) & 1], raw);
+    if (kb + 1 < n_blocks) block_store<D>(kblk[(kb + 1) & 1], store_from);
+  };
+  block_load<D>(K, 0, p.N, rawA);
+  if (n_blocks > 1) block_load<D>(K, BR, p.N, rawB);
+  block_store<D>(kblk[0], rawA);
+  for (int kb = 0; kb < n_blocks; kb += 2) {
+    step(kb, rawA, rawB);
+    if (kb + 1 >= n_blocks) break;
+    step(kb + 1, rawB, rawA);
   }
   // lanes l and l ^ 32 hold the same row (the two halves of every key tile)
 #pragma unroll
-  for (int i = 0; i < TPW; ++i) {
+  for (int i = 0; i < TW; ++i) {
     const float mo = __shfl_xor(m[i], 32, 64), lo = __shfl_xor(l[i], 32, 64);
     const float M = fmaxf(m[i], mo);
-    const float L = (m[i] > -INFINITY ? l[i] * exp2f(m[i] - M) : 0.f) + (mo > -INFINITY ? lo * exp2f(mo - M) : 0.f);
-    const int row = P0 + (wave * TPW + i) * 32 + (lane & 31);
+    const float Lsum = (m[i] > -INFINITY ? l[i] * exp2f(m[i] - M) : 0.f) + (mo > -INFINITY ? lo * exp2f(mo - M) : 0.f);
+    const int row = r0 + i * 32 + (lane & 31);
     if (lane < 32 && row < p.N) {
       float2* st = reinterpret_cast<float2*>(p.rowstat) + ((size_t)b * p.Hq + h) * p.N + row;
-      *st = make_float2(M, 1.f / L);
+      *st = make_float2(M, 1.f / Lsum);
     }
   }
 }
 
 // ------------------------------------------------------------------ 2. column sums
-// Key tiles per wave in pass 2: the K fragments of KT tiles stay in registers, and each
-// Q fragment read from LDS serves all of them.
-template <int D>
-constexpr int key_tiles_per_wave() { return D == 64 ? 4 : (D == 128 ? 2 : 1); }
-template <int D>
-constexpr int col_keys() { return 4 * 32 * key_tiles_per_wave<D>(); }  // keys per workgroup
-
+// Workgroup: 4 * 32 * TW keys of one KV head (K fragments in registers).
+// Iteration: a block of prompt rows of one query head of the group (Q rows and their
+// statistics staged in LDS), rows from the workgroup's first key to the end; each wave
+// adds the weights 2^(x - M_t) / L_t of its keys over the block's rows.
 template <int D>
 __global__ void __launch_bounds__(kThreads, 2) h2o_colsum_kernel(H2oPromptParams p) {
   constexpr int KS = D / 16;
-  __shared__ __attribute__((aligned(16))) char qtile[2][tile_bytes<D>()];
-  __shared__ float2 qstat[2][32];
+  constexpr int BT = block_tiles<D>(), BR = block_rows<D>();
+  constexpr int TW = wave_tiles<D>();
+  constexpr int WK = 4 * 32 * TW;  // keys per workgroup
+  __shared__ __attribute__((aligned(16))) char qblk[2][block_bytes<D>()];
+  __shared__ float2 qstat[2][BR];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int kb = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int G = p.Hq / p.Hkv;
-  constexpr int KT = key_tiles_per_wave<D>();
-  const int kblk0 = kb * col_keys<D>();
-  const int key0 = kblk0 + wave * KT * 32;  // the wave's first key
+  const int key0 = kb * WK + wave * 32 * TW;  // the wave's first key
   const uint16_t* K = reinterpret_cast<const uint16_t*>(p.k) + ((size_t)b * p.Hkv + g) * p.N * D;
-  bf16x8 kf[KT][KS];
+  bf16x8 kf[TW][KS];
 #pragma unroll
-  for (int t = 0; t < KT; ++t) {
-    const int key = key0 + t * 32 + (lane & 31);
+  for (int i = 0; i < TW; ++i) {
+    const int key = key0 + i * 32 + (lane & 31);
 #pragma unroll
     for (int s = 0; s < KS; ++s)
-      kf[t][s] = key < p.N ? frag_global(K + (size_t)key * D + 16 * s + 8 * (lane >> 5)) : frag_zero();
+      kf[i][s] = key < p.N ? frag_global(K + (size_t)key * D + 16 * s + 8 * (lane >> 5)) : frag_zero();
   }
-  float col[KT][16];
+  float col[TW][16];
 #pragma unroll
-  for (int t = 0; t < KT; ++t)
+  for (int i = 0; i < TW; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) col[t][r] = 0.f;
+    for (int r = 0; r < 16; ++r) col[i][r] = 0.f;
 
-  // work units: (row tile, head) for row tiles from the block's first key to the end
-  const int t_first = kblk0 / 32;
-  const int n_rt = (p.N + 31) / 32;
-  const int units = (n_rt - t_first) * G;
-  auto unit_src = [&](int u, const uint16_t** q, const float2** st, int* row0) {
-    const int rt = t_first + u / G, j = u % G;
-    const size_t bh = (size_t)b * p.Hq + g * G + j;
-    *q = reinterpret_cast<const uint16_t*>(p.q) + bh * p.N * D;
-    *st = reinterpret_cast<const float2*>(p.rowstat) + bh * p.N;
-    *row0 = rt * 32;
+  // units: (row block, head j) from the row block holding the workgroup's first key
+  const int rb_first = (kb * WK) / BR;
+  const int n_rb = (p.N + BR - 1) / BR;
+  const int units = (n_rb - rb_first) * G;
+  // units are loaded two iterations ahead into alternating register sets (named, so
+  // they stay in registers), stored to LDS one iteration ahead
+  constexpr int P = block_pieces_per_thread<D>();
+  uint4 rawA[P], rawB[P];
+  float2 sA = make_float2(0.f, 0.f), sB = make_float2(0.f, 0.f);
+  auto load_unit = [&](int u, uint4 (&raw)[P], float2& sraw) {
+    const int row0 = (rb_first + u / G) * BR;
+    const size_t bh = (size_t)b * p.Hq + g * G + u % G;
+    block_load<D>(reinterpret_cast<const uint16_t*>(p.q) + bh * p.N * D, row0, p.N, raw);
+    if ((int)threadIdx.x < BR)
+      sraw = row0 + (int)threadIdx.x < p.N ? reinterpret_cast<const float2*>(p.rowstat)[bh * p.N + row0 + threadIdx.x]
+                                           : make_float2(0.f, 0.f);
   };
-  uint4 raw[tile_pieces_per_thread<D>()];
-  float2 sraw = make_float2(0.f, 0.f);
-  {
-    const uint16_t* q;
-    const float2* st;
-    int row0;
-    unit_src(0, &q, &st, &row0);
-    tile_load<D>(q, row0, p.N, raw);
-    if (threadIdx.x < 32) sraw = row0 + (int)threadIdx.x < p.N ? st[row0 + threadIdx.x] : make_float2(0.f, 0.f);
-    tile_store<D>(qtile[0], raw);
-    if (threadIdx.x < 32) qstat[0][threadIdx.x] = sraw;
-  }
-  for (int u = 0; u < units; ++u) {
-    const uint16_t* qn = nullptr;
-    const float2* stn = nullptr;
-    int row0n = 0;
-    if (u + 1 < units) {
-      unit_src(u + 1, &qn, &stn, &row0n);
-      tile_load<D>(qn, row0n, p.N, raw);
-      if (threadIdx.x < 32) sraw = row0n + (int)threadIdx.x < p.N ? stn[row0n + threadIdx.x] : make_float2(0.f, 0.f);
-    }
+  auto store_unit = [&](int buf, const uint4 (&raw)[P], float2 sraw) {
+    block_store<D>(qblk[buf], raw);
+    if ((int)threadIdx.x < BR) qstat[buf][threadIdx.x] = sraw;
+  };
+  auto step = [&](int u, uint4 (&load_into)[P], float2& s_into, const uint4 (&store_from)[P], float2 s_from) {
+    if (u + 2 < units) load_unit(u + 2, load_into, s_into);
     __syncthreads();  // unit u is in buffer u & 1; every wave is done with unit u - 1
-    const int row0 = (t_first + u / G) * 32;
-    const char* ql = qtile[u & 1];
-    bool act[KT];
+    const int row0 = (rb_first + u / G) * BR;
+    const char* ql = qblk[u & 1];
+    // (row tile, key tile) pairs the wave computes: some row of the tile sees some key
+    bool act[BT][TW];
 #pragma unroll
-    for (int t = 0; t < KT; ++t) act[t] = row0 + 31 >= key0 + t * 32 && key0 + t * 32 < p.N;
-    f32x16 acc[KT];
+    for (int t = 0; t < BT; ++t)
 #pragma unroll
-    for (int t = 0; t < KT; ++t) acc[t] = f32x16{};
+      for (int i = 0; i < TW; ++i) act[t][i] = key0 + i * 32 < p.N && row0 + t * 32 + 31 >= key0 + i * 32;
+    f32x16 acc[BT][TW];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const bf16x8 bq = frag_lds<D>(ql, s, lane);
+    for (int t = 0; t < BT; ++t)
 #pragma unroll
-      for (int t = 0; t < KT; ++t)
-        if (act[t]) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t][s], bq, acc[t], 0, 0, 0);
-    }
-    const float2 st = qstat[u & 1][lane & 31];  // rows past N carry (0, 0): weight 0
+      for (int i = 0; i < TW; ++i) acc[t][i] = f32x16{};
 #pragma unroll
-    for (int t = 0; t < KT; ++t) {
-      if (!act[t]) continue;
-      if (row0 >= key0 + t * 32 + 31) {  // every key of the tile is <= every row (wave-uniform)
+    for (int s = 0; s < KS; ++s)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) col[t][r] += exp2f(acc[t][r] * p.qscale - st.x) * st.y;
-      } else {  // the diagonal tile: key <= row <=> c_row <= row - first key
-        const int dlt = row0 + (lane & 31) - (key0 + t * 32);
+      for (int t = 0; t < BT; ++t) {
+        if (!(act[t][0] || act[t][TW - 1])) continue;
+        const bf16x8 bq = frag_lds<D>(ql + t * tile_bytes<D>(), s, lane);
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          col[t][r] += c_row(r, lane) <= dlt ? exp2f(acc[t][r] * p.qscale - st.x) * st.y : 0.f;
+        for (int i = 0; i < TW; ++i)
+          if (act[t][i]) acc[t][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i][s], bq, acc[t][i], 0, 0, 0);
+      }
+#pragma unroll
+    for (int t = 0; t < BT; ++t) {
+      const float2 st = qstat[u & 1][t * 32 + (lane & 31)];  // rows past N carry (0, 0): weight 0
+      const int rt0 = row0 + t * 32;
+#pragma unroll
+      for (int i = 0; i < TW; ++i) {
+        if (!act[t][i]) continue;
+        const int ki = key0 + i * 32;
+        if (rt0 >= ki + 31) {  // every key of the tile is <= every row (wave-uniform)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) col[i][r] = fmaf(exp2_hw(fmaf(acc[t][i][r], p.qscale, -st.x)), st.y, col[i][r]);
+        } else {  // the diagonal: key <= row <=> c_row <= row - first key
+          const int dlt = rt0 + (lane & 31) - ki;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float e = exp2_hw(fmaf(acc[t][i][r], p.qscale, -st.x));
+            col[i][r] = c_row(r, lane) <= dlt ? fmaf(e, st.y, col[i][r]) : col[i][r];
+          }
+        }
       }
     }
-    if (u + 1 < units) {
-      tile_store<D>(qtile[(u + 1) & 1], raw);
-      if (threadIdx.x < 32) qstat[(u + 1) & 1][threadIdx.x] = sraw;
-    }
+    if (u + 1 < units) store_unit((u + 1) & 1, store_from, s_from);
+  };
+  load_unit(0, rawA, sA);
+  if (units > 1) load_unit(1, rawB, sB);
+  store_unit(0, rawA, sA);
+  for (int u = 0; u < units; u += 2) {
+    step(u, rawA, sA, rawB, sB);
+    if (u + 1 >= units) break;
+    step(u + 1, rawB, sB, rawA, sA);
   }
   // lanes of one half (lane / 32 fixed) hold the same 16 keys for different rows
 #pragma unroll
-  for (int t = 0; t < KT; ++t)
+  for (int i = 0; i < TW; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float x = col[t][r];
+      float x = col[i][r];
 #pragma unroll
       for (int off = 1; off < 32; off <<= 1) x += __shfl_xor(x, off, 64);
-      col[t][r] = x;
+      col[i][r] = x;
     }
   if ((lane & 31) == 0) {
-    float* s = p.scores + ((size_t)b * p.Hkv + g) * p.N;
+    float* sc = p.scores + ((size_t)b * p.Hkv + g) * p.N;
 #pragma unroll
-    for (int t = 0; t < KT; ++t)
+    for (int i = 0; i < TW; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = key0 + t * 32 + c_row(r, lane);
-        if (key < p.N) s[key] = col[t][r];
+        const int key = key0 + i * 32 + c_row(r, lane);
+        if (key < p.N) sc[key] = col[i][r];
       }
   }
 }
@@ -513,10 +574,10 @@ __global__ void __launch_bounds__(kThreads) h2o_gather_kernel(H2oPromptParams p)
 
 template <int D>
 hipError_t launch_d(const H2oPromptParams& p, hipStream_t s) {
-  constexpr int RB = 4 * rows_tiles_per_wave<D>() * 32;
-  hipLaunchKernelGGL(h2o_rowstats_kernel<D>, dim3((p.N + RB - 1) / RB, p.Hq, p.B), dim3(kThreads), 0, s, p);
-  hipLaunchKernelGGL(h2o_colsum_kernel<D>, dim3((p.N + col_keys<D>() - 1) / col_keys<D>(), p.Hkv, p.B),
-                     dim3(kThreads), 0, s, p);
+  constexpr int W = 4 * 32 * wave_tiles<D>();  // rows / keys per workgroup
+  const int wgs = (p.N + W - 1) / W;
+  hipLaunchKernelGGL(h2o_rowstats_kernel<D>, dim3(wgs, p.Hq, p.B), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL(h2o_colsum_kernel<D>, dim3(wgs, p.Hkv, p.B), dim3(kThreads), 0, s, p);
   hipLaunchKernelGGL(h2o_topk_kernel, dim3(p.B * p.Hkv), dim3(kTopkThreads), 0, s, p);
   const int rows = p.budget < p.N ? p.budget : p.N;
   const int blocks = (rows * (D * 2 / 16) + kThreads - 1) / kThreads;
