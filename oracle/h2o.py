@@ -95,3 +95,71 @@ def h2o_prompt_select(Q, K, budget: int, n_recent: int, scale=None):
     order = sorted(range(old), key=lambda j: (-float(s32[j]), j))
     keep = sorted(order[: budget - n_recent]) + list(range(old, T))
     return np.array(keep, dtype=np.int64), s
+
+
+class H2OBlockHead:
+    """Block-level H2O cache of one (batch row, KV head): [KVC] "Implementação prática em
+    vLLM e SGLang" — memory is managed in blocks of 16 or 32 tokens, a block's score is the
+    sum of its tokens' accumulated attention, Score(B_k) = sum_{t in B_k} s_t, and when
+    memory runs out the lowest-scoring blocks are freed whole (and reused, no copies).
+
+    Readings:
+    * The budget is ``n_blocks`` blocks of ``block_size`` tokens.  Tokens fill an open
+      block in arrival order; a new block is needed when the open one is full.  While the
+      budget allows, a fresh block is opened; at the budget the lowest-scoring block is
+      freed first and becomes the new open block.
+    * A block is an eviction candidate only if none of its tokens is among the n_recent
+      newest (positions <= t - n_recent for the arriving token t, as in H2OHead).  Its
+      score is the float64 sum of its tokens' s, decided in float32; ties free the block
+      holding the newer token.
+    * Step order, scores and GQA as in H2OHead.
+    """
+
+    def __init__(self, n_blocks: int, block_size: int, n_recent: int):
+        if n_blocks < 2 or block_size < 1 or not 0 < n_recent <= (n_blocks - 1) * block_size:
+            raise ValueError("need >= 2 blocks and 0 < n_recent <= (n_blocks - 1) * block_size")
+        self.n_blocks, self.block_size, self.n_recent = int(n_blocks), int(block_size), int(n_recent)
+        self.blocks = []  # each: dict(pos=[...], k=[...], v=[...], s=[...]); the last is the open block
+
+    def tokens(self):
+        return [p for blk in self.blocks for p in blk["pos"]]
+
+    def block_score(self, blk) -> float:
+        return float(np.float32(sum(blk["s"])))
+
+    def victim_block(self, t: int) -> int:
+        """Index of the block freed before writing token ``t`` (budget full, open block full)."""
+        cands = [i for i, blk in enumerate(self.blocks) if max(blk["pos"]) <= t - self.n_recent]
+        if not cands:
+            raise ValueError("no eviction candidate")
+        return min(cands, key=lambda i: (self.block_score(self.blocks[i]), -max(self.blocks[i]["pos"])))
+
+    def step(self, t: int, q: np.ndarray, k_t: np.ndarray, v_t: np.ndarray, scale=None):
+        """Decode token ``t`` with queries q[G][D]; returns (out[G][D], freed positions or None)."""
+        q = np.asarray(q, np.float64)
+        freed = None
+        if not self.blocks or len(self.blocks[-1]["pos"]) == self.block_size:
+            if len(self.blocks) == self.n_blocks:
+                i = self.victim_block(t)
+                freed = list(self.blocks[i]["pos"])
+                del self.blocks[i]
+            self.blocks.append(dict(pos=[], k=[], v=[], s=[]))
+        blk = self.blocks[-1]
+        blk["pos"].append(int(t))
+        blk["k"].append(np.asarray(k_t, np.float64))
+        blk["v"].append(np.asarray(v_t, np.float64))
+        blk["s"].append(0.0)
+        K = np.stack([x for b in self.blocks for x in b["k"]])
+        V = np.stack([x for b in self.blocks for x in b["v"]])
+        sc = 1.0 / np.sqrt(q.shape[-1]) if scale is None else float(scale)
+        out = np.empty((q.shape[0], V.shape[1]))
+        weights = np.zeros(K.shape[0])
+        for h in range(q.shape[0]):
+            out[h], p = attend_one(q[h], K, V, sc)
+            weights += p
+        j = 0
+        for b in self.blocks:
+            for e in range(len(b["s"])):
+                b["s"][e] += weights[j]
+                j += 1
+        return out, freed

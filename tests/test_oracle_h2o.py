@@ -119,3 +119,69 @@ def test_prompt_selection_pins():
     assert list(keep[-3:]) == [17, 18, 19] and len(keep) == 8
     top = np.lexsort((np.arange(17), -ref[:17].astype(np.float32)))[:5]
     assert sorted(top) == list(keep[:5])
+
+
+# ---------------------------------------------------------------- block-level eviction
+def _bstream(T, G, D, seed):
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal((T, G, D)), rng.standard_normal((T, D)), rng.standard_normal((T, D))
+
+
+def test_block_size_one_is_token_level_h2o():
+    """With blocks of one token, block eviction is H2O's token eviction (no recent block
+    can be a candidate either way)."""
+    T, G, D, C, R = 60, 2, 8, 12, 3
+    Q, K, V = _bstream(T, G, D, 11)
+    a, b = oracle.H2OHead(C, R), oracle.H2OBlockHead(C, 1, R)
+    for t in range(T):
+        oa, ea = a.step(t, Q[t], K[t], V[t])
+        ob, eb = b.step(t, Q[t], K[t], V[t])
+        np.testing.assert_allclose(oa, ob, rtol=1e-12, atol=1e-12)
+        assert (ea is None and eb is None) or [ea] == eb
+        assert sorted(a.pos) == sorted(b.tokens())
+
+
+def test_block_eviction_frees_whole_blocks_by_summed_score():
+    """Literal pin of the rule: at each boundary with the budget full, the freed block is
+    the candidate with the smallest float32 sum of its tokens' s (ties: newer block),
+    computed here from a separately tracked per-token score table."""
+    T, G, D, NB, BS, R = 120, 2, 8, 4, 8, 5
+    Q, K, V = _bstream(T, G, D, 12)
+    head = oracle.H2OBlockHead(NB, BS, R)
+    s_tab = {}  # position -> accumulated weight, tracked independently
+    for t in range(T):
+        before = [list(b["pos"]) for b in head.blocks]
+        out, freed = head.step(t, Q[t], K[t], V[t])
+        toks = head.tokens()
+        assert len(toks) <= NB * BS and len(head.blocks) <= NB
+        if freed is not None:
+            cands = [blk for blk in before if max(blk) <= t - R]
+            want = min(cands, key=lambda blk: (float(np.float32(sum(s_tab[p] for p in blk))), -max(blk)))
+            assert freed == want and len(freed) == BS
+            for p in freed:
+                del s_tab[p]
+        # brute-force attention over the cached tokens and the score update
+        Ks, Vs = K[toks], V[toks]
+        w = np.zeros(len(toks))
+        for h in range(G):
+            x = Ks @ Q[t, h] / np.sqrt(D)
+            a = np.exp(x - x.max())
+            a /= a.sum()
+            np.testing.assert_allclose(out[h], a @ Vs, rtol=1e-12, atol=1e-12)
+            w += a
+        s_tab[t] = 0.0
+        for p, x in zip(toks, w):
+            s_tab[p] += x
+    # blocks fill in arrival order; once the budget is reached every boundary frees one block
+    assert len(head.blocks) == NB
+
+
+def test_block_recent_protection():
+    """The blocks holding any of the n_recent newest tokens are never freed."""
+    T, G, D, NB, BS, R = 90, 1, 4, 3, 8, 9  # 9 recent tokens span two blocks at each boundary
+    Q, K, V = _bstream(T, G, D, 13)
+    head = oracle.H2OBlockHead(NB, BS, R)
+    for t in range(T):
+        _, freed = head.step(t, Q[t], K[t], V[t])
+        if freed is not None:
+            assert max(freed) <= t - R
