@@ -13,8 +13,8 @@ of back-to-back decode_attn launches), the decode kernel's counter-measured HBM 
 when the record under profiles/ matches the current kernel sources, the SnapKV
 compression time, the H2O prompt-phase compression time and MFMA rate, secondary decode
 workloads
-(the 16-layer GQA 32k cache, the H2O 4096 budget, the DuoAttention 128k mixed-head
-layer, the tiny fp32 stream) unless
+(the 16-layer GQA 32k cache, the H2O 4096 budget with token- and block-level eviction,
+the DuoAttention 128k mixed-head layer, the tiny fp32 stream) unless
 --only, and the fp64 CPU oracle timed on a bounded sample of the headline step.
 """
 from __future__ import annotations
@@ -31,8 +31,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK = 8.0e12  # B/s, MI355X HBM3E
 MFMA_BF16_PEAK = 2.5e15  # flop/s, dense
 METRIC = "decode steps/s + achieved HBM TB/s (% of peak); SnapKV compress ms"
-DEFAULTS = {"llama2_7b_layer": (8192, 64), "gqa_long": (64, 4), "h2o_128k": (1024, 32), "duo_128k": (192, 16),
-            "tiny_streaming": (448, 64)}
+DEFAULTS = {"llama2_7b_layer": (8192, 64), "gqa_long": (64, 4), "h2o_128k": (1024, 32),
+            "h2o_blocks_128k": (1024, 32), "duo_128k": (192, 16), "tiny_streaming": (448, 64)}
 
 
 def _parse(argv=None):
@@ -210,7 +210,7 @@ class _Stepper:
             from synth.workloads import h2o_state_torch
 
             cfg = L.cache_config(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, dt, L.LCD_H2O,
-                                 capacity=w.budget, n_recent=w.n_recent)
+                                 capacity=w.budget, n_recent=w.n_recent, block_size=w.block_size)
             self.cache = L.KVCache(cfg, device=dev)
             K, V, P, S = h2o_state_torch(w, dev)
             kv, vv = self.cache.layer_tensors(0)
@@ -253,6 +253,8 @@ class _Stepper:
         if w.kind == "h2o":
             logits = 2 * w.batch * w.n_q_heads * self.slots * 4  # written then read
             state = w.batch * w.n_kv_heads * self.slots * (4 + 4 + 4)  # score read+write, pos read
+            if w.block_size > 1:
+                state += w.batch * w.n_kv_heads * self.slots * 4  # positions read again to skip emptied slots
             return kv + io + logits + state
         return kv + io
 
@@ -491,7 +493,7 @@ def main(argv=None):
         line["h2o_prompt"] = _h2o_prompt_bench(L, WORKLOADS["h2o_prompt_128k"])
     if not a.only:
         others = []
-        for name in ("gqa_long", "h2o_128k", "duo_128k", "tiny_streaming"):
+        for name in ("gqa_long", "h2o_128k", "h2o_blocks_128k", "duo_128k", "tiny_streaming"):
             if name == a.workload:
                 continue
             s2, w2 = DEFAULTS[name]

@@ -111,6 +111,14 @@ typedef struct lcd_cache_config {
                           head, 0 = streaming head (n_kv_heads <= 128); read during
                           lcd_cache_sizes / lcd_kv_cache_init only (the handle keeps
                           a copy).  Ignored by the other policies (may be NULL).    */
+  int32_t block_size;  /* H2O: 0 or 1 = token-level eviction; 16 or 32 = block-level
+                          eviction ([KVC] "Implementação prática em vLLM e SGLang"):
+                          slots form blocks of block_size consecutive slots (capacity a
+                          multiple of it, n_recent <= capacity - block_size); tokens
+                          fill the open block, and when a full cache needs a new block
+                          the block with the lowest summed score among those holding
+                          none of the n_recent newest tokens (ties: the newer block) is
+                          freed whole and reused.  Ignored by the other policies.      */
 } lcd_cache_config;
 
 typedef struct lcd_cache lcd_cache; /* opaque host handle */

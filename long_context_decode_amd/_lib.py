@@ -32,7 +32,7 @@ class CacheConfig(ctypes.Structure):
                 ("policy", ctypes.c_int32), ("n_sink", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("capacity", ctypes.c_int32), ("n_recent", ctypes.c_int32), ("rope", ctypes.c_int32),
                 ("rope_base", ctypes.c_double), ("scale", ctypes.c_double),
-                ("retrieval", ctypes.POINTER(ctypes.c_int32))]
+                ("retrieval", ctypes.POINTER(ctypes.c_int32)), ("block_size", ctypes.c_int32)]
 
 
 class SnapkvParams(ctypes.Structure):
@@ -136,10 +136,10 @@ def _stream(stream):
 
 def cache_config(batch, n_q_heads, n_kv_heads, head_dim, dtype=LCD_BF16, policy=LCD_SINK_RING, n_layers=1,
                  n_sink=0, window=0, capacity=0, n_recent=0, rope=0, rope_base=10000.0, scale=0.0,
-                 retrieval=None):
+                 retrieval=None, block_size=0):
     """``retrieval``: DUO head kinds, [n_layers][n_kv_heads] of 0/1 (any nested sequence)."""
     cfg = CacheConfig(batch, n_layers, n_q_heads, n_kv_heads, head_dim, dtype, policy, n_sink, window,
-                      capacity, n_recent, rope, rope_base, scale, None)
+                      capacity, n_recent, rope, rope_base, scale, None, block_size)
     if retrieval is not None:
         flat = [int(x) for row in retrieval for x in row]
         arr = (ctypes.c_int32 * len(flat))(*flat)

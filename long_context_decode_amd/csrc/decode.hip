@@ -284,6 +284,38 @@ __device__ inline HeadView head_view(const DecodeParams& p, int b, int g) {
   return {reinterpret_cast<const char*>(p.k) + off, reinterpret_cast<const char*>(p.v) + off, p.n};
 }
 
+// H2O eviction candidates: folds one slot per lane (score s, position ps, in range) into
+// the running minimum of the u64 key (score bits << 32 | ~position): the lowest score,
+// ties to the newer token.  Token granule (bs <= 1): every slot with ps <= max_pos.
+// Blocks of bs = 16 or 32 slots (bs consecutive lanes, every lane active): the block's
+// summed score and newest position, a candidate only if all its slots hold tokens
+// with ps <= max_pos; lane 0 of the block folds it.  Scores are >= 0, so their bits
+// order like the values.
+__device__ inline void fold_victim(unsigned long long& best, float s, int ps, bool in, int64_t max_pos, int bs,
+                                   int lane) {
+  if (bs <= 1) {
+    if (in && (int64_t)ps <= max_pos) {
+      const unsigned long long key =
+          ((unsigned long long)__float_as_uint(s) << 32) | (unsigned long long)(0xffffffffu - (uint32_t)ps);
+      best = key < best ? key : best;
+    }
+    return;
+  }
+  float sum = in ? s : 0.f;
+  int mpos = in ? ps : -1;
+  int bad = (!in || ps < 0 || (int64_t)ps > max_pos) ? 1 : 0;
+  for (int off = 1; off < bs; off <<= 1) {
+    sum += __shfl_xor(sum, off, 64);
+    mpos = max(mpos, __shfl_xor(mpos, off, 64));
+    bad = max(bad, __shfl_xor(bad, off, 64));
+  }
+  if ((lane & (bs - 1)) == 0 && !bad) {
+    const unsigned long long key =
+        ((unsigned long long)__float_as_uint(sum) << 32) | (unsigned long long)(0xffffffffu - (uint32_t)mpos);
+    best = key < best ? key : best;
+  }
+}
+
 // ---------------------------------------------------------------- split finish
 // The end of a decode workgroup: ored[0 .. G*D) (LDS) holds its range's unnormalised
 // output and Mh / Lh (LDS) its maximum and sum per query head.  With one split the
@@ -351,14 +383,16 @@ __device__ inline void split_finish(const DecodeParams& p, const float* ored, co
 
   if constexpr (LOGITS) {
     // H2O: add this step's weights (summed over the group's query heads) to every
-    // filled slot's score and pick the slot the next append overwrites: the lowest
-    // score among slots with pos <= max_pos, ties evicting the higher position.
+    // filled slot's score and pick what the next append overwrites: the lowest score
+    // among slots (or blocks of slots) of tokens with pos <= max_pos, ties evicting the
+    // newer token.  The loop bound is wave-uniform so block reductions see whole waves.
     __shared__ unsigned long long wbest[4];
     float* score = p.score + bg * p.C;
     const int* pos = p.pos + bg * p.C;
     unsigned long long best = ~0ull;
     constexpr int EU = LCD_H2O_EU;  // slots per thread per iteration, all loads issued first
-    for (int i0 = threadIdx.x; i0 < p.n; i0 += kDecodeThreads * EU) {
+    for (int base = threadIdx.x - lane; base < p.n; base += kDecodeThreads * EU) {
+      const int i0 = base + lane;
       float x[EU][G], sc[EU];
       int ps[EU];
 #pragma unroll
@@ -373,17 +407,17 @@ __device__ inline void split_finish(const DecodeParams& p, const float* ored, co
 #pragma unroll
       for (int u = 0; u < EU; ++u) {
         const int i = i0 + u * kDecodeThreads;
-        if (i >= p.n) break;
-        float a = 0.f;
+        const bool in = i < p.n;
+        float snew = 0.f;
+        if (in) {
+          float a = 0.f;
 #pragma unroll
-        for (int j = 0; j < G; ++j) a += exp2f(x[u][j] - Mtot[j]) * Linv[j];
-        const float snew = sc[u] + a;
-        score[i] = snew;
-        if (p.pick_victim && (int64_t)ps[u] <= p.max_pos) {
-          const unsigned long long key = ((unsigned long long)__float_as_uint(snew) << 32) |
-                                         (unsigned long long)(0xffffffffu - (uint32_t)ps[u]);
-          best = key < best ? key : best;
+          for (int j = 0; j < G; ++j) a += exp2f(x[u][j] - Mtot[j]) * Linv[j];
+          snew = sc[u] + a;
+          score[i] = snew;
         }
+        if (p.pick_victim && base + u * kDecodeThreads < p.n)  // wave-uniform
+          fold_victim(best, snew, ps[u], in, p.max_pos, p.bs, lane);
       }
     }
     if (p.pick_victim) {
@@ -400,7 +434,7 @@ __device__ inline void split_finish(const DecodeParams& p, const float* ored, co
       if (best != ~0ull) {
         const int win_pos = (int)(0xffffffffu - (uint32_t)(best & 0xffffffffull));
         for (int i = threadIdx.x; i < p.n; i += kDecodeThreads)
-          if (pos[i] == win_pos) p.victim[bg] = i;
+          if (pos[i] == win_pos) p.victim[bg] = p.bs > 1 ? i / p.bs : i;
       }
     }
   }
@@ -507,6 +541,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_onepass_kernel(DecodePa
   struct Buf {
     Words<W> klo[U], khi[U], vlo[U], vhi[U];
     float c[NCS][HALF], sn[NCS][HALF];
+    int mp[U];  // H2O blocks: the slots' positions (< 0: empty)
   };
   auto load_iter = [&](int base, Buf& bf) {
     const int key0 = base + wave * KPW + kg;
@@ -519,7 +554,9 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_onepass_kernel(DecodePa
         bf.khi[u] = load_words<W>(kbase + roff + hi_off);
         bf.vlo[u] = load_words<W>(vbase + roff + lo_off);
         bf.vhi[u] = load_words<W>(vbase + roff + hi_off);
+        if constexpr (LOGITS) bf.mp[u] = p.mask_pos ? p.mask_pos[((size_t)b * p.Hkv + g) * p.C + s_begin + key] : 0;
       } else {
+        if constexpr (LOGITS) bf.mp[u] = -1;
         bf.klo[u] = zero_words<W>();
         bf.khi[u] = zero_words<W>();
         bf.vlo[u] = zero_words<W>();
@@ -611,14 +648,15 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_onepass_kernel(DecodePa
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int key = key0 + u * KPI;
-      const bool valid = key < cnt;
+      bool valid = key < cnt;
+      if constexpr (LOGITS) valid = valid && bf.mp[u] >= 0;
 #pragma unroll
       for (int j = 0; j < G; ++j) {
         d[u * G + j] = valid ? d[u * G + j] : -INFINITY;
         mn[j] = fmaxf(mn[j], d[u * G + j]);
       }
-      if constexpr (LOGITS) {
-        if (valid && sub == 0) {
+      if constexpr (LOGITS) {  // masked (empty) slots store -inf: their weight is 0
+        if (key < cnt && sub == 0) {
 #pragma unroll
           for (int j = 0; j < G; ++j)
             store_dev(&p.logits[((size_t)b * p.Hq + g * G + j) * p.C + s_begin + key], d[u * G + j]);
@@ -828,6 +866,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
   struct KBuf {
     Words<4> lo[U], hi[U];
     float c[NCS][HALF], sn[NCS][HALF];
+    int mp[U];  // H2O blocks: the slots' positions (< 0: empty)
   };
   auto load_iter = [&](int base, KBuf& bf) {
     const int key0 = base + wave * KPW + kg;
@@ -838,9 +877,11 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
         const char* row = kbase + (size_t)(s_begin + key) * D * sizeof(T);
         bf.lo[u] = load_words<4>(row + lo_off);
         bf.hi[u] = load_words<4>(row + hi_off);
+        if constexpr (LOGITS) bf.mp[u] = p.mask_pos ? p.mask_pos[((size_t)b * p.Hkv + g) * p.C + s_begin + key] : 0;
       } else {
         bf.lo[u] = zero_words<4>();
         bf.hi[u] = zero_words<4>();
+        if constexpr (LOGITS) bf.mp[u] = -1;
       }
     }
     if constexpr (ROPE) {
@@ -892,6 +933,12 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
     for (int u = 0; u < U; ++u) {
       const int key = key0 + u * KPI;
       const bool valid = key < cnt;
+      if constexpr (LOGITS) {  // empty slots (H2O blocks): logit -inf, weight 0
+        if (bf.mp[u] < 0) {
+#pragma unroll
+          for (int j = 0; j < G; ++j) d[u * G + j] = -INFINITY;
+        }
+      }
 #pragma unroll
       for (int j = 0; j < G; ++j) mx[j] = fmaxf(mx[j], valid ? d[u * G + j] : -INFINITY);
       if (valid && sub == 0) {
@@ -1043,20 +1090,18 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
 }
 
 // Victim choice for a seeded H2O layer (no decode step has run yet): the lowest score
-// among slots whose token position is <= max_pos, ties evicting the higher position.
+// (token granule) or summed block score (blocks of bs slots) among candidates whose
+// tokens have pos <= max_pos, ties evicting the newer token.
 __global__ void __launch_bounds__(256) h2o_pick_victim_kernel(const float* score, const int* pos, int* victim, int C,
-                                                              int n, int64_t max_pos) {
+                                                              int n, int64_t max_pos, int bs) {
   __shared__ unsigned long long wbest[4];
   const size_t bg = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   unsigned long long best = ~0ull;
-  for (int i = threadIdx.x; i < n; i += 256) {
-    const int ps = pos[bg * C + i];
-    if ((int64_t)ps <= max_pos) {
-      const unsigned long long key = ((unsigned long long)__float_as_uint(score[bg * C + i]) << 32) |
-                                     (unsigned long long)(0xffffffffu - (uint32_t)ps);
-      best = key < best ? key : best;
-    }
+  for (int base = threadIdx.x - lane; base < n; base += 256) {  // wave-uniform bound
+    const int i = base + lane;
+    const bool in = i < n;
+    fold_victim(best, in ? score[bg * C + i] : 0.f, in ? pos[bg * C + i] : 0, in, max_pos, bs, lane);
   }
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -1070,12 +1115,12 @@ __global__ void __launch_bounds__(256) h2o_pick_victim_kernel(const float* score
   if (best == ~0ull) return;
   const int win_pos = (int)(0xffffffffu - (uint32_t)(best & 0xffffffffull));
   for (int i = threadIdx.x; i < n; i += 256)
-    if (pos[bg * C + i] == win_pos) victim[bg] = i;
+    if (pos[bg * C + i] == win_pos) victim[bg] = bs > 1 ? i / bs : i;
 }
 
 hipError_t launch_h2o_pick_victim(const float* score, const int* pos, int* victim, int BHkv, int C, int n,
-                                  int64_t max_pos, hipStream_t s) {
-  hipLaunchKernelGGL(h2o_pick_victim_kernel, dim3(BHkv), dim3(256), 0, s, score, pos, victim, C, n, max_pos);
+                                  int64_t max_pos, int bs, hipStream_t s) {
+  hipLaunchKernelGGL(h2o_pick_victim_kernel, dim3(BHkv), dim3(256), 0, s, score, pos, victim, C, n, max_pos, bs);
   return hipGetLastError();
 }
 

@@ -36,7 +36,22 @@ __global__ void append_rows_kernel(AppendParams p) {
 // once the budget is full, into the victim slot chosen by the previous decode step.
 __global__ void append_h2o_kernel(AppendParams p) {
   const int bh = blockIdx.x;
-  const int slot = p.fill < p.C ? p.fill : p.victim[bh];
+  int slot;
+  if (p.fill < p.C) {
+    slot = p.fill;
+  } else if (p.bs <= 1) {
+    slot = p.victim[bh];
+  } else if (p.new_block) {  // block-level: the freed block becomes the open block
+    const int blk = p.victim[bh];
+    slot = blk * p.bs;
+    for (int e = 1 + threadIdx.x; e < p.bs; e += blockDim.x) {
+      p.pos[(size_t)bh * p.C + slot + e] = -1;  // emptied: not attended until refilled
+      p.score[(size_t)bh * p.C + slot + e] = 0.f;
+    }
+    if (threadIdx.x == 0) p.open[bh] = blk;
+  } else {
+    slot = p.open[bh] * p.bs + p.offset;
+  }
   const int chunks = p.row_bytes / 16;
   const size_t src = (size_t)bh * p.row_bytes;
   const size_t dst = ((size_t)bh * p.C + slot) * p.row_bytes;

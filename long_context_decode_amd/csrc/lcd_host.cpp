@@ -59,6 +59,7 @@ struct Layout {
   uint64_t layer_bytes = 0;  // one of K or V of one layer
   uint64_t kv_bytes = 0;
   uint64_t aux_bytes = 0, off_cos = 0, off_sin = 0, off_pos = 0, off_score = 0, off_victim = 0, off_arrive = 0;
+  uint64_t off_open = 0;
   uint64_t ws_bytes = 0, ws_off_ml = 0, ws_off_logits = 0;
   int max_splits = 0, chunk_cap = 0, chunk_force = 0, target_wgs = 0;
   // mixed retrieval / streaming heads (DUO): streaming capacity, per-layer retrieval
@@ -94,6 +95,14 @@ lcd_status check_config(const lcd_cache_config* c, Layout* L) {
       C = c->capacity;
       if (c->policy == LCD_H2O && (c->n_recent < 1 || c->n_recent > c->capacity))
         return fail(LCD_ESHAPE, "H2O needs 1 <= n_recent <= capacity");
+      if (c->policy == LCD_H2O && c->block_size > 1) {
+        if (c->block_size != 16 && c->block_size != 32) return fail(LCD_ESHAPE, "H2O block_size must be 0, 1, 16 or 32");
+        if (c->capacity % c->block_size) return fail(LCD_ESHAPE, "capacity must be a multiple of block_size");
+        if (c->n_recent > c->capacity - c->block_size)
+          return fail(LCD_ESHAPE, "block-level H2O needs n_recent <= capacity - block_size");
+      } else if (c->policy == LCD_H2O && c->block_size < 0) {
+        return fail(LCD_ESHAPE, "block_size must be >= 0");
+      }
       break;
     case LCD_DUO:
       if (c->capacity < 1) return fail(LCD_ESHAPE, "capacity must be >= 1");
@@ -174,6 +183,8 @@ lcd_status check_config(const lcd_cache_config* c, Layout* L) {
     L->off_score = aux;
     aux = align256(aux + per * sizeof(float));
     L->off_victim = aux;
+    aux = align256(aux + (uint64_t)c->n_layers * c->batch * c->n_kv_heads * sizeof(int32_t));
+    L->off_open = aux;  // block-level: the block receiving new tokens
     aux = align256(aux + (uint64_t)c->n_layers * c->batch * c->n_kv_heads * sizeof(int32_t));
   }
   L->aux_bytes = aux;
@@ -275,6 +286,14 @@ struct lcd_cache {
                ? reinterpret_cast<int32_t*>(aux + L.off_victim) + (uint64_t)l * cfg.batch * cfg.n_kv_heads
                : nullptr;
   }
+  int32_t* open_block(int l) const {
+    return cfg.policy == LCD_H2O
+               ? reinterpret_cast<int32_t*>(aux + L.off_open) + (uint64_t)l * cfg.batch * cfg.n_kv_heads
+               : nullptr;
+  }
+  // H2O eviction granule (1 = token) and, per layer, slots used in the open block
+  int bs() const { return cfg.policy == LCD_H2O && cfg.block_size > 1 ? cfg.block_size : 1; }
+  std::vector<int> open_fill;
 };
 
 extern "C" {
@@ -320,6 +339,7 @@ lcd_status lcd_kv_cache_init(const lcd_cache_config* cfg, void* kv_mem, uint64_t
   c->aux = static_cast<char*>(aux_mem);
   c->tokens.assign(cfg->n_layers, 0);
   c->filled.assign(cfg->n_layers, 0);
+  c->open_fill.assign(cfg->n_layers, 0);
   const double scale = cfg->scale > 0 ? cfg->scale : 1.0 / std::sqrt((double)cfg->head_dim);
   c->qscale = (float)(scale * 1.4426950408889634074);  // scale * log2(e), rounded once
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -331,6 +351,7 @@ lcd_status lcd_kv_cache_init(const lcd_cache_config* cfg, void* kv_mem, uint64_t
     e = lcd::launch_fill_i32(c->pos(0), -1, n, s);
     if (e == hipSuccess) e = lcd::launch_fill_f32(c->score(0), 0.f, n, s);
     if (e == hipSuccess) e = lcd::launch_fill_i32(c->victim(0), 0, (int64_t)cfg->n_layers * cfg->batch * cfg->n_kv_heads, s);
+    if (e == hipSuccess) e = lcd::launch_fill_i32(c->open_block(0), 0, (int64_t)cfg->n_layers * cfg->batch * cfg->n_kv_heads, s);
   }
   if (e != hipSuccess) {
     delete c;
@@ -437,9 +458,23 @@ lcd_status lcd_kv_append(lcd_cache* c, int32_t layer, const void* k, const void*
     p.pos = c->pos(layer);
     p.score = c->score(layer);
     p.token = t0;
+    const int bs = c->bs();
+    p.bs = bs;
+    p.open = c->open_block(layer);
+    int next_fill = 0;  // slots used in the open block after this append
+    if (p.fill < C) {
+      next_fill = (p.fill % bs) + 1;
+    } else if (c->open_fill[layer] >= bs) {  // a full cache needs a new block: the victim
+      p.new_block = 1;
+      next_fill = 1;
+    } else {
+      p.offset = c->open_fill[layer];
+      next_fill = c->open_fill[layer] + 1;
+    }
     const hipError_t e = lcd::launch_append(p, s);
     if (e != hipSuccess) return hip_fail(e, "kv_append launch");
     new_filled = std::min<int64_t>(c->filled[layer] + 1, C);
+    c->open_fill[layer] = next_fill;
   }
   c->tokens[layer] = t0 + n_new;
   c->filled[layer] = new_filled;
@@ -522,8 +557,12 @@ lcd_status lcd_decode_attn(lcd_cache* c, int32_t layer, const void* q, float* ou
     p.score = c->score(layer);
     p.pos = c->pos(layer);
     p.victim = c->victim(layer);
-    p.pick_victim = n == L.C ? 1 : 0;
+    // a victim is needed iff the next append finds the cache full and (blocks) the open
+    // block full
+    p.bs = c->bs();
+    p.pick_victim = n == L.C && c->open_fill[layer] >= p.bs ? 1 : 0;
     p.max_pos = c->tokens[layer] - cfg.n_recent;  // next token id minus the protected count
+    p.mask_pos = p.bs > 1 ? c->pos(layer) : nullptr;  // emptied slots of a reopened block
   }
   const hipError_t e =
       lcd::launch_decode_split(cfg.dtype, cfg.head_dim, L.G, mode, p, static_cast<hipStream_t>(stream));
@@ -586,12 +625,14 @@ lcd_status lcd_kv_set_filled(lcd_cache* c, int32_t layer, int32_t n, int64_t nex
   if (n < 0 || n > c->L.C) return fail(LCD_ECAPACITY, "n=%d outside [0, %d]", n, c->L.C);
   if (next_token < n) return fail(LCD_EINVAL, "next_token must be >= n");
   if (c->cfg.policy == LCD_H2O && next_token > INT32_MAX) return fail(LCD_ECAPACITY, "H2O token positions are int32");
+  const int bs = c->bs();
   if (c->cfg.policy == LCD_H2O && n == c->L.C) {
     const hipError_t e = lcd::launch_h2o_pick_victim(c->score(layer), c->pos(layer), c->victim(layer),
                                                      c->cfg.batch * c->cfg.n_kv_heads, c->L.C, n,
-                                                     next_token - c->cfg.n_recent, static_cast<hipStream_t>(stream));
+                                                     next_token - c->cfg.n_recent, bs, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "set_filled victim launch");
   }
+  if (c->cfg.policy == LCD_H2O) c->open_fill[layer] = n % bs ? n % bs : (n ? bs : 0);
   c->filled[layer] = n;
   c->tokens[layer] = next_token;
   return ok();

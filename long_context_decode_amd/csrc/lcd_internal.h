@@ -35,6 +35,8 @@ struct DecodeParams {
   int* victim;         // layer [B][Hkv]
   int pick_victim;     // cache full: choose the slot the next append overwrites
   int64_t max_pos;     // victim candidates have pos <= max_pos
+  int bs;              // H2O eviction granule: 1 = token, 16 / 32 = block of slots
+  const int* mask_pos; // H2O blocks: slots with mask_pos[slot] < 0 are empty (not attended)
   int B, Hq, Hkv, C;
   int n;               // attended slots 0..n-1
   int chunk;           // slots per split (multiple of 64)
@@ -69,8 +71,11 @@ struct AppendParams {
   //   slot_lin + (r - r0)                      if r <  r_split
   //   S + (ring_off + (r - r_split)) % W       if r >= r_split
   int r0, n_rows, r_split, slot_lin, ring_off, S, W;
-  // H2O: one row per (b, kv head), slot = fill < C ? fill : victim[bh]
-  int h2o, fill;
+  // H2O: one row per (b, kv head), slot = fill < C ? fill : victim[bh]; blocks of bs
+  // slots: at a full cache a new block (new_block) takes victim[bh] (recorded in open[bh],
+  // its other slots emptied), otherwise the row goes to slot open[bh] * bs + offset
+  int h2o, fill, bs, new_block, offset;
+  int* open;
   // mixed heads (duo = 1): rows of input token a = t0 + r go to a retrieval head's
   // slot a, or to a streaming head's sink / ring slot when a < S or a >= a_first
   int duo, Hkv, Hret, Hstr, C2;
@@ -87,7 +92,7 @@ struct AppendParams {
 hipError_t launch_decode_split(int dtype, int D, int G, int mode, const DecodeParams& p, hipStream_t s);
 hipError_t launch_append(const AppendParams& p, hipStream_t s);
 hipError_t launch_h2o_pick_victim(const float* score, const int* pos, int* victim, int BHkv, int C, int n,
-                                  int64_t max_pos, hipStream_t s);
+                                  int64_t max_pos, int bs, hipStream_t s);
 hipError_t launch_rope_table(float* cos_t, float* sin_t, int C, int D, double base, hipStream_t s);
 hipError_t launch_fill_i32(int* p, int value, int64_t n, hipStream_t s);
 hipError_t launch_fill_f32(float* p, float value, int64_t n, hipStream_t s);

@@ -121,6 +121,17 @@ class H2OBlockHead:
         self.n_blocks, self.block_size, self.n_recent = int(n_blocks), int(block_size), int(n_recent)
         self.blocks = []  # each: dict(pos=[...], k=[...], v=[...], s=[...]); the last is the open block
 
+    def load(self, positions, keys, values, scores):
+        """Seed a full cache: consecutive runs of block_size entries form the blocks."""
+        n = len(positions)
+        if n != self.n_blocks * self.block_size:
+            raise ValueError("a seeded block cache must be full")
+        bs = self.block_size
+        self.blocks = [dict(pos=[int(x) for x in positions[i:i + bs]],
+                            k=[np.asarray(x, np.float64) for x in keys[i:i + bs]],
+                            v=[np.asarray(x, np.float64) for x in values[i:i + bs]],
+                            s=[float(x) for x in scores[i:i + bs]]) for i in range(0, n, bs)]
+
     def tokens(self):
         return [p for blk in self.blocks for p in blk["pos"]]
 

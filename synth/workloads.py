@@ -48,6 +48,7 @@ class Workload:
     # h2o
     budget: int = 0
     n_recent: int = 0
+    block_size: int = 0  # 0: token-level eviction; 16 / 32: block-level
     # duo: per layer, per KV head, 1 = retrieval head (full history), 0 = streaming
     # head (n_sink sinks + window recent tokens)
     retrieval: tuple = ()
@@ -340,6 +341,12 @@ WORKLOADS = {
               "scored by its full causal attention, kept in a 4096 budget (512 recent + 3584 heavy)",
         kind="h2o_prompt", batch=16, n_q_heads=32, n_kv_heads=8, head_dim=128, dtype="bf16",
         n_prompt=131072, budget=4096, n_recent=512),
+    "h2o_blocks_128k": Workload(
+        name="h2o_128k",  # the same seeded tensors as h2o_128k
+        title="H2O block-level decode: B=16, 32 q / 8 kv heads, D=128, bf16, 131072-token prompt held in "
+              "a 4096 budget of 16-token blocks (512 recent + 3584 heavy), 1024 decode steps",
+        kind="h2o", batch=16, n_q_heads=32, n_kv_heads=8, head_dim=128, dtype="bf16",
+        n_prompt=131072, budget=4096, n_recent=512, steps=1024, plant_frac=0.02, plant_scale=3.0, block_size=16),
     "h2o_128k": Workload(
         name="h2o_128k",
         title="H2O budgeted decode: B=16, 32 q / 8 kv heads, D=128, bf16, 131072-token prompt held in "

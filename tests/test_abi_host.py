@@ -164,7 +164,7 @@ def test_duo_too_many_heads(L):
 def test_destroy_null_is_ignored(L):
     L.lib.lcd_kv_cache_destroy(None)
     assert isinstance(L.last_error(), str)
-    assert ctypes.sizeof(L._lib.CacheConfig) == 12 * 4 + 2 * 8 + 8  # + the DUO head-map pointer
+    assert ctypes.sizeof(L._lib.CacheConfig) == 12 * 4 + 2 * 8 + 8 + 8  # + DUO map pointer, block size (padded)
 
 
 # ---------------------------------------------------------------- PyramidKV budgets (host-only)
@@ -197,3 +197,18 @@ def test_h2o_prompt_param_validation(L):
         with pytest.raises(L.LcdError) as e:
             L.h2o_prompt_sizes(L.h2o_prompt_params(**p))
         assert e.value.name == status, kw
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(block_size=8), "LCD_ESHAPE"), (dict(block_size=16, capacity=100), "LCD_ESHAPE"),
+    (dict(block_size=16, capacity=64, n_recent=60), "LCD_ESHAPE"), (dict(block_size=-1), "LCD_ESHAPE"),
+])
+def test_h2o_block_validation(L, kw, status):
+    base = dict(batch=1, n_q_heads=4, n_kv_heads=1, head_dim=128, dtype=1, policy=L.LCD_H2O, capacity=64,
+                n_recent=8)
+    base.update(kw)
+    with pytest.raises(L.LcdError) as e:
+        L.cache_sizes(L.cache_config(**base))
+    assert e.value.name == status
+    ok = dict(base, block_size=32, capacity=128, n_recent=96)
+    assert L.cache_sizes(L.cache_config(**ok))[0] > 0
