@@ -64,6 +64,7 @@ TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_onepass_kernel_llama2_b1
 TRAFFIC_SOURCES = ("long_context_decode_amd/csrc/decode.hip", "long_context_decode_amd/csrc/lcd_internal.h",
                    "long_context_decode_amd/csrc/lcd_host.cpp")
 COPY_BYTES = 1 << 30  # the calibration copy
+COUNTER_RUN = "python3 bench.py --only --copy-calibration --steps 64 --warmup 8 --no-cpu-baseline"
 
 
 def _sources_digest():
@@ -119,12 +120,9 @@ def _counter_summary(fetch_csv, write_csv, out=TRAFFIC_RECORD):
         "Two rocprofv3 counter runs of the same command, one counter each:",
         "",
         "```",
-        "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/p26/fetch -o run -- "
-        "python3 bench.py --only --copy-calibration --steps 64 --warmup 8 --no-cpu-baseline",
-        "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/p26/write -o run -- "
-        "python3 bench.py --only --copy-calibration --steps 64 --warmup 8 --no-cpu-baseline",
-        "python3 bench.py --counters gpurun_out/p26/fetch/run_counter_collection.csv "
-        "gpurun_out/p26/write/run_counter_collection.csv",
+        f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {os.path.dirname(fetch_csv)} -o run -- {COUNTER_RUN}",
+        f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {os.path.dirname(write_csv)} -o run -- {COUNTER_RUN}",
+        f"python3 bench.py --counters {fetch_csv} {write_csv}",
         "```",
         "",
         "The calibration copy moves 1 GiB in each direction; each counter is scaled by "

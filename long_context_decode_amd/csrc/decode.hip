@@ -321,8 +321,9 @@ __device__ inline void fold_victim(unsigned long long& best, float s, int ps, bo
 // output and Mh / Lh (LDS) its maximum and sum per query head.  With one split the
 // output is normalised and written; otherwise the partial is published and the last
 // workgroup of (b, g) to arrive merges every split in split order (deterministic).  In
-// logits mode the merging workgroup then runs the H2O epilogue.
-template <int D, int G, bool LOGITS>
+// logits mode the merging workgroup then runs the H2O epilogue, evicting whole blocks of
+// p.bs slots when BLOCKS is set.
+template <int D, int G, bool LOGITS, bool BLOCKS>
 __device__ inline void split_finish(const DecodeParams& p, const float* ored, const float* Mh, const float* Lh,
                                     int split, int n_splits, int b, int g) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -390,6 +391,7 @@ __device__ inline void split_finish(const DecodeParams& p, const float* ored, co
     float* score = p.score + bg * p.C;
     const int* pos = p.pos + bg * p.C;
     unsigned long long best = ~0ull;
+    const int bs = BLOCKS ? p.bs : 1;  // eviction granule
     constexpr int EU = LCD_H2O_EU;  // slots per thread per iteration, all loads issued first
     for (int base = threadIdx.x - lane; base < p.n; base += kDecodeThreads * EU) {
       const int i0 = base + lane;
@@ -417,7 +419,7 @@ __device__ inline void split_finish(const DecodeParams& p, const float* ored, co
           score[i] = snew;
         }
         if (p.pick_victim && base + u * kDecodeThreads < p.n)  // wave-uniform
-          fold_victim(best, snew, ps[u], in, p.max_pos, p.bs, lane);
+          fold_victim(best, snew, ps[u], in, p.max_pos, bs, lane);
       }
     }
     if (p.pick_victim) {
@@ -434,7 +436,7 @@ __device__ inline void split_finish(const DecodeParams& p, const float* ored, co
       if (best != ~0ull) {
         const int win_pos = (int)(0xffffffffu - (uint32_t)(best & 0xffffffffull));
         for (int i = threadIdx.x; i < p.n; i += kDecodeThreads)
-          if (pos[i] == win_pos) p.victim[bg] = p.bs > 1 ? i / p.bs : i;
+          if (pos[i] == win_pos) p.victim[bg] = bs > 1 ? i / bs : i;
       }
     }
   }
@@ -446,7 +448,8 @@ __device__ inline void split_finish(const DecodeParams& p, const float* ored, co
 template <typename T, int D, int G, int MODE>
 __global__ void __launch_bounds__(kDecodeThreads) decode_onepass_kernel(DecodeParams p) {
   constexpr bool ROPE = MODE == kModeRope;
-  constexpr bool LOGITS = MODE == kModePlainLogits;
+  constexpr bool LOGITS = MODE == kModePlainLogits || MODE == kModeMaskedLogits;
+  constexpr bool MASKED = MODE == kModeMaskedLogits;
   using GE = Geo<T, D, G>;
   constexpr int W = GE::W, HALF = GE::HALF, EPL = GE::EPL, LPK = GE::LPK, KPW = GE::KPW, KPI = GE::KPI;
   constexpr int U = GE::U, STEP = GE::STEP;
@@ -554,9 +557,9 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_onepass_kernel(DecodePa
         bf.khi[u] = load_words<W>(kbase + roff + hi_off);
         bf.vlo[u] = load_words<W>(vbase + roff + lo_off);
         bf.vhi[u] = load_words<W>(vbase + roff + hi_off);
-        if constexpr (LOGITS) bf.mp[u] = p.mask_pos ? p.mask_pos[((size_t)b * p.Hkv + g) * p.C + s_begin + key] : 0;
+        if constexpr (MASKED) bf.mp[u] = p.mask_pos[((size_t)b * p.Hkv + g) * p.C + s_begin + key];
       } else {
-        if constexpr (LOGITS) bf.mp[u] = -1;
+        if constexpr (MASKED) bf.mp[u] = -1;
         bf.klo[u] = zero_words<W>();
         bf.khi[u] = zero_words<W>();
         bf.vlo[u] = zero_words<W>();
@@ -649,7 +652,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_onepass_kernel(DecodePa
     for (int u = 0; u < U; ++u) {
       const int key = key0 + u * KPI;
       bool valid = key < cnt;
-      if constexpr (LOGITS) valid = valid && bf.mp[u] >= 0;
+      if constexpr (MASKED) valid = valid && bf.mp[u] >= 0;
 #pragma unroll
       for (int j = 0; j < G; ++j) {
         d[u * G + j] = valid ? d[u * G + j] : -INFINITY;
@@ -773,7 +776,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_onepass_kernel(DecodePa
     ored[idx] = acc;
   }
   __syncthreads();
-  split_finish<D, G, LOGITS>(p, ored, Mh, Lh, split, n_splits, b, g);
+  split_finish<D, G, LOGITS, MASKED>(p, ored, Mh, Lh, split, n_splits, b, g);
 }
 
 // ---------------------------------------------------------------- two-pass kernel
@@ -786,7 +789,8 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_onepass_kernel(DecodePa
 template <typename T, int D, int G, int MODE>
 __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodeParams p) {
   constexpr bool ROPE = MODE == kModeRope;
-  constexpr bool LOGITS = MODE == kModePlainLogits;
+  constexpr bool LOGITS = MODE == kModePlainLogits || MODE == kModeMaskedLogits;
+  constexpr bool MASKED = MODE == kModeMaskedLogits;
   using E = Elem<T, 4>;
   constexpr int HALF = E::N;
   constexpr int EPL = 2 * HALF;    // elements per lane (HALF pairs)
@@ -877,11 +881,11 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
         const char* row = kbase + (size_t)(s_begin + key) * D * sizeof(T);
         bf.lo[u] = load_words<4>(row + lo_off);
         bf.hi[u] = load_words<4>(row + hi_off);
-        if constexpr (LOGITS) bf.mp[u] = p.mask_pos ? p.mask_pos[((size_t)b * p.Hkv + g) * p.C + s_begin + key] : 0;
+        if constexpr (MASKED) bf.mp[u] = p.mask_pos[((size_t)b * p.Hkv + g) * p.C + s_begin + key];
       } else {
         bf.lo[u] = zero_words<4>();
         bf.hi[u] = zero_words<4>();
-        if constexpr (LOGITS) bf.mp[u] = -1;
+        if constexpr (MASKED) bf.mp[u] = -1;
       }
     }
     if constexpr (ROPE) {
@@ -933,7 +937,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
     for (int u = 0; u < U; ++u) {
       const int key = key0 + u * KPI;
       const bool valid = key < cnt;
-      if constexpr (LOGITS) {  // empty slots (H2O blocks): logit -inf, weight 0
+      if constexpr (MASKED) {  // empty slots (H2O blocks): logit -inf, weight 0
         if (bf.mp[u] < 0) {
 #pragma unroll
           for (int j = 0; j < G; ++j) d[u * G + j] = -INFINITY;
@@ -1086,7 +1090,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
   for (int idx = threadIdx.x; idx < G * D; idx += kDecodeThreads)  // each thread reads only its idx
     ored[idx] = ored[idx] + ored[G * D + idx] + ored[2 * G * D + idx] + ored[3 * G * D + idx];
   __syncthreads();
-  split_finish<D, G, LOGITS>(p, ored, Mh, Lh, split, n_splits, b, g);
+  split_finish<D, G, LOGITS, MASKED>(p, ored, Mh, Lh, split, n_splits, b, g);
 }
 
 // Victim choice for a seeded H2O layer (no decode step has run yet): the lowest score
@@ -1138,6 +1142,9 @@ static hipError_t launch_tdg(int mode, const DecodeParams& p, hipStream_t s) {
       case kModePlainLogits:
         hipLaunchKernelGGL((decode_onepass_kernel<T, D, G, kModePlainLogits>), grid, block, lds, s, p);
         break;
+      case kModeMaskedLogits:
+        hipLaunchKernelGGL((decode_onepass_kernel<T, D, G, kModeMaskedLogits>), grid, block, lds, s, p);
+        break;
       default: return hipErrorInvalidValue;
     }
   } else {
@@ -1147,6 +1154,9 @@ static hipError_t launch_tdg(int mode, const DecodeParams& p, hipStream_t s) {
       case kModePlain: hipLaunchKernelGGL((decode_twopass_kernel<T, D, G, kModePlain>), grid, block, lds, s, p); break;
       case kModePlainLogits:
         hipLaunchKernelGGL((decode_twopass_kernel<T, D, G, kModePlainLogits>), grid, block, lds, s, p);
+        break;
+      case kModeMaskedLogits:
+        hipLaunchKernelGGL((decode_twopass_kernel<T, D, G, kModeMaskedLogits>), grid, block, lds, s, p);
         break;
       default: return hipErrorInvalidValue;
     }

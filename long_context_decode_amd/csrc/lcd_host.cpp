@@ -549,7 +549,7 @@ lcd_status lcd_decode_attn(lcd_cache* c, int32_t layer, const void* q, float* ou
     p.ring_head = p.full ? (int)((t - cfg.window + 1 - cfg.n_sink) % cfg.window) : 0;
     p.q_rank = n - 1;
   } else if (cfg.policy == LCD_H2O) {
-    mode = lcd::kModePlainLogits;
+    mode = c->bs() > 1 ? lcd::kModeMaskedLogits : lcd::kModePlainLogits;
   }
   p.out = out;
   p.arrivals = c->arrivals(layer);

@@ -12,7 +12,8 @@ constexpr int kDecodeThreads = 256;
 // Decode workgroups assumed resident at once (2 per CU on 256 CUs), for the split plan.
 constexpr int kResidentWorkgroups = 512;
 
-enum DecodeMode { kModeRope = 0, kModePlain = 1, kModePlainLogits = 2 };
+// kModeMaskedLogits: kModePlainLogits where slots with mask_pos[slot] < 0 are skipped
+enum DecodeMode { kModeRope = 0, kModePlain = 1, kModePlainLogits = 2, kModeMaskedLogits = 3 };
 
 // Most KV heads per layer of a mixed retrieval / streaming (DuoAttention) cache: the
 // per-head map travels in the kernel arguments.
