@@ -31,7 +31,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK = 8.0e12  # B/s, MI355X HBM3E
 MFMA_BF16_PEAK = 2.5e15  # flop/s, dense
 METRIC = "decode steps/s + achieved HBM TB/s (% of peak); SnapKV compress ms"
-DEFAULTS = {"llama2_7b_layer": (8192, 64), "gqa_long": (64, 4), "h2o_128k": (1024, 32),
+DEFAULTS = {"llama2_7b_layer": (8192, 64), "llama3_8b_layer": (1024, 32), "gqa_long": (64, 4), "h2o_128k": (1024, 32),
             "h2o_blocks_128k": (1024, 32), "duo_128k": (192, 16), "tiny_streaming": (448, 64)}
 
 
@@ -491,7 +491,7 @@ def main(argv=None):
         line["h2o_prompt"] = _h2o_prompt_bench(L, WORKLOADS["h2o_prompt_128k"])
     if not a.only:
         others = []
-        for name in ("gqa_long", "h2o_128k", "h2o_blocks_128k", "duo_128k", "tiny_streaming"):
+        for name in ("llama3_8b_layer", "gqa_long", "h2o_128k", "h2o_blocks_128k", "duo_128k", "tiny_streaming"):
             if name == a.workload:
                 continue
             s2, w2 = DEFAULTS[name]

@@ -53,11 +53,20 @@ struct bf16_t {
 #ifndef LCD_U2_G4
 #define LCD_U2_G4 4
 #endif
+#ifndef LCD_U2_G4R
+#define LCD_U2_G4R 2  // G = 4 with RoPE (4 keys leave one wave per SIMD)
+#endif
 #ifndef LCD_U2_G6
 #define LCD_U2_G6 2
 #endif
 #ifndef LCD_H2O_EU
-#define LCD_H2O_EU 4  // H2O epilogue: slots per thread per iteration
+#define LCD_H2O_EU 16  // token-level H2O epilogue: slots per thread per iteration (4 for blocks)
+#endif
+#ifndef LCD_OP_MINB
+#define LCD_OP_MINB 1  // one-pass kernel: minimum resident workgroups per CU the registers must allow
+#endif
+#ifndef LCD_REC2
+#define LCD_REC2 1  // two-pass kernel: RoPE angles by angle addition within an iteration
 #endif
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -284,49 +293,94 @@ __device__ inline HeadView head_view(const DecodeParams& p, int b, int g) {
   return {reinterpret_cast<const char*>(p.k) + off, reinterpret_cast<const char*>(p.v) + off, p.n};
 }
 
-// H2O eviction candidates: folds one slot per lane (score s, position ps, in range) into
-// the running minimum of the u64 key (score bits << 32 | ~position): the lowest score,
-// ties to the newer token.  Token granule (bs <= 1): every slot with ps <= max_pos.
-// Blocks of bs = 16 or 32 slots (bs consecutive lanes, every lane active): the block's
-// summed score and newest position, a candidate only if all its slots hold tokens
-// with ps <= max_pos; lane 0 of the block folds it.  Scores are >= 0, so their bits
-// order like the values.
-__device__ inline void fold_victim(unsigned long long& best, float s, int ps, bool in, int64_t max_pos, int bs,
-                                   int lane) {
+// H2O eviction candidates.  A candidate's key is (score bits << 32 | ~position): the
+// minimum is the lowest score, ties to the newer token; positions are unique, so the
+// minimum is unique and carries the index to evict.  Scores are >= 0, so their bits order
+// like the values.
+struct Victim {
+  unsigned long long key = ~0ull;  // ~0: no candidate
+  int at = 0;                      // slot (token granule) or block index of key
+};
+
+// Folds one slot per lane (score s, position ps, slot index i, in range) into v.  Token
+// granule (bs <= 1): every slot with ps <= max_pos.  Blocks of bs = 16 or 32 slots (bs
+// consecutive lanes starting at a multiple of bs, every lane active): the block's summed
+// score and newest position, a candidate only if all its slots hold tokens with
+// ps <= max_pos; lane 0 of the block folds it.
+__device__ inline void fold_victim(Victim& v, float s, int ps, int i, bool in, int64_t max_pos, int bs, int lane) {
   if (bs <= 1) {
     if (in && (int64_t)ps <= max_pos) {
       const unsigned long long key =
           ((unsigned long long)__float_as_uint(s) << 32) | (unsigned long long)(0xffffffffu - (uint32_t)ps);
-      best = key < best ? key : best;
+      if (key < v.key) {
+        v.key = key;
+        v.at = i;
+      }
     }
     return;
   }
   float sum = in ? s : 0.f;
   int mpos = in ? ps : -1;
   int bad = (!in || ps < 0 || (int64_t)ps > max_pos) ? 1 : 0;
-  for (int off = 1; off < bs; off <<= 1) {
-    sum += __shfl_xor(sum, off, 64);
-    mpos = max(mpos, __shfl_xor(mpos, off, 64));
-    bad = max(bad, __shfl_xor(bad, off, 64));
+#pragma unroll
+  for (int off = 1; off < 32; off <<= 1) {  // a fixed trip count keeps the callers' loops unrolled
+    if (off < bs) {
+      sum += __shfl_xor(sum, off, 64);
+      mpos = max(mpos, __shfl_xor(mpos, off, 64));
+      bad = max(bad, __shfl_xor(bad, off, 64));
+    }
   }
   if ((lane & (bs - 1)) == 0 && !bad) {
     const unsigned long long key =
         ((unsigned long long)__float_as_uint(sum) << 32) | (unsigned long long)(0xffffffffu - (uint32_t)mpos);
-    best = key < best ? key : best;
+    if (key < v.key) {
+      v.key = key;
+      v.at = i / bs;
+    }
   }
 }
 
+// The workgroup's minimum (256 threads; every thread calls it; wk / wa: 4 LDS entries each).
+__device__ inline Victim reduce_victim(Victim v, unsigned long long* wk, int* wa) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const unsigned long long ok = __shfl_xor(v.key, off, 64);
+    const int oa = __shfl_xor(v.at, off, 64);
+    if (ok < v.key) {
+      v.key = ok;
+      v.at = oa;
+    }
+  }
+  if (lane == 0) {
+    wk[wave] = v.key;
+    wa[wave] = v.at;
+  }
+  __syncthreads();
+  Victim r;
+  r.key = wk[0];
+  r.at = wa[0];
+#pragma unroll
+  for (int w = 1; w < 4; ++w)
+    if (wk[w] < r.key) {
+      r.key = wk[w];
+      r.at = wa[w];
+    }
+  return r;
+}
+
 // ---------------------------------------------------------------- split finish
-// The end of a decode workgroup: ored[0 .. G*D) (LDS) holds its range's unnormalised
-// output and Mh / Lh (LDS) its maximum and sum per query head.  With one split the
-// output is normalised and written; otherwise the partial is published and the last
-// workgroup of (b, g) to arrive merges every split in split order (deterministic).  In
+// The end of a decode workgroup: ored[0 .. G*D) (LDS, at least 64 * G floats) holds its
+// range's unnormalised output and Mh / Lh (LDS) its maximum and sum per query head.  With
+// one split the output is normalised and written; otherwise the partial is published and
+// the last workgroup of (b, g) to arrive merges every split (deterministic), reusing ored
+// for per-split weights.  In
 // logits mode the merging workgroup then runs the H2O epilogue, evicting whole blocks of
 // p.bs slots when BLOCKS is set.
 template <int D, int G, bool LOGITS, bool BLOCKS>
-__device__ inline void split_finish(const DecodeParams& p, const float* ored, const float* Mh, const float* Lh,
+__device__ inline void split_finish(const DecodeParams& p, float* ored, const float* Mh, const float* Lh,
                                     int split, int n_splits, int b, int g) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
   const size_t bg = (size_t)b * p.Hkv + g;
   const size_t bh0 = (size_t)b * p.Hq + g * G;
   __shared__ float Mtot[G], Linv[G];
@@ -356,27 +410,64 @@ __device__ inline void split_finish(const DecodeParams& p, const float* ored, co
                 n_splits - 1;
     __syncthreads();
     if (!is_last) return;
-    // last arrival: merge every split in split order (deterministic)
-    if (threadIdx.x < G) {
-      const int j = threadIdx.x;
-      float mt = -INFINITY;
-      for (int s = 0; s < n_splits; ++s) mt = fmaxf(mt, load_dev(&p.part_ml[((size_t)s * BH + bh0 + j) * 2]));
+    // last arrival: merge every split (fixed order, so deterministic).  The totals per
+    // query head come from wave-wide reductions with one split per lane; the outputs
+    // from per-split weights staged in LDS, 64 splits at a time, with the loads of
+    // SU splits of each thread's EPT elements issued before their arithmetic.
+    const int wave = threadIdx.x >> 6;
+    for (int j = wave; j < G; j += kDecodeThreads / 64) {
+      float mx = -INFINITY;
+      for (int s = lane; s < n_splits; s += 64) mx = fmaxf(mx, load_dev(&p.part_ml[((size_t)s * BH + bh0 + j) * 2]));
+      mx = wave_max(mx);
       float lt = 0.f;
-      for (int s = 0; s < n_splits; ++s) {
+      for (int s = lane; s < n_splits; s += 64) {
         const float* ml = p.part_ml + ((size_t)s * BH + bh0 + j) * 2;
-        lt += load_dev(&ml[1]) * exp2f(load_dev(&ml[0]) - mt);
+        lt += load_dev(&ml[1]) * exp2f(load_dev(&ml[0]) - mx);
       }
-      Mtot[j] = mt;
-      Linv[j] = 1.f / lt;
+      lt = wave_sum(lt);
+      if (lane == 0) {
+        Mtot[j] = mx;
+        Linv[j] = 1.f / lt;
+      }
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < G * D; idx += kDecodeThreads) {
-      const int j = idx / D, dd = idx % D;
-      float acc = 0.f;
-      for (int s = 0; s < n_splits; ++s)
-        acc += load_dev(&p.part_o[((size_t)s * BH + bh0 + j) * D + dd]) *
-               exp2f(load_dev(&p.part_ml[((size_t)s * BH + bh0 + j) * 2]) - Mtot[j]);
-      p.out[(bh0 + j) * D + dd] = acc * Linv[j];
+    constexpr int EPT = (G * D + kDecodeThreads - 1) / kDecodeThreads;  // output elements per thread
+    constexpr int SU = 4;
+    float* wsp = ored;  // [64][G] weights of the current group of splits (the partial is published)
+    float acc[EPT];
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) acc[k] = 0.f;
+    for (int s0 = 0; s0 < n_splits; s0 += 64) {
+      const int ns = min(64, n_splits - s0);
+      for (int e = threadIdx.x; e < ns * G; e += kDecodeThreads) {
+        const int j = e % G;
+        wsp[e] = exp2f(load_dev(&p.part_ml[((size_t)(s0 + e / G) * BH + bh0 + j) * 2]) - Mtot[j]) * Linv[j];
+      }
+      __syncthreads();
+      for (int s1 = 0; s1 < ns; s1 += SU) {
+        float x[SU][EPT];
+#pragma unroll
+        for (int u = 0; u < SU; ++u)
+#pragma unroll
+          for (int k = 0; k < EPT; ++k) {
+            const int idx = threadIdx.x + k * kDecodeThreads;
+            const bool in = s1 + u < ns && idx < G * D;
+            x[u][k] = in ? load_dev(&p.part_o[((size_t)(s0 + s1 + u) * BH + bh0) * D + idx]) : 0.f;
+          }
+#pragma unroll
+        for (int u = 0; u < SU; ++u)
+#pragma unroll
+          for (int k = 0; k < EPT; ++k) {
+            const int idx = threadIdx.x + k * kDecodeThreads;
+            if (s1 + u < ns && idx < G * D) acc[k] = fmaf(x[u][k], wsp[(s1 + u) * G + idx / D], acc[k]);
+          }
+      }
+      __syncthreads();  // wsp is rewritten by the next group
+    }
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+      const int idx = threadIdx.x + k * kDecodeThreads;
+      if (idx < G * D) p.out[bh0 * D + idx] = acc[k];
     }
     if (threadIdx.x == 0)  // ready for the next call
       __hip_atomic_store(&p.arrivals[bg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -387,12 +478,13 @@ __device__ inline void split_finish(const DecodeParams& p, const float* ored, co
     // filled slot's score and pick what the next append overwrites: the lowest score
     // among slots (or blocks of slots) of tokens with pos <= max_pos, ties evicting the
     // newer token.  The loop bound is wave-uniform so block reductions see whole waves.
-    __shared__ unsigned long long wbest[4];
+    __shared__ unsigned long long wkey[4];
+    __shared__ int wat[4];
     float* score = p.score + bg * p.C;
     const int* pos = p.pos + bg * p.C;
-    unsigned long long best = ~0ull;
+    Victim best;
     const int bs = BLOCKS ? p.bs : 1;  // eviction granule
-    constexpr int EU = LCD_H2O_EU;  // slots per thread per iteration, all loads issued first
+    constexpr int EU = BLOCKS ? 4 : LCD_H2O_EU;  // slots per thread per iteration, all loads issued first
     for (int base = threadIdx.x - lane; base < p.n; base += kDecodeThreads * EU) {
       const int i0 = base + lane;
       float x[EU][G], sc[EU];
@@ -419,25 +511,12 @@ __device__ inline void split_finish(const DecodeParams& p, const float* ored, co
           score[i] = snew;
         }
         if (p.pick_victim && base + u * kDecodeThreads < p.n)  // wave-uniform
-          fold_victim(best, snew, ps[u], in, p.max_pos, bs, lane);
+          fold_victim(best, snew, ps[u], i, in, p.max_pos, bs, lane);
       }
     }
     if (p.pick_victim) {
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const unsigned long long other = __shfl_xor(best, off, 64);
-        best = other < best ? other : best;
-      }
-      if (lane == 0) wbest[wave] = best;
-      __syncthreads();
-      best = wbest[0];
-#pragma unroll
-      for (int w = 1; w < 4; ++w) best = wbest[w] < best ? wbest[w] : best;
-      if (best != ~0ull) {
-        const int win_pos = (int)(0xffffffffu - (uint32_t)(best & 0xffffffffull));
-        for (int i = threadIdx.x; i < p.n; i += kDecodeThreads)
-          if (pos[i] == win_pos) p.victim[bg] = bs > 1 ? i / bs : i;
-      }
+      const Victim v = reduce_victim(best, wkey, wat);
+      if (threadIdx.x == 0 && v.key != ~0ull) p.victim[bg] = v.at;
     }
   }
 }
@@ -446,7 +525,7 @@ __device__ inline void split_finish(const DecodeParams& p, const float* ored, co
 // For up to 2 query heads per KV head (registers hold the queries and the outputs
 // together).
 template <typename T, int D, int G, int MODE>
-__global__ void __launch_bounds__(kDecodeThreads) decode_onepass_kernel(DecodeParams p) {
+__global__ void __launch_bounds__(kDecodeThreads, LCD_OP_MINB) decode_onepass_kernel(DecodeParams p) {
   constexpr bool ROPE = MODE == kModeRope;
   constexpr bool LOGITS = MODE == kModePlainLogits || MODE == kModeMaskedLogits;
   constexpr bool MASKED = MODE == kModeMaskedLogits;
@@ -557,13 +636,20 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_onepass_kernel(DecodePa
         bf.khi[u] = load_words<W>(kbase + roff + hi_off);
         bf.vlo[u] = load_words<W>(vbase + roff + lo_off);
         bf.vhi[u] = load_words<W>(vbase + roff + hi_off);
-        if constexpr (MASKED) bf.mp[u] = p.mask_pos[((size_t)b * p.Hkv + g) * p.C + s_begin + key];
       } else {
-        if constexpr (MASKED) bf.mp[u] = -1;
         bf.klo[u] = zero_words<W>();
         bf.khi[u] = zero_words<W>();
         bf.vlo[u] = zero_words<W>();
         bf.vhi[u] = zero_words<W>();
+      }
+    }
+    if constexpr (MASKED) {  // an in-range index for every lane, then a select on the value
+      const int* mrow = p.mask_pos + ((size_t)b * p.Hkv + g) * p.C + s_begin;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int key = key0 + u * KPI;
+        const int v = mrow[min(key, cnt - 1)];
+        bf.mp[u] = key < cnt ? v : -1;
       }
     }
     if constexpr (ROPE) {
@@ -852,12 +938,20 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
     }
   }
 
-  // ---- K pass: U keys per lane group per iteration, every key with its own table row;
-  // for up to 6 query heads the next iteration's loads are issued before this
-  // iteration's arithmetic (two register sets alternate)
-  constexpr int U = G <= 4 ? LCD_U2_G4 : (G <= 6 ? LCD_U2_G6 : 2);
-  constexpr int NCS = ROPE ? U : 1;
+  // ---- K pass: U keys per lane group per iteration; for up to 6 query heads the next
+  // iteration's loads are issued before this iteration's arithmetic (two register sets
+  // alternate).  RoPE angles as in the one-pass kernel: one table row per iteration and
+  // angle additions of (cos, sin)(KPI * theta_i) for the following keys, except in waves
+  // that straddle a rank discontinuity, which read every key's row.
+  constexpr int U = G <= 4 ? (ROPE ? LCD_U2_G4R : LCD_U2_G4) : (G <= 6 ? LCD_U2_G6 : 2);
+  constexpr bool REC = ROPE && LCD_REC2;
+  constexpr int NCS = ROPE ? (REC ? 1 : U) : 1;  // table rows held per iteration
   constexpr int STEP = KPI * U;
+  float dc[HALF], ds[HALF];
+  if constexpr (REC) {
+    load_floats<HALF>(p.cos_t + (size_t)KPI * D2 + i0, dc);
+    load_floats<HALF>(p.sin_t + (size_t)KPI * D2 + i0, ds);
+  }
   auto rank_of = [&](int slot) {
     int rank = slot;
     if (p.full && slot >= p.S) {
@@ -866,6 +960,10 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
       rank = p.S + r;
     }
     return rank;
+  };
+  auto load_cs = [&](int rank, float (&c)[HALF], float (&sn)[HALF]) {
+    load_floats<HALF>(p.cos_t + (size_t)rank * D2 + i0, c);
+    load_floats<HALF>(p.sin_t + (size_t)rank * D2 + i0, sn);
   };
   struct KBuf {
     Words<4> lo[U], hi[U];
@@ -881,20 +979,23 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
         const char* row = kbase + (size_t)(s_begin + key) * D * sizeof(T);
         bf.lo[u] = load_words<4>(row + lo_off);
         bf.hi[u] = load_words<4>(row + hi_off);
-        if constexpr (MASKED) bf.mp[u] = p.mask_pos[((size_t)b * p.Hkv + g) * p.C + s_begin + key];
       } else {
         bf.lo[u] = zero_words<4>();
         bf.hi[u] = zero_words<4>();
-        if constexpr (MASKED) bf.mp[u] = -1;
+      }
+    }
+    if constexpr (MASKED) {  // an in-range index for every lane, then a select on the value
+      const int* mrow = p.mask_pos + ((size_t)b * p.Hkv + g) * p.C + s_begin;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int key = key0 + u * KPI;
+        const int v = mrow[min(key, cnt - 1)];
+        bf.mp[u] = key < cnt ? v : -1;
       }
     }
     if constexpr (ROPE) {
 #pragma unroll
-      for (int u = 0; u < NCS; ++u) {
-        const int rank = rank_of(s_begin + min(key0 + u * KPI, cnt - 1));
-        load_floats<HALF>(p.cos_t + (size_t)rank * D2 + i0, bf.c[u]);
-        load_floats<HALF>(p.sin_t + (size_t)rank * D2 + i0, bf.sn[u]);
-      }
+      for (int u = 0; u < NCS; ++u) load_cs(rank_of(s_begin + min(key0 + u * KPI, cnt - 1)), bf.c[u], bf.sn[u]);
     }
   };
   float mx[G];
@@ -902,6 +1003,17 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
   for (int j = 0; j < G; ++j) mx[j] = -INFINITY;
   auto compute_iter = [&](int base, KBuf& bf) {
     const int key0 = base + wave * KPW + kg;
+    bool stepwise = false;  // REC: this wave straddles a rank discontinuity
+    if constexpr (REC) {
+      const int rank0 = rank_of(s_begin + min(key0, cnt - 1));
+      bool disc = false;
+#pragma unroll
+      for (int u = 1; u < U; ++u) {
+        const int key = key0 + u * KPI;
+        disc |= key < cnt && rank_of(s_begin + key) != rank0 + u * KPI;
+      }
+      stepwise = __any(disc);
+    }
     float d[U * G];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -911,10 +1023,25 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
         E::cvt(bf.lo[u], lo);
         E::cvt(bf.hi[u], hi);
         if constexpr (ROPE) {
+          const int ci = REC ? 0 : u;
+          if constexpr (REC) {
+            if (u > 0) {
+              if (stepwise) {
+                load_cs(rank_of(s_begin + min(key0 + u * KPI, cnt - 1)), bf.c[0], bf.sn[0]);
+              } else {
+#pragma unroll
+                for (int e = 0; e < HALF; ++e) {
+                  const float cc = bf.c[0][e] * dc[e] - bf.sn[0][e] * ds[e];
+                  bf.sn[0][e] = bf.sn[0][e] * dc[e] + bf.c[0][e] * ds[e];
+                  bf.c[0][e] = cc;
+                }
+              }
+            }
+          }
 #pragma unroll
           for (int e = 0; e < HALF; ++e) {
-            kf[e] = lo[e] * bf.c[u][e] - hi[e] * bf.sn[u][e];
-            kf[HALF + e] = lo[e] * bf.sn[u][e] + hi[e] * bf.c[u][e];
+            kf[e] = lo[e] * bf.c[ci][e] - hi[e] * bf.sn[ci][e];
+            kf[HALF + e] = lo[e] * bf.sn[ci][e] + hi[e] * bf.c[ci][e];
           }
         } else {
 #pragma unroll
@@ -1098,28 +1225,18 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
 // tokens have pos <= max_pos, ties evicting the newer token.
 __global__ void __launch_bounds__(256) h2o_pick_victim_kernel(const float* score, const int* pos, int* victim, int C,
                                                               int n, int64_t max_pos, int bs) {
-  __shared__ unsigned long long wbest[4];
+  __shared__ unsigned long long wkey[4];
+  __shared__ int wat[4];
   const size_t bg = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  unsigned long long best = ~0ull;
+  const int lane = threadIdx.x & 63;
+  Victim best;
   for (int base = threadIdx.x - lane; base < n; base += 256) {  // wave-uniform bound
     const int i = base + lane;
     const bool in = i < n;
-    fold_victim(best, in ? score[bg * C + i] : 0.f, in ? pos[bg * C + i] : 0, in, max_pos, bs, lane);
+    fold_victim(best, in ? score[bg * C + i] : 0.f, in ? pos[bg * C + i] : 0, i, in, max_pos, bs, lane);
   }
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const unsigned long long other = __shfl_xor(best, off, 64);
-    best = other < best ? other : best;
-  }
-  if (lane == 0) wbest[wave] = best;
-  __syncthreads();
-  best = wbest[0];
-  for (int w = 1; w < 4; ++w) best = wbest[w] < best ? wbest[w] : best;
-  if (best == ~0ull) return;
-  const int win_pos = (int)(0xffffffffu - (uint32_t)(best & 0xffffffffull));
-  for (int i = threadIdx.x; i < n; i += 256)
-    if (pos[bg * C + i] == win_pos) victim[bg] = bs > 1 ? i / bs : i;
+  const Victim v = reduce_victim(best, wkey, wat);
+  if (threadIdx.x == 0 && v.key != ~0ull) victim[bg] = v.at;
 }
 
 hipError_t launch_h2o_pick_victim(const float* score, const int* pos, int* victim, int BHkv, int C, int n,

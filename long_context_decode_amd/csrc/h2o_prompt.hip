@@ -11,14 +11,14 @@
 // each lane 16 keys of one row (lane % 32), and the per-row softmax statistics of pass 1
 // and the per-key sums of pass 2 need no cross-lane work inside the loop.
 //
-//   1. h2o_rowstats_kernel  per (256 prompt rows, query head): Q rows held in registers,
-//                           K streamed through LDS in blocks of 128 (D = 256: 64) keys,
-//                           double buffered, over keys 0 .. last row; running (max, sum
-//                           of 2^(x - max)) per row -> (M_t, 1/L_t).
-//   2. h2o_colsum_kernel    per (256 keys, KV head): K rows in registers, blocks of 128
-//                           (64) rows of the group's query heads and their statistics
-//                           streamed through LDS over rows t >= first key; weights
-//                           2^(x - M_t) / L_t summed per key in a fixed order -> s_j.
+//   1. h2o_rowstats_kernel  per (256 prompt rows, query head; 128 at D = 256): Q rows
+//                           held in registers, K streamed through LDS in blocks of 64
+//                           keys, double buffered, over keys 0 .. last row; running (max,
+//                           sum of 2^(x - max)) per row -> (M_t, 1/L_t).
+//   2. h2o_colsum_kernel    per (256 keys, KV head; 128 at D = 256): K rows in registers,
+//                           blocks of 64 rows of the group's query heads and their
+//                           statistics streamed through LDS over rows t >= first key;
+//                           weights 2^(x - M_t) / L_t summed per key in a fixed order -> s_j.
 //   3. h2o_topk_kernel      per (batch row, KV head): exact selection of the heavy
 //                           hitters on float32 s (radix select over range-relative
 //                           bits, candidates streamed from memory), then an ascending,
@@ -36,7 +36,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 #ifndef LCD_H2OP_TW
-#define LCD_H2OP_TW 1  // register tiles per wave at D <= 128
+#define LCD_H2OP_TW 2  // register tiles per wave at D <= 128
 #endif
 #ifndef LCD_H2OP_BT
 #define LCD_H2OP_BT 2  // 32-row tiles per staged block at D <= 128
@@ -79,11 +79,10 @@ __device__ inline bf16x8 frag_lds(const char* lds, int s, int lane) {
 // B-column lane % 32 (the prompt row).
 __device__ inline int c_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
-// Keys (pass 1) or rows (pass 2) staged per iteration: four 32-row tiles for D = 64, two
-// otherwise (LDS buffers within 2 x 34 KiB, prefetch registers within 32 VGPRs).  With
-// two register tiles per wave (D <= 128) every iteration gives each wave 32 MFMAs (16
-// at D = 256, each twice as long), enough to cover the global loads issued one
-// iteration ahead.
+// Keys (pass 1) or rows (pass 2) staged per iteration: two 32-row tiles (LDS buffers
+// within 2 x 34 KiB, prefetch registers within 32 VGPRs).  With two register tiles per
+// wave (D <= 128) every iteration gives each wave 32 MFMAs (16 at D = 256, each twice as
+// long), enough to cover the global loads issued two iterations ahead.
 template <int D>
 constexpr int block_tiles() { return D == 256 ? 2 : LCD_H2OP_BT; }
 template <int D>
@@ -161,58 +160,52 @@ __global__ void __launch_bounds__(kThreads, 2) h2o_rowstats_kernel(H2oPromptPara
     __syncthreads();  // block kb is in kblk[kb & 1]; every wave is done with block kb - 1
     const char* kl = kblk[kb & 1];
     const int k0 = kb * BR;
-    // (key tile, row tile) pairs the wave computes: some key of the tile is <= some row
-    bool act[BT][TW];
+    // Blocks wholly past the wave's last row are skipped (a wave-uniform test per block).
+    // Otherwise every tile is multiplied, with no test between the MFMAs so that the LDS
+    // reads and MFMAs of the block pipeline; key tiles past a row tile's diagonal (at
+    // most one block per wave) are masked to -inf by the fold like the diagonal itself.
+    if (k0 <= r0 + 32 * TW - 1) {
+      f32x16 acc[BT][TW];
 #pragma unroll
-    for (int t = 0; t < BT; ++t)
+      for (int t = 0; t < BT; ++t)
 #pragma unroll
-      for (int i = 0; i < TW; ++i) act[t][i] = r0 + i * 32 < p.N && k0 + t * 32 <= r0 + i * 32 + 31;
-    // every MFMA of the block first (independent accumulators), then the folds
-    f32x16 acc[BT][TW];
+        for (int i = 0; i < TW; ++i) acc[t][i] = f32x16{};
 #pragma unroll
-    for (int t = 0; t < BT; ++t)
-#pragma unroll
-      for (int i = 0; i < TW; ++i) acc[t][i] = f32x16{};
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-#pragma unroll
-      for (int t = 0; t < BT; ++t) {
-        if (!(act[t][0] || act[t][TW - 1])) continue;
-        const bf16x8 a = frag_lds<D>(kl + t * tile_bytes<D>(), s, lane);
-#pragma unroll
-        for (int i = 0; i < TW; ++i)
-          if (act[t][i]) acc[t][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[i][s], acc[t][i], 0, 0, 0);
-      }
-    // fold the block into each row's (max, sum): the maximum on the raw products (the
-    // scale is positive), masked keys set to -inf, then 2^(acc * scale - max)
-#pragma unroll
-    for (int i = 0; i < TW; ++i) {
-      const int ri = r0 + i * 32;
-      float bm = -INFINITY;
-#pragma unroll
-      for (int t = 0; t < BT; ++t) {
-        if (!act[t][i]) continue;
-        const int kt0 = k0 + t * 32;
-        if (kt0 + 31 > ri) {  // the diagonal tile: key <= row <=> c_row <= row - first key
-          const int dlt = ri + (lane & 31) - kt0;
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (c_row(r, lane) > dlt) acc[t][i][r] = -INFINITY;
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) bm = fmaxf(bm, acc[t][i][r]);
-      }
-      const float mn = fmaxf(m[i], bm * p.qscale);
-      if (mn > -INFINITY) {
-        float add = 0.f;
+      for (int s = 0; s < KS; ++s)
 #pragma unroll
         for (int t = 0; t < BT; ++t) {
-          if (!act[t][i]) continue;
+          const bf16x8 a = frag_lds<D>(kl + t * tile_bytes<D>(), s, lane);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) add += exp2_hw(fmaf(acc[t][i][r], p.qscale, -mn));
+          for (int i = 0; i < TW; ++i) acc[t][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[i][s], acc[t][i], 0, 0, 0);
         }
-        l[i] = l[i] * exp2_hw(m[i] - mn) + add;
-        m[i] = mn;
+      // fold the block into each row's (max, sum): the maximum on the raw products (the
+      // scale is positive), masked keys set to -inf, then 2^(acc * scale - max)
+#pragma unroll
+      for (int i = 0; i < TW; ++i) {
+        const int ri = r0 + i * 32;
+        float bm = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < BT; ++t) {
+          const int kt0 = k0 + t * 32;
+          if (kt0 + 31 > ri) {  // some key of the tile is past some row: key <= row <=> c_row <= row - first key
+            const int dlt = ri + (lane & 31) - kt0;
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (c_row(r, lane) > dlt) acc[t][i][r] = -INFINITY;
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) bm = fmaxf(bm, acc[t][i][r]);
+        }
+        const float mn = fmaxf(m[i], bm * p.qscale);
+        if (mn > -INFINITY) {
+          float add = 0.f;
+#pragma unroll
+          for (int t = 0; t < BT; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) add += exp2_hw(fmaf(acc[t][i][r], p.qscale, -mn));
+          l[i] = l[i] * exp2_hw(m[i] - mn) + add;
+          m[i] = mn;
+        }
       }
     }
     if (kb + 1 < n_blocks) block_store<D>(kblk[(kb + 1) & 1], store_from);
@@ -297,44 +290,40 @@ __global__ void __launch_bounds__(kThreads, 2) h2o_colsum_kernel(H2oPromptParams
     __syncthreads();  // unit u is in buffer u & 1; every wave is done with unit u - 1
     const int row0 = (rb_first + u / G) * BR;
     const char* ql = qblk[u & 1];
-    // (row tile, key tile) pairs the wave computes: some row of the tile sees some key
-    bool act[BT][TW];
+    // Row blocks wholly before the wave's first key are skipped (a wave-uniform test per
+    // block); otherwise every tile is multiplied with no test between the MFMAs, and the
+    // fold masks rows before a key (the diagonal tiles and any tile before it).
+    if (row0 + BR - 1 >= key0) {
+      f32x16 acc[BT][TW];
 #pragma unroll
-    for (int t = 0; t < BT; ++t)
+      for (int t = 0; t < BT; ++t)
 #pragma unroll
-      for (int i = 0; i < TW; ++i) act[t][i] = key0 + i * 32 < p.N && row0 + t * 32 + 31 >= key0 + i * 32;
-    f32x16 acc[BT][TW];
+        for (int i = 0; i < TW; ++i) acc[t][i] = f32x16{};
 #pragma unroll
-    for (int t = 0; t < BT; ++t)
+      for (int s = 0; s < KS; ++s)
 #pragma unroll
-      for (int i = 0; i < TW; ++i) acc[t][i] = f32x16{};
+        for (int t = 0; t < BT; ++t) {
+          const bf16x8 bq = frag_lds<D>(ql + t * tile_bytes<D>(), s, lane);
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
+          for (int i = 0; i < TW; ++i) acc[t][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i][s], bq, acc[t][i], 0, 0, 0);
+        }
 #pragma unroll
       for (int t = 0; t < BT; ++t) {
-        if (!(act[t][0] || act[t][TW - 1])) continue;
-        const bf16x8 bq = frag_lds<D>(ql + t * tile_bytes<D>(), s, lane);
+        const float2 st = qstat[u & 1][t * 32 + (lane & 31)];  // rows past N carry (0, 0): weight 0
+        const int rt0 = row0 + t * 32;
 #pragma unroll
-        for (int i = 0; i < TW; ++i)
-          if (act[t][i]) acc[t][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i][s], bq, acc[t][i], 0, 0, 0);
-      }
+        for (int i = 0; i < TW; ++i) {
+          const int ki = key0 + i * 32;
+          if (rt0 >= ki + 31) {  // every key of the tile is <= every row (wave-uniform)
 #pragma unroll
-    for (int t = 0; t < BT; ++t) {
-      const float2 st = qstat[u & 1][t * 32 + (lane & 31)];  // rows past N carry (0, 0): weight 0
-      const int rt0 = row0 + t * 32;
+            for (int r = 0; r < 16; ++r) col[i][r] = fmaf(exp2_hw(fmaf(acc[t][i][r], p.qscale, -st.x)), st.y, col[i][r]);
+          } else {  // key <= row <=> c_row <= row - first key (none where the tile is wholly before)
+            const int dlt = rt0 + (lane & 31) - ki;
 #pragma unroll
-      for (int i = 0; i < TW; ++i) {
-        if (!act[t][i]) continue;
-        const int ki = key0 + i * 32;
-        if (rt0 >= ki + 31) {  // every key of the tile is <= every row (wave-uniform)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) col[i][r] = fmaf(exp2_hw(fmaf(acc[t][i][r], p.qscale, -st.x)), st.y, col[i][r]);
-        } else {  // the diagonal: key <= row <=> c_row <= row - first key
-          const int dlt = rt0 + (lane & 31) - ki;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float e = exp2_hw(fmaf(acc[t][i][r], p.qscale, -st.x));
-            col[i][r] = c_row(r, lane) <= dlt ? fmaf(e, st.y, col[i][r]) : col[i][r];
+            for (int r = 0; r < 16; ++r) {
+              const float e = exp2_hw(fmaf(acc[t][i][r], p.qscale, -st.x));
+              col[i][r] = c_row(r, lane) <= dlt ? fmaf(e, st.y, col[i][r]) : col[i][r];
+            }
           }
         }
       }

@@ -316,6 +316,12 @@ WORKLOADS = {
         "prefilled to 2048 then 8192 decode steps",
         batch=16, n_q_heads=32, n_kv_heads=32, head_dim=128, dtype="bf16",
         n_sink=4, window=2044, prefill=2048, steps=8192),
+    "llama3_8b_layer": _streaming(
+        "llama3_8b_layer",
+        "Llama-3-8B-shaped decode layer: B=16, 32 q / 8 kv heads, D=128, bf16, 4 sinks + 8188 ring, "
+        "prefilled to 8192 then 1024 decode steps",
+        batch=16, n_q_heads=32, n_kv_heads=8, head_dim=128, dtype="bf16", rope_base=500000.0,
+        n_sink=4, window=8188, prefill=8192, steps=1024),
     "gqa_long": _streaming(
         "gqa_long",
         "GQA long-cache decode: B=16, 24 q / 4 kv heads, D=256, bf16, 16 attention layers, "

@@ -151,6 +151,15 @@ def test_llama2_layer_full_size_sampled(L):
     print(f"  worst abs err {worst:.2e}")
 
 
+def test_llama3_layer_full_size_sampled(L):
+    """B=16, 32/8 heads (G=4), D=128, 4+8188, RoPE base 5e5: prefill 8192, then wrapped steps."""
+    w = WORKLOADS["llama3_8b_layer"]
+    checks = {0, 1, 37}
+    print(f"[llama3_8b_layer] {w.title}; checks {sorted(checks)}", flush=True)
+    worst = _run_stream(L, w, checks, sample_bg=[(0, 0), (15, 7), (9, 3)])
+    print(f"  worst abs err {worst:.2e}")
+
+
 def test_gqa_long_full_size_sampled(L):
     """B=16, 24/4 heads, D=256, 4+32764, 16 layers allocated; layers 0 and 15 checked."""
     w = WORKLOADS["gqa_long"]
