@@ -62,14 +62,12 @@ struct bf16_t {
 #ifndef LCD_H2O_EU
 #define LCD_H2O_EU 16  // token-level H2O epilogue: slots per thread per iteration (4 for blocks)
 #endif
-#ifndef LCD_OP_MINB
-#define LCD_OP_MINB 1  // one-pass kernel: minimum resident workgroups per CU the registers must allow
-#endif
 #ifndef LCD_REC2
 #define LCD_REC2 1  // two-pass kernel: RoPE angles by angle addition within an iteration
 #endif
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 // W 32-bit words of one row piece, loaded in one instruction (W = 4: 16 bytes, W = 2: 8).
@@ -525,7 +523,7 @@ __device__ inline void split_finish(const DecodeParams& p, float* ored, const fl
 // For up to 2 query heads per KV head (registers hold the queries and the outputs
 // together).
 template <typename T, int D, int G, int MODE>
-__global__ void __launch_bounds__(kDecodeThreads, LCD_OP_MINB) decode_onepass_kernel(DecodeParams p) {
+__global__ void __launch_bounds__(kDecodeThreads) decode_onepass_kernel(DecodeParams p) {
   constexpr bool ROPE = MODE == kModeRope;
   constexpr bool LOGITS = MODE == kModePlainLogits || MODE == kModeMaskedLogits;
   constexpr bool MASKED = MODE == kModeMaskedLogits;
@@ -564,11 +562,19 @@ __global__ void __launch_bounds__(kDecodeThreads, LCD_OP_MINB) decode_onepass_ke
   const size_t lo_off = (size_t)i0 * sizeof(T);
   const size_t hi_off = (size_t)(D2 + i0) * sizeof(T);
 
-  // ---- queries of the group: load, rotate at the query's position, pre-scale
+  // ---- queries of the group: load, rotate at the query's position, pre-scale (without
+  // RoPE, bf16 queries stay packed for v_dot2_f32_bf16, as in the two-pass kernel)
+  constexpr bool DOT2 = !ROPE && sizeof(T) == 2;
   float qf[G][EPL];
+  Words<W> qlo[G], qhi[G];
 #pragma unroll
   for (int j = 0; j < G; ++j) {
     const char* qrow = reinterpret_cast<const char*>(p.q) + ((size_t)b * p.Hq + g * G + j) * D * sizeof(T);
+    if constexpr (DOT2) {
+      qlo[j] = load_words<W>(qrow + lo_off);
+      qhi[j] = load_words<W>(qrow + hi_off);
+      continue;
+    }
     float lo[HALF], hi[HALF];
     E::cvt(load_words<W>(qrow + lo_off), lo);
     E::cvt(load_words<W>(qrow + hi_off), hi);
@@ -686,6 +692,21 @@ __global__ void __launch_bounds__(kDecodeThreads, LCD_OP_MINB) decode_onepass_ke
     float d[U * G];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      if constexpr (DOT2) {
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+          float acc = 0.f;
+#pragma unroll
+          for (int w = 0; w < W; ++w) {
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qlo[j].w[w]),
+                                                  __builtin_bit_cast(bf16x2, bf.klo[u].w[w]), acc, false);
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qhi[j].w[w]),
+                                                  __builtin_bit_cast(bf16x2, bf.khi[u].w[w]), acc, false);
+          }
+          d[u * G + j] = acc;
+        }
+        continue;
+      }
       float kf[EPL];
       {
         float lo[HALF], hi[HALF];
@@ -729,6 +750,10 @@ __global__ void __launch_bounds__(kDecodeThreads, LCD_OP_MINB) decode_onepass_ke
       }
     }
     group_sum_n<LPK, U * G>(d);
+    if constexpr (DOT2) {
+#pragma unroll
+      for (int i = 0; i < U * G; ++i) d[i] *= p.qscale;
+    }
 
     // mask the keys past the range, record logits (H2O), new running maxima
     float mn[G];
@@ -793,7 +818,7 @@ __global__ void __launch_bounds__(kDecodeThreads, LCD_OP_MINB) decode_onepass_ke
   };
 
   // ---- the pass: two register sets alternate, the next iteration's loads are issued
-  // before this iteration's arithmetic
+  // before this iteration's arithmetic (a third set measured no faster)
   {
     Buf A, B;
     load_iter(0, A);
@@ -912,11 +937,20 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
   const size_t lo_off = (size_t)i0 * sizeof(T);
   const size_t hi_off = (size_t)(D2 + i0) * sizeof(T);
 
-  // ---- queries of the group: load, rotate at the query's position, pre-scale
+  // ---- queries of the group: load, rotate at the query's position, pre-scale.  Without
+  // RoPE, bf16 queries stay packed: the K pass takes exact bf16 x bf16 pair products
+  // with float32 sums (v_dot2_f32_bf16) and scales after the lane-group reduction.
+  constexpr bool DOT2 = !ROPE && sizeof(T) == 2;
   float qf[G][EPL];
+  Words<4> qlo[G], qhi[G];
 #pragma unroll
   for (int j = 0; j < G; ++j) {
     const char* qrow = reinterpret_cast<const char*>(p.q) + ((size_t)b * p.Hq + g * G + j) * D * sizeof(T);
+    if constexpr (DOT2) {
+      qlo[j] = load_words<4>(qrow + lo_off);
+      qhi[j] = load_words<4>(qrow + hi_off);
+      continue;
+    }
     float lo[HALF], hi[HALF];
     E::cvt(load_words<4>(qrow + lo_off), lo);
     E::cvt(load_words<4>(qrow + hi_off), hi);
@@ -1017,6 +1051,21 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
     float d[U * G];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      if constexpr (DOT2) {
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+          float acc = 0.f;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qlo[j].w[w]),
+                                                  __builtin_bit_cast(bf16x2, bf.lo[u].w[w]), acc, false);
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qhi[j].w[w]),
+                                                  __builtin_bit_cast(bf16x2, bf.hi[u].w[w]), acc, false);
+          }
+          d[u * G + j] = acc;
+        }
+        continue;
+      }
       float kf[EPL];
       {
         float lo[HALF], hi[HALF];
@@ -1060,6 +1109,10 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
       }
     }
     group_sum_n<LPK, U * G>(d);
+    if constexpr (DOT2) {
+#pragma unroll
+      for (int i = 0; i < U * G; ++i) d[i] *= p.qscale;
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int key = key0 + u * KPI;

@@ -100,6 +100,16 @@ def test_h2o_from_empty_small(L):
     assert compared >= 4 * 150 and ev > 100
 
 
+def test_h2o_one_pass_kernel_g2(L):
+    """G=2, bf16, D=128 (the one-pass kernel's logits path), budget 96 over 250 steps."""
+    w = scaled(WORKLOADS["h2o_128k"], name="h2o_g2", batch=2, n_q_heads=4, n_kv_heads=2, n_prompt=0,
+               budget=96, n_recent=12, steps=250)
+    sample = [(b, g) for b in range(2) for g in range(2)]
+    compared, ev = _run(L, w, 250, sample, seeded=False)
+    print(f"[h2o G=2] compared {compared} head-steps, {ev} evictions")
+    assert compared >= 4 * 150 and ev > 100
+
+
 def test_h2o_sliding_window_case(L):
     # n_recent == budget: the oldest token is always the victim
     w = scaled(WORKLOADS["h2o_128k"], name="h2o_window", batch=1, n_q_heads=4, n_kv_heads=1, head_dim=64,
