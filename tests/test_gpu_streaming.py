@@ -140,6 +140,15 @@ def test_bf16_shapes(L, G, D, S, W, pre, steps):
     _run_stream(L, w, checks, sample_bg=[(0, 0), (1, 1)], check_slots=True)
 
 
+def test_many_splits_grouped_merge(L):
+    """B=1, 4/1 heads, D=128, 4+8188 wrapped: the plan gives more than 64 splits of one
+    (row, KV head), so the merge stages its per-split weights in more than one group."""
+    w = scaled(WORKLOADS["llama2_7b_layer"], name="bf16_many_splits", batch=1, n_kv_heads=1, n_q_heads=4,
+               n_sink=4, window=8188, prefill=8200, steps=3)
+    print("[many splits] B=1, 4/1 heads, 4+8188", flush=True)
+    _run_stream(L, w, {0, 2}, sample_bg=[(0, 0)])
+
+
 def test_llama2_layer_full_size_sampled(L):
     """B=16, 32/32 heads, D=128, 4+2044: prefill 2048, decode through two ring wraps."""
     w = WORKLOADS["llama2_7b_layer"]
