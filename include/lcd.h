@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define LCD_ABI_VERSION 2
+#define LCD_ABI_VERSION 3
 
 typedef enum lcd_status {
   LCD_OK = 0,
@@ -199,6 +199,21 @@ lcd_status lcd_kv_append(lcd_cache* cache, int32_t layer, const void* k, const v
  * holds no token. */
 lcd_status lcd_decode_attn(lcd_cache* cache, int32_t layer, const void* q, float* out, void* ws,
                            uint64_t ws_bytes, void* stream);
+
+/* decode_step: lcd_kv_append of one token followed by lcd_decode_attn, in one
+ * launch ([KVL] "01 · Conceito": a decode step appends the token's k_t, v_t and
+ * attends its q_t over the cache that now holds them).
+ *   k, v   device, [batch][n_kv_heads][head_dim] in the cache dtype: the new token's
+ *          rows (un-rotated).
+ *   q, out, ws  as lcd_decode_attn.
+ * The workgroup whose slot range holds the new token's slot reads the rows from k and
+ * v and writes them into that slot; the cache contents and the output equal those of
+ * the two calls (the same arithmetic in the same order).  SINK_RING and APPEND only
+ * (others LCD_EUNSUPPORTED); APPEND needs a free slot (else LCD_ECAPACITY).  Advances
+ * the layer's token counter by one; on an error nothing is enqueued and the counters
+ * are unchanged. */
+lcd_status lcd_decode_step(lcd_cache* cache, int32_t layer, const void* k, const void* v, const void* q,
+                           float* out, void* ws, uint64_t ws_bytes, void* stream);
 
 /* Host-side queries (pure host functions, no HIP call; -1 on invalid arguments).
  *   lcd_kv_tokens   tokens appended so far to `layer` (int64 counter).

@@ -20,6 +20,7 @@ from ._lib import (  # noqa: F401
     cache_config,
     cache_sizes,
     decode_attn,
+    decode_step,
     kv_append,
     kv_cache_destroy,
     kv_cache_init,

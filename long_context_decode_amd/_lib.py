@@ -78,6 +78,7 @@ _SIGS = {
     "lcd_kv_cache_destroy": (None, [_P]),
     "lcd_kv_append": (_S, [_P, _I32, _P, _P, _I32, _P]),
     "lcd_decode_attn": (_S, [_P, _I32, _P, _P, _P, _U64, _P]),
+    "lcd_decode_step": (_S, [_P, _I32, _P, _P, _P, _P, _P, _U64, _P]),
     "lcd_kv_tokens": (_I64, [_P, _I32]),
     "lcd_kv_filled": (_I64, [_P, _I32]),
     "lcd_kv_slot_of": (_I64, [_P, _I32, _I64]),
@@ -173,6 +174,12 @@ def decode_attn(h, layer, q, out, ws, ws_bytes, stream=None):
     _check(lib.lcd_decode_attn(h, layer, _ptr(q), _ptr(out), _ptr(ws), ws_bytes, _stream(stream)))
 
 
+def decode_step(h, layer, k, v, q, out, ws, ws_bytes, stream=None):
+    """Append one token (k, v: [B][H_kv][D]) and attend q over the cache, one launch."""
+    _check(lib.lcd_decode_step(h, layer, _ptr(k), _ptr(v), _ptr(q), _ptr(out), _ptr(ws), ws_bytes,
+                               _stream(stream)))
+
+
 def kv_tokens(h, layer):
     return lib.lcd_kv_tokens(h, layer)
 
@@ -264,6 +271,10 @@ class KVCache:
 
     def decode(self, layer, q, out, stream=None):
         decode_attn(self.handle, layer, q, out, self.ws, self.ws_bytes, stream)
+
+    def step(self, layer, k, v, q, out, stream=None):
+        """Fused append of one token (k, v: [B][H_kv][D]) and decode."""
+        decode_step(self.handle, layer, k, v, q, out, self.ws, self.ws_bytes, stream)
 
     def layer_tensors(self, layer):
         """(K, V) views of one layer as [B][H_kv][C][D] torch tensors, at the addresses

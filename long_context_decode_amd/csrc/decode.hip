@@ -367,6 +367,24 @@ __device__ inline Victim reduce_victim(Victim v, unsigned long long* wk, int* wa
   return r;
 }
 
+// Fused append: the workgroup whose slot range [s_begin, s_begin + cnt) holds the new
+// token's slot writes its K and V rows into the cache (16-byte pieces, one per thread).
+// The launch never reads that slot from the cache: its loads take the input rows.
+template <typename T, int D>
+__device__ inline void write_new_rows(const DecodeParams& p, int b, int g, int s_begin, int cnt) {
+  if (p.new_slot < s_begin || p.new_slot >= s_begin + cnt) return;
+  constexpr int PIECES = D * (int)sizeof(T) / 16;  // per row
+  const size_t src = ((size_t)b * p.Hkv + g) * D * sizeof(T);
+  const size_t dst = (((size_t)b * p.Hkv + g) * p.C + p.new_slot) * D * sizeof(T);
+  for (int i = threadIdx.x; i < 2 * PIECES; i += kDecodeThreads) {
+    const bool is_v = i >= PIECES;
+    const int piece = is_v ? i - PIECES : i;
+    const char* from = reinterpret_cast<const char*>(is_v ? p.v_new : p.k_new) + src + 16 * piece;
+    char* to = reinterpret_cast<char*>(is_v ? p.v : p.k) + dst + 16 * piece;
+    *reinterpret_cast<u32x4*>(to) = *reinterpret_cast<const u32x4*>(from);
+  }
+}
+
 // ---------------------------------------------------------------- split finish
 // The end of a decode workgroup: ored[0 .. G*D) (LDS, at least 64 * G floats) holds its
 // range's unnormalised output and Mh / Lh (LDS) its maximum and sum per query head.  With
@@ -561,6 +579,10 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_onepass_kernel(DecodePa
   const char* vbase = hv.v;
   const size_t lo_off = (size_t)i0 * sizeof(T);
   const size_t hi_off = (size_t)(D2 + i0) * sizeof(T);
+  // fused append: the new token's rows come from the input (the slot is written below)
+  const int new_key = p.new_slot - s_begin;  // key index of the new slot (outside 0..cnt-1 if none here)
+  const size_t new_row = ((size_t)b * p.Hkv + g) * D * sizeof(T);
+  write_new_rows<T, D>(p, b, g, s_begin, cnt);
 
   // ---- queries of the group: load, rotate at the query's position, pre-scale (without
   // RoPE, bf16 queries stay packed for v_dot2_f32_bf16, as in the two-pass kernel)
@@ -637,11 +659,15 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_onepass_kernel(DecodePa
     for (int u = 0; u < U; ++u) {
       const int key = key0 + u * KPI;
       if (key < cnt) {
-        const size_t roff = (size_t)(s_begin + key) * D * sizeof(T);
-        bf.klo[u] = load_words<W>(kbase + roff + lo_off);
-        bf.khi[u] = load_words<W>(kbase + roff + hi_off);
-        bf.vlo[u] = load_words<W>(vbase + roff + lo_off);
-        bf.vhi[u] = load_words<W>(vbase + roff + hi_off);
+        const bool fresh = key == new_key;
+        const char* krow = fresh ? reinterpret_cast<const char*>(p.k_new) + new_row
+                                 : kbase + (size_t)(s_begin + key) * D * sizeof(T);
+        const char* vrow = fresh ? reinterpret_cast<const char*>(p.v_new) + new_row
+                                 : vbase + (size_t)(s_begin + key) * D * sizeof(T);
+        bf.klo[u] = load_words<W>(krow + lo_off);
+        bf.khi[u] = load_words<W>(krow + hi_off);
+        bf.vlo[u] = load_words<W>(vrow + lo_off);
+        bf.vhi[u] = load_words<W>(vrow + hi_off);
       } else {
         bf.klo[u] = zero_words<W>();
         bf.khi[u] = zero_words<W>();
@@ -936,6 +962,10 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
   const char* vbase = hv.v;
   const size_t lo_off = (size_t)i0 * sizeof(T);
   const size_t hi_off = (size_t)(D2 + i0) * sizeof(T);
+  // fused append: the new token's rows come from the input (the slot is written below)
+  const int new_key = p.new_slot - s_begin;  // key index of the new slot (outside 0..cnt-1 if none here)
+  const size_t new_row = ((size_t)b * p.Hkv + g) * D * sizeof(T);
+  write_new_rows<T, D>(p, b, g, s_begin, cnt);
 
   // ---- queries of the group: load, rotate at the query's position, pre-scale.  Without
   // RoPE, bf16 queries stay packed: the K pass takes exact bf16 x bf16 pair products
@@ -1010,7 +1040,8 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
     for (int u = 0; u < U; ++u) {
       const int key = key0 + u * KPI;
       if (key < cnt) {
-        const char* row = kbase + (size_t)(s_begin + key) * D * sizeof(T);
+        const char* row = key == new_key ? reinterpret_cast<const char*>(p.k_new) + new_row
+                                         : kbase + (size_t)(s_begin + key) * D * sizeof(T);
         bf.lo[u] = load_words<4>(row + lo_off);
         bf.hi[u] = load_words<4>(row + hi_off);
       } else {
@@ -1165,7 +1196,8 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
     for (int u = 0; u < UV; ++u) {
       const int key = base + u * KPI + wave * KPW + kg;
       if (key < cnt) {
-        const char* row = vbase + (size_t)(s_begin + key) * D * sizeof(T);
+        const char* row = key == new_key ? reinterpret_cast<const char*>(p.v_new) + new_row
+                                         : vbase + (size_t)(s_begin + key) * D * sizeof(T);
         vlo[u] = load_words<4>(row + lo_off);
         vhi[u] = load_words<4>(row + hi_off);
       } else {

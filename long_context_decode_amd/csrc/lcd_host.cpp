@@ -481,16 +481,25 @@ lcd_status lcd_kv_append(lcd_cache* c, int32_t layer, const void* k, const void*
   return ok();
 }
 
-lcd_status lcd_decode_attn(lcd_cache* c, int32_t layer, const void* q, float* out, void* ws, uint64_t ws_bytes,
-                           void* stream) {
-  lcd_status st = check_layer(c, layer);
-  if (st) return st;
+}  // extern "C"
+
+namespace {
+
+// Checks shared by lcd_decode_attn and lcd_decode_step.
+lcd_status check_decode_args(const lcd_cache* c, const void* q, const float* out, const void* ws,
+                             uint64_t ws_bytes) {
   if (!q || !out || !ws) return fail(LCD_EINVAL, "q, out or ws is NULL");
   if (!aligned16(q) || !aligned16(out) || !aligned16(ws)) return fail(LCD_EALIGN, "q, out or ws not 16-byte aligned");
   if (ws_bytes < c->L.ws_bytes)
     return fail(LCD_ESIZE, "ws_bytes %llu < required %llu", (unsigned long long)ws_bytes,
                 (unsigned long long)c->L.ws_bytes);
-  if (c->tokens[layer] < 1 || c->filled[layer] < 1) return fail(LCD_EINVAL, "layer %d holds no token", layer);
+  return LCD_OK;
+}
+
+// One decode launch over the layer's current state; with new_slot >= 0 the kernel also
+// writes the token's rows k_new / v_new into that slot (fused append).
+lcd_status launch_decode(lcd_cache* c, int32_t layer, const void* q, float* out, void* ws, void* stream,
+                         const void* k_new, const void* v_new, int new_slot) {
   const lcd_cache_config& cfg = c->cfg;
   const Layout& L = c->L;
   const int n = (int)c->filled[layer];
@@ -553,6 +562,9 @@ lcd_status lcd_decode_attn(lcd_cache* c, int32_t layer, const void* q, float* ou
   }
   p.out = out;
   p.arrivals = c->arrivals(layer);
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.new_slot = new_slot;
   if (cfg.policy == LCD_H2O) {
     p.score = c->score(layer);
     p.pos = c->pos(layer);
@@ -568,6 +580,54 @@ lcd_status lcd_decode_attn(lcd_cache* c, int32_t layer, const void* q, float* ou
       lcd::launch_decode_split(cfg.dtype, cfg.head_dim, L.G, mode, p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+lcd_status lcd_decode_attn(lcd_cache* c, int32_t layer, const void* q, float* out, void* ws, uint64_t ws_bytes,
+                           void* stream) {
+  lcd_status st = check_layer(c, layer);
+  if (st) return st;
+  if ((st = check_decode_args(c, q, out, ws, ws_bytes))) return st;
+  if (c->tokens[layer] < 1 || c->filled[layer] < 1) return fail(LCD_EINVAL, "layer %d holds no token", layer);
+  return launch_decode(c, layer, q, out, ws, stream, nullptr, nullptr, -1);
+}
+
+lcd_status lcd_decode_step(lcd_cache* c, int32_t layer, const void* k, const void* v, const void* q, float* out,
+                           void* ws, uint64_t ws_bytes, void* stream) {
+  lcd_status st = check_layer(c, layer);
+  if (st) return st;
+  if (c->cfg.policy != LCD_SINK_RING && c->cfg.policy != LCD_APPEND)
+    return fail(LCD_EUNSUPPORTED, "decode_step is defined for the SINK_RING and APPEND caches");
+  if (!k || !v) return fail(LCD_EINVAL, "k or v is NULL");
+  if (!aligned16(k) || !aligned16(v)) return fail(LCD_EALIGN, "k or v is not 16-byte aligned");
+  if ((st = check_decode_args(c, q, out, ws, ws_bytes))) return st;
+  const int64_t t = c->tokens[layer];
+  const int C = c->L.C;
+  int slot;
+  int64_t filled;
+  if (c->cfg.policy == LCD_SINK_RING) {
+    const int64_t S = c->cfg.n_sink, W = c->cfg.window;
+    slot = (int)(t < S ? t : S + (t - S) % W);
+    filled = std::min<int64_t>(t + 1, C);
+  } else {
+    if (c->filled[layer] + 1 > C)
+      return fail(LCD_ECAPACITY, "append of 1 row to %lld filled of capacity %d", (long long)c->filled[layer], C);
+    slot = (int)c->filled[layer];
+    filled = c->filled[layer] + 1;
+  }
+  // the launch sees the state after the append
+  const int64_t t_prev = c->tokens[layer], f_prev = c->filled[layer];
+  c->tokens[layer] = t + 1;
+  c->filled[layer] = filled;
+  st = launch_decode(c, layer, q, out, ws, stream, k, v, slot);
+  if (st) {  // nothing was enqueued: keep the bookkeeping as it was
+    c->tokens[layer] = t_prev;
+    c->filled[layer] = f_prev;
+  }
+  return st;
 }
 
 int64_t lcd_kv_tokens(const lcd_cache* c, int32_t layer) {

@@ -20,8 +20,8 @@ enum DecodeMode { kModeRope = 0, kModePlain = 1, kModePlainLogits = 2, kModeMask
 constexpr int kMaxDuoHeads = 128;
 
 struct DecodeParams {
-  const void* k;       // layer K [B][Hkv][C][D] (cache dtype)
-  const void* v;       // layer V
+  void* k;             // layer K [B][Hkv][C][D] (cache dtype; written only by a fused append)
+  void* v;             // layer V
   const void* q;       // [B][Hq][D]
   const float* cos_t;  // [C][D/2] (rope mode)
   const float* sin_t;
@@ -58,6 +58,12 @@ struct DecodeParams {
   int16_t duo_ret[kMaxDuoHeads];
   int16_t duo_str[kMaxDuoHeads];
   int ring_head;       // ring index of the oldest window token (rope mode, full)
+  // fused append (new_slot >= 0): the token's K / V rows ([B][Hkv][D], cache dtype) are
+  // read from k_new / v_new for slot new_slot and written there by the workgroup whose
+  // range holds it; no workgroup reads that slot from the cache
+  const void* k_new;
+  const void* v_new;
+  int new_slot;
   int q_rank;          // in-cache position of the query (rope mode)
   float qscale;        // logit scale * log2(e)
 };

@@ -57,8 +57,9 @@ def _assert_close(got, ref, atol, where):
     return err.max(), row.max()
 
 
-def _run_stream(L, w, check_steps, sample_bg, layers=None, check_slots=False):
-    """Prefill w.prefill tokens in one bulk append, then decode w.steps tokens."""
+def _run_stream(L, w, check_steps, sample_bg, layers=None, check_slots=False, fused=False):
+    """Prefill w.prefill tokens in one bulk append, then decode w.steps tokens (with
+    fused=True each step is one lcd_decode_step instead of kv_append + decode_attn)."""
     dev = "cuda"
     layers = list(range(w.n_layers)) if layers is None else layers
     cache = L.KVCache(_cfg(L, w))
@@ -78,8 +79,11 @@ def _run_stream(L, w, check_steps, sample_bg, layers=None, check_slots=False):
     for s in range(steps):
         t = w.prefill + s
         for layer in layers:
-            cache.append(layer, k_all[layer][s].unsqueeze(2), v_all[layer][s].unsqueeze(2))
-            cache.decode(layer, q_all[layer][s], out)
+            if fused:
+                cache.step(layer, k_all[layer][s], v_all[layer][s], q_all[layer][s], out)
+            else:
+                cache.append(layer, k_all[layer][s].unsqueeze(2), v_all[layer][s].unsqueeze(2))
+                cache.decode(layer, q_all[layer][s], out)
             if s in check_steps:
                 got = out.cpu().numpy().astype(np.float64)
                 G = w.group
@@ -138,6 +142,32 @@ def test_bf16_shapes(L, G, D, S, W, pre, steps):
     checks = {0, 1, steps - 1} | {s for s in range(steps) if (pre + s) % W in (0, 1, W - 1)}
     print(f"[bf16 G={G} D={D} S={S} W={W} prefill={pre}] checks {sorted(checks)}", flush=True)
     _run_stream(L, w, checks, sample_bg=[(0, 0), (1, 1)], check_slots=True)
+
+
+def test_llama2_layer_full_size_fused_step(L):
+    """The benchmarked step: one lcd_decode_step per token (append fused into the decode
+    launch) on the full Llama-2-shaped layer, sampled heads against the oracle, ring slots
+    checked bit for bit."""
+    w = scaled(WORKLOADS["llama2_7b_layer"], steps=2050)
+    checks = {0, 1, 2043, 2044, 2049}
+    print(f"[llama2_7b_layer fused] checks {sorted(checks)}", flush=True)
+    rng = np.random.default_rng(1)
+    sample = [(0, 0), (15, 31)] + [tuple(x) for x in rng.integers(0, [16, 32], (2, 2))]
+    worst = _run_stream(L, w, checks, sample_bg=sample, fused=True)
+    print(f"  worst abs err {worst:.2e}")
+
+
+@pytest.mark.parametrize("G,D,S,W,pre,steps", [
+    (4, 128, 4, 252, 100, 200),   # growth phase then wrap, two-pass kernel
+    (6, 256, 4, 1020, 1100, 12),  # D=256, several splits
+    (1, 64, 2, 190, 0, 260),      # from empty
+])
+def test_fused_step_bf16_shapes(L, G, D, S, W, pre, steps):
+    w = scaled(WORKLOADS["llama2_7b_layer"], name=f"fused_G{G}_D{D}", batch=2, n_kv_heads=2,
+               n_q_heads=2 * G, head_dim=D, n_sink=S, window=W, prefill=pre, steps=steps)
+    checks = {0, 1, steps - 1} | {s for s in range(steps) if (pre + s) % W in (0, 1, W - 1)}
+    print(f"[fused bf16 G={G} D={D} S={S} W={W} prefill={pre}] checks {sorted(checks)}", flush=True)
+    _run_stream(L, w, checks, sample_bg=[(0, 0), (1, 1)], check_slots=True, fused=True)
 
 
 def test_many_splits_grouped_merge(L):
