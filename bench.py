@@ -228,12 +228,31 @@ class _Stepper:
         self.i = 0
         torch.cuda.synchronize()
 
+    @property
+    def fused(self):
+        """Streaming caches run one lcd_decode_step launch per layer and token."""
+        return self.w.kind == "streaming"
+
     def step(self):
         i = self.i
         for l in range(self.w.n_layers):
-            self.cache.append(l, self.k[l][i].unsqueeze(2), self.v[l][i].unsqueeze(2))
-            self.cache.decode(l, self.q[l][i], self.out)
+            if self.fused:
+                self.cache.step(l, self.k[l][i], self.v[l][i], self.q[l][i], self.out)
+            else:
+                self.cache.append(l, self.k[l][i].unsqueeze(2), self.v[l][i].unsqueeze(2))
+                self.cache.decode(l, self.q[l][i], self.out)
         self.i += 1
+
+    def launch(self, j):
+        """The decode launch alone, for timing: a fused step re-appending staged token
+        j % staged (the ring advances; the data do not change the work), else decode_attn
+        on the current state."""
+        l = j % self.w.n_layers
+        if self.fused:
+            t = j % self.q[l].shape[0]
+            self.cache.step(l, self.k[l][t], self.v[l][t], self.q[l][t], self.out)
+        else:
+            self.cache.decode(l, self.q[l][0], self.out)
 
     def launch_bytes(self):
         """Algorithmic bytes of one decode_attn launch (one layer)."""
@@ -254,11 +273,13 @@ class _Stepper:
             if w.block_size > 1:
                 state += w.batch * w.n_kv_heads * self.slots * 4  # positions read again to skip emptied slots
             return kv + io + logits + state
+        if self.fused:  # the new rows are read from the input instead of the cache, then written
+            return kv + io + 2 * w.batch * w.n_kv_heads * w.head_dim * w.esize
         return kv + io
 
     def step_bytes(self):
         w = self.w
-        append = 2 * w.batch * w.n_kv_heads * w.head_dim * w.esize
+        append = 0 if self.fused else 2 * w.batch * w.n_kv_heads * w.head_dim * w.esize
         return w.n_layers * (self.launch_bytes() + append)
 
 
@@ -277,16 +298,15 @@ def _decode_bench(L, w, steps, warmup, launch_batches=4, launch_batch=64):
     end.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
-    # decode kernel duration: batches of back-to-back decode_attn launches on the state the
-    # steps left (every launch reads the full cache), one event pair per batch on the
-    # launch stream
-    nl = w.n_layers
+    # decode kernel duration: batches of back-to-back decode launches (fused steps for
+    # streaming caches) on the state the steps left (every launch reads the full cache),
+    # one event pair per batch on the launch stream
     batch_ms = []
     for _ in range(launch_batches):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for i in range(launch_batch):
-            st.cache.decode(i % nl, st.q[i % nl][0], st.out)
+            st.launch(i)
         b.record()
         torch.cuda.synchronize()
         batch_ms.append(a.elapsed_time(b) / launch_batch)
@@ -477,7 +497,7 @@ def main(argv=None):
                    "cache_slots": w.n_sink + w.window if w.kind == "streaming" else w.budget},
         "hbm_tb_s": round(r["step_bytes"] * r["steps_per_s"] / 1e12, 3),
         "hbm_frac_of_peak": round(r["step_bytes"] * r["steps_per_s"] / HBM_PEAK, 4),
-        "roofline": {"bound": "hbm", "kernel": DECODE_KERNEL + " (lcd_decode_attn)",
+        "roofline": {"bound": "hbm", "kernel": DECODE_KERNEL + " (lcd_decode_step)",
                      "achieved": round(achieved / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK, 4),
                      "traffic": _traffic() if a.workload == "llama2_7b_layer" else None,
