@@ -147,6 +147,12 @@ __device__ inline void load_floats(const float* p, float (&x)[N]) {
   }
 }
 
+// Waits for every outstanding vector-memory load of this wave (s_waitcnt vmcnt(0), other
+// counters untouched).  Placed inside a rarely taken branch that loads registers the
+// code after the branch reads, it keeps the compiler from waiting for all loads (those of
+// the next iteration included) on the common path, where it merges the branch's state.
+__device__ inline void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // DPP lane moves inside 16-lane rows (no LDS traffic).
 constexpr int kDppXor1 = 0xB1;          // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;          // quad_perm [2,3,0,1]
@@ -657,23 +663,19 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_onepass_kernel(DecodePa
     const int key0 = base + wave * KPW + kg;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int key = key0 + u * KPI;
-      if (key < cnt) {
-        const bool fresh = key == new_key;
-        const char* krow = fresh ? reinterpret_cast<const char*>(p.k_new) + new_row
-                                 : kbase + (size_t)(s_begin + key) * D * sizeof(T);
-        const char* vrow = fresh ? reinterpret_cast<const char*>(p.v_new) + new_row
-                                 : vbase + (size_t)(s_begin + key) * D * sizeof(T);
-        bf.klo[u] = load_words<W>(krow + lo_off);
-        bf.khi[u] = load_words<W>(krow + hi_off);
-        bf.vlo[u] = load_words<W>(vrow + lo_off);
-        bf.vhi[u] = load_words<W>(vrow + hi_off);
-      } else {
-        bf.klo[u] = zero_words<W>();
-        bf.khi[u] = zero_words<W>();
-        bf.vlo[u] = zero_words<W>();
-        bf.vhi[u] = zero_words<W>();
-      }
+      // keys past the range load the range's last row (their logits are masked and their
+      // weights are 0): no branch around the loads, so the compiler counts this set's
+      // loads exactly and leaves them in flight while the previous set is consumed
+      const int key = min(key0 + u * KPI, cnt - 1);
+      const bool fresh = key == new_key;
+      const char* krow = fresh ? reinterpret_cast<const char*>(p.k_new) + new_row
+                               : kbase + (size_t)(s_begin + key) * D * sizeof(T);
+      const char* vrow = fresh ? reinterpret_cast<const char*>(p.v_new) + new_row
+                               : vbase + (size_t)(s_begin + key) * D * sizeof(T);
+      bf.klo[u] = load_words<W>(krow + lo_off);
+      bf.khi[u] = load_words<W>(krow + hi_off);
+      bf.vlo[u] = load_words<W>(vrow + lo_off);
+      bf.vhi[u] = load_words<W>(vrow + hi_off);
     }
     if constexpr (MASKED) {  // an in-range index for every lane, then a select on the value
       const int* mrow = p.mask_pos + ((size_t)b * p.Hkv + g) * p.C + s_begin;
@@ -744,6 +746,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_onepass_kernel(DecodePa
             if (u > 0) {
               if (stepwise) {
                 load_cs(rank_of(s_begin + min(key0 + u * KPI, cnt - 1)), bf.c[0], bf.sn[0]);
+                wait_loads();  // complete here, so the common path keeps the next set's loads in flight
               } else {
 #pragma unroll
                 for (int e = 0; e < HALF; ++e) {
@@ -849,10 +852,10 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_onepass_kernel(DecodePa
     Buf A, B;
     load_iter(0, A);
     for (int base = 0; base < cnt; base += 2 * STEP) {
-      if (base + STEP < cnt) load_iter(base + STEP, B);
+      load_iter(base + STEP, B);  // unconditional (past the range: clamped rows)
       compute_iter(base, A);
       if (base + STEP >= cnt) break;
-      if (base + 2 * STEP < cnt) load_iter(base + 2 * STEP, A);
+      load_iter(base + 2 * STEP, A);
       compute_iter(base + STEP, B);
     }
   }
@@ -1038,16 +1041,11 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
     const int key0 = base + wave * KPW + kg;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int key = key0 + u * KPI;
-      if (key < cnt) {
-        const char* row = key == new_key ? reinterpret_cast<const char*>(p.k_new) + new_row
-                                         : kbase + (size_t)(s_begin + key) * D * sizeof(T);
-        bf.lo[u] = load_words<4>(row + lo_off);
-        bf.hi[u] = load_words<4>(row + hi_off);
-      } else {
-        bf.lo[u] = zero_words<4>();
-        bf.hi[u] = zero_words<4>();
-      }
+      const int key = min(key0 + u * KPI, cnt - 1);  // unconditional loads, as in the one-pass kernel
+      const char* row = key == new_key ? reinterpret_cast<const char*>(p.k_new) + new_row
+                                       : kbase + (size_t)(s_begin + key) * D * sizeof(T);
+      bf.lo[u] = load_words<4>(row + lo_off);
+      bf.hi[u] = load_words<4>(row + hi_off);
     }
     if constexpr (MASKED) {  // an in-range index for every lane, then a select on the value
       const int* mrow = p.mask_pos + ((size_t)b * p.Hkv + g) * p.C + s_begin;
@@ -1108,6 +1106,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
             if (u > 0) {
               if (stepwise) {
                 load_cs(rank_of(s_begin + min(key0 + u * KPI, cnt - 1)), bf.c[0], bf.sn[0]);
+                wait_loads();  // complete here, so the common path keeps the next set's loads in flight
               } else {
 #pragma unroll
                 for (int e = 0; e < HALF; ++e) {
@@ -1173,10 +1172,10 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
       KBuf A, B;
       load_iter(0, A);
       for (int base = 0; base < cnt; base += 2 * STEP) {
-        if (base + STEP < cnt) load_iter(base + STEP, B);
+        load_iter(base + STEP, B);  // unconditional (past the range: clamped rows)
         compute_iter(base, A);
         if (base + STEP >= cnt) break;
-        if (base + 2 * STEP < cnt) load_iter(base + 2 * STEP, A);
+        load_iter(base + 2 * STEP, A);
         compute_iter(base + STEP, B);
       }
     } else {
@@ -1194,16 +1193,11 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
   auto load_v = [&](int base) {
 #pragma unroll
     for (int u = 0; u < UV; ++u) {
-      const int key = base + u * KPI + wave * KPW + kg;
-      if (key < cnt) {
-        const char* row = key == new_key ? reinterpret_cast<const char*>(p.v_new) + new_row
-                                         : vbase + (size_t)(s_begin + key) * D * sizeof(T);
-        vlo[u] = load_words<4>(row + lo_off);
-        vhi[u] = load_words<4>(row + hi_off);
-      } else {
-        vlo[u] = zero_words<4>();
-        vhi[u] = zero_words<4>();
-      }
+      const int key = min(base + u * KPI + wave * KPW + kg, cnt - 1);  // unconditional loads
+      const char* row = key == new_key ? reinterpret_cast<const char*>(p.v_new) + new_row
+                                       : vbase + (size_t)(s_begin + key) * D * sizeof(T);
+      vlo[u] = load_words<4>(row + lo_off);
+      vhi[u] = load_words<4>(row + hi_off);
     }
   };
   load_v(0);
@@ -1257,7 +1251,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
       clo[u] = vlo[u];
       chi[u] = vhi[u];
     }
-    if (base + KPI * UV < cnt) load_v(base + KPI * UV);
+    load_v(base + KPI * UV);  // unconditional (past the range: clamped rows)
 #pragma unroll
     for (int u = 0; u < UV; ++u) {
       const int key = base + u * KPI + wave * KPW + kg;
