@@ -175,3 +175,33 @@ def test_pyramid_budgets_feed_snapkv(L):
         _run(L, w)
         kept += b_l
     assert kept == n_layers * b_target
+
+
+def test_snapkv_exact_ties_keep_lowest_positions(L):
+    """All keys zero: every observation row's weights are uniform over the keys it sees, so
+    all prefix scores are exactly equal and average pooling (zero padding) lowers only the
+    two positions at each end.  The tie rule of the selection (lower position first) then
+    fixes the kept set in closed form: positions 2 .. k + 1, then the window."""
+    H, D, N, Lo, K = 2, 128, 700, 16, 100
+    rng = np.random.default_rng(11)
+    q = rng.standard_normal((1, H, Lo, D)).astype(np.float32)
+    v = rng.standard_normal((1, H, N, D)).astype(np.float32)
+    tq = torch.from_numpy(q).to(torch.bfloat16).cuda()
+    tk = torch.zeros((1, H, N, D), dtype=torch.bfloat16, device="cuda")
+    tv = torch.from_numpy(v).to(torch.bfloat16).cuda()
+    p = L.snapkv_params(1, H, D, N, Lo, 5, K)
+    wsb = L.snapkv_sizes(p)
+    ko = torch.empty((1, H, K + Lo, D), dtype=torch.bfloat16, device="cuda")
+    vo = torch.empty_like(ko)
+    idx = torch.empty((1, H, K + Lo), dtype=torch.int32, device="cuda")
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    L.snapkv_compress(p, tq, tk, tv, ko, vo, idx, None, ws, wsb)
+    torch.cuda.synchronize()
+    want = list(range(2, K + 2)) + list(range(N - Lo, N))
+    vb = _bits(tv)[0]
+    for h in range(H):
+        ref_idx, _, _, _ = oracle.snapkv_compress(tq.float().cpu().numpy()[0, h], np.zeros((N, D)),
+                                                  tv.float().cpu().numpy()[0, h], K, 5)
+        assert list(ref_idx) == want
+        assert idx.cpu().numpy()[0, h].tolist() == want, f"head {h}"
+        assert np.array_equal(_bits(vo)[0, h], vb[h][want])
