@@ -331,7 +331,7 @@ def _summary(w, r):
 
 def _snapkv_bench(L, w, reps=20):
     """SnapKV compression of the 32k prompt: ms per compress (median of ``reps``, each
-    started with the memory-side cache flushed)."""
+    started with the caches flushed by a read)."""
     import torch
 
     B, H, D, N, Lo, K = w.batch, w.n_q_heads, w.head_dim, w.n_prompt, w.l_obs, w.k_keep
@@ -345,16 +345,16 @@ def _snapkv_bench(L, w, reps=20):
     vo = torch.empty_like(ko)
     idx = torch.empty((B, H, K + Lo), dtype=torch.int32, device=dev)
     ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
-    # Written between calls, outside the timed region, so that each compress starts with
-    # none of the prompt in the 256 MB memory-side cache (as after the prefill of other
-    # layers); back-to-back calls of the same prompt would otherwise run ~15% faster.
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    # Read between calls, outside the timed region, so that each compress starts with none
+    # of the prompt in the caches (256 MB memory-side cache included) and with clean lines:
+    # a write flush would leave dirty lines whose write-back lands in the timed call.
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     for _ in range(3):
         L.snapkv_compress(p, q, k, v, ko, vo, idx, None, ws, wsb)
     torch.cuda.synchronize()
     times = []
     for _ in range(reps):
-        flush.fill_(1)
+        flush.sum()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         L.snapkv_compress(p, q, k, v, ko, vo, idx, None, ws, wsb)
