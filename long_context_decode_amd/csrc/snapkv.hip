@@ -402,6 +402,20 @@ constexpr int kDigitBits = 11;
 constexpr int kBins = 1 << kDigitBits;
 constexpr int kHistCopies = 4;
 
+// Pooled scores of the thread's PER positions from its window w (HALO raw scores on each
+// side, zero past the ends): the 2 RAD + 1 taps in ascending order, then 1/kernel_size
+// for the average.  Scores are >= 0, so 0 is also the identity of the maximum.
+template <int PER, int HALO, int RAD, bool MAX>
+__device__ inline void pool_taps(const float (&w)[PER + 2 * HALO], uint32_t (&u)[PER], float inv_k) {
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    float acc = 0.f;
+#pragma unroll
+    for (int d = -RAD; d <= RAD; ++d) acc = MAX ? fmaxf(acc, w[j + HALO + d]) : acc + w[j + HALO + d];
+    u[j] = __float_as_uint(MAX ? acc : acc * inv_k);
+  }
+}
+
 template <int PER, int HALO>
 __global__ void __launch_bounds__(kSelectThreads) snapkv_select_kernel(SnapkvParams p) {
   static_assert(PER % 4 == 0 && HALO % 4 == 0, "16-byte pieces");
@@ -422,29 +436,42 @@ __global__ void __launch_bounds__(kSelectThreads) snapkv_select_kernel(SnapkvPar
   {
     constexpr int NW = PER + 2 * HALO;
     float w[NW];
+    // every load in range (clamped to the row's first and last 16-byte pieces; a row
+    // holds at least one), positions outside [0, Np) zeroed after the load
+    const int last = Np > 0 ? ((Np - 1) & ~3) : 0;
 #pragma unroll
     for (int q = 0; q < NW / 4; ++q) {
       const int e0 = i0 - HALO + 4 * q;  // a multiple of 4
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (e0 >= 0 && e0 < Np) v = *reinterpret_cast<const float4*>(src + e0);
-      w[4 * q] = v.x;
-      w[4 * q + 1] = e0 + 1 < Np ? v.y : 0.f;
-      w[4 * q + 2] = e0 + 2 < Np ? v.z : 0.f;
-      w[4 * q + 3] = e0 + 3 < Np ? v.w : 0.f;
+      const float4 v = *reinterpret_cast<const float4*>(src + min(max(e0, 0), last));
+      const bool lo = e0 >= 0;
+      w[4 * q] = lo && e0 < Np ? v.x : 0.f;
+      w[4 * q + 1] = lo && e0 + 1 < Np ? v.y : 0.f;
+      w[4 * q + 2] = lo && e0 + 2 < Np ? v.z : 0.f;
+      w[4 * q + 3] = lo && e0 + 3 < Np ? v.w : 0.f;
     }
     if constexpr (HALO > 0) {
-      const int rad = p.ksize / 2;
       const float inv_k = 1.f / (float)p.ksize;
-      float* so = p.scores_out ? p.scores_out + bh * Np : nullptr;
+      // one branch on the (uniform) radius and kind, then straight-line taps
+#define LCD_POOL(R)                                                                  \
+  do {                                                                               \
+    if (p.pool)                                                                      \
+      pool_taps<PER, HALO, (R) < HALO ? (R) : HALO, true>(w, u, inv_k);             \
+    else                                                                             \
+      pool_taps<PER, HALO, (R) < HALO ? (R) : HALO, false>(w, u, inv_k);            \
+  } while (0)
+      switch (p.ksize / 2) {
+        case 0: LCD_POOL(0); break;
+        case 1: LCD_POOL(1); break;
+        case 2: LCD_POOL(2); break;
+        case 3: LCD_POOL(3); break;
+        default: LCD_POOL(4); break;
+      }
+#undef LCD_POOL
+      if (p.scores_out) {
+        float* so = p.scores_out + bh * Np;
 #pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        float acc = 0.f;  // scores are >= 0: also the identity of max; padding adds 0
-#pragma unroll
-        for (int d = -HALO; d <= HALO; ++d)
-          if (d >= -rad && d <= rad) acc = p.pool ? fmaxf(acc, w[j + HALO + d]) : acc + w[j + HALO + d];
-        const float sc = p.pool ? acc : acc * inv_k;
-        if (so && i0 + j < Np) so[i0 + j] = sc;
-        u[j] = __float_as_uint(sc);
+        for (int j = 0; j < PER; ++j)
+          if (i0 + j < Np) so[i0 + j] = __uint_as_float(u[j]);
       }
     } else {
 #pragma unroll
