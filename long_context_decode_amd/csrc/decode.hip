@@ -513,27 +513,37 @@ __device__ inline void split_finish(const DecodeParams& p, float* ored, const fl
       int ps[EU];
 #pragma unroll
       for (int u = 0; u < EU; ++u) {
-        const int i = i0 + u * kDecodeThreads;
-        const bool in = i < p.n;
+        // unconditional loads (slots past n read slot n - 1; their values are not used),
+        // so that no branch separates a load from its use
+        const int ic = min(i0 + u * kDecodeThreads, p.n - 1);
 #pragma unroll
-        for (int j = 0; j < G; ++j) x[u][j] = in ? load_dev(&p.logits[(bh0 + j) * p.C + i]) : 0.f;
-        sc[u] = in ? score[i] : 0.f;
-        ps[u] = in ? pos[i] : 0;
+        for (int j = 0; j < G; ++j) x[u][j] = load_dev(&p.logits[(bh0 + j) * p.C + ic]);
+        sc[u] = score[ic];
+        ps[u] = pos[ic];
+      }
+      // arithmetic and victim folds first, the score stores last: a store issued before
+      // a later branch would make the compiler's wait at that branch cover it too
+      float snew[EU];
+#pragma unroll
+      for (int u = 0; u < EU; ++u) {
+        const bool in = i0 + u * kDecodeThreads < p.n;
+        float a = 0.f;
+#pragma unroll
+        for (int j = 0; j < G; ++j) a += exp2f(x[u][j] - Mtot[j]) * Linv[j];
+        snew[u] = in ? sc[u] + a : 0.f;
+      }
+      if (p.pick_victim) {
+#pragma unroll
+        for (int u = 0; u < EU; ++u) {
+          const int i = i0 + u * kDecodeThreads;
+          if (base + u * kDecodeThreads < p.n)  // wave-uniform
+            fold_victim(best, snew[u], ps[u], i, i < p.n, p.max_pos, bs, lane);
+        }
       }
 #pragma unroll
       for (int u = 0; u < EU; ++u) {
         const int i = i0 + u * kDecodeThreads;
-        const bool in = i < p.n;
-        float snew = 0.f;
-        if (in) {
-          float a = 0.f;
-#pragma unroll
-          for (int j = 0; j < G; ++j) a += exp2f(x[u][j] - Mtot[j]) * Linv[j];
-          snew = sc[u] + a;
-          score[i] = snew;
-        }
-        if (p.pick_victim && base + u * kDecodeThreads < p.n)  // wave-uniform
-          fold_victim(best, snew, ps[u], i, in, p.max_pos, bs, lane);
+        if (i < p.n) score[i] = snew[u];
       }
     }
     if (p.pick_victim) {
