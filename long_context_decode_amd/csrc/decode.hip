@@ -60,7 +60,13 @@ struct bf16_t {
 #define LCD_U2_G6 2
 #endif
 #ifndef LCD_H2O_EU
-#define LCD_H2O_EU 16  // token-level H2O epilogue: slots per thread per iteration (4 for blocks)
+#define LCD_H2O_EU 16  // token-level H2O epilogue: slots per thread per iteration
+#endif
+#ifndef LCD_H2O_EU_BLK
+#define LCD_H2O_EU_BLK 8  // the same for block-level eviction
+#endif
+#ifndef LCD_MERGE_SU
+#define LCD_MERGE_SU 4  // split merge: splits whose loads are issued together
 #endif
 #ifndef LCD_REC2
 #define LCD_REC2 1  // two-pass kernel: RoPE angles by angle addition within an iteration
@@ -454,7 +460,7 @@ __device__ inline void split_finish(const DecodeParams& p, float* ored, const fl
     }
     __syncthreads();
     constexpr int EPT = (G * D + kDecodeThreads - 1) / kDecodeThreads;  // output elements per thread
-    constexpr int SU = 4;
+    constexpr int SU = LCD_MERGE_SU;
     float* wsp = ored;  // [64][G] weights of the current group of splits (the partial is published)
     float acc[EPT];
 #pragma unroll
@@ -506,7 +512,7 @@ __device__ inline void split_finish(const DecodeParams& p, float* ored, const fl
     const int* pos = p.pos + bg * p.C;
     Victim best;
     const int bs = BLOCKS ? p.bs : 1;  // eviction granule
-    constexpr int EU = BLOCKS ? 4 : LCD_H2O_EU;  // slots per thread per iteration, all loads issued first
+    constexpr int EU = BLOCKS ? LCD_H2O_EU_BLK : LCD_H2O_EU;  // slots per thread per iteration, all loads issued first
     for (int base = threadIdx.x - lane; base < p.n; base += kDecodeThreads * EU) {
       const int i0 = base + lane;
       float x[EU][G], sc[EU];
