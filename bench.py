@@ -463,7 +463,7 @@ def main(argv=None):
         _counter_summary(*a.counters)
         return 0
     if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1",
                           "n_gpus_requested": a.gpus}))
         return 2
     import torch

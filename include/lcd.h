@@ -52,7 +52,7 @@ typedef enum lcd_status {
   LCD_ECAPACITY = 4,    /* operation would exceed the cache capacity          */
   LCD_ESIZE = 5,        /* a caller buffer is smaller than required          */
   LCD_EHIP = 6,         /* a HIP runtime call or kernel launch failed        */
-  LCD_EUNSUPPORTED = 7  /* valid request this build does not implement        */
+  LCD_EUNSUPPORTED = 7  /* valid request the library does not implement         */
 } lcd_status;
 
 typedef enum lcd_dtype { LCD_F32 = 0, LCD_BF16 = 1 } lcd_dtype;
