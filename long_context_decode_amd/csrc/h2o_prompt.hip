@@ -26,6 +26,8 @@
 //   4. h2o_gather_kernel    kept K / V rows, positions and scores.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "lcd_internal.h"
 
 namespace lcd {
@@ -37,6 +39,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 #ifndef LCD_H2OP_TW
 #define LCD_H2OP_TW 2  // register tiles per wave at D <= 128
+#endif
+#ifndef LCD_H2OP_SPLITLOOP
+#define LCD_H2OP_SPLITLOOP 1  // loop split: unconditional prefetches while both blocks exist
 #endif
 #ifndef LCD_H2OP_BT
 #define LCD_H2OP_BT 2  // 32-row tiles per staged block at D <= 128
@@ -105,6 +110,21 @@ __device__ inline void block_load(const uint16_t* base, int row0, int n, uint4 (
   }
 }
 
+// The same with every load issued (rows past n read row n - 1; callers mask them), for
+// loops in which no branch may separate a load from its use: then the compiler's wait
+// before the LDS store leaves the later prefetch in flight.
+template <int D>
+__device__ inline void block_load_all(const uint16_t* base, int row0, int n,
+                                      uint4 (&r)[block_pieces_per_thread<D>()]) {
+  constexpr int PPR = D * 2 / 16;  // pieces per row
+#pragma unroll
+  for (int i = 0; i < block_pieces_per_thread<D>(); ++i) {
+    const int piece = i * kThreads + (int)threadIdx.x;
+    const int row = min(row0 + piece / PPR, n - 1), col = piece % PPR;
+    r[i] = *reinterpret_cast<const uint4*>(base + (size_t)row * D + col * 8);
+  }
+}
+
 template <int D>
 __device__ inline void block_store(char* lds, const uint4 (&r)[block_pieces_per_thread<D>()]) {
   constexpr int PPR = D * 2 / 16;
@@ -154,9 +174,12 @@ __global__ void __launch_bounds__(kThreads, 2) h2o_rowstats_kernel(H2oPromptPara
   // blocks are loaded two iterations ahead into alternating register sets (named, so
   // they stay in registers), stored to LDS one iteration ahead
   uint4 rawA[block_pieces_per_thread<D>()], rawB[block_pieces_per_thread<D>()];
-  auto step = [&](int kb, uint4 (&load_into)[block_pieces_per_thread<D>()],
+  auto step = [&](auto all, int kb, uint4 (&load_into)[block_pieces_per_thread<D>()],
                   const uint4 (&store_from)[block_pieces_per_thread<D>()]) {
-    if (kb + 2 < n_blocks) block_load<D>(K, (kb + 2) * BR, p.N, load_into);
+    if constexpr (decltype(all)::value)
+      block_load_all<D>(K, (kb + 2) * BR, p.N, load_into);  // kb + 2 < n_blocks: no branch
+    else if (kb + 2 < n_blocks)
+      block_load<D>(K, (kb + 2) * BR, p.N, load_into);
     __syncthreads();  // block kb is in kblk[kb & 1]; every wave is done with block kb - 1
     const char* kl = kblk[kb & 1];
     const int k0 = kb * BR;
@@ -213,10 +236,17 @@ __global__ void __launch_bounds__(kThreads, 2) h2o_rowstats_kernel(H2oPromptPara
   block_load<D>(K, 0, p.N, rawA);
   if (n_blocks > 1) block_load<D>(K, BR, p.N, rawB);
   block_store<D>(kblk[0], rawA);
-  for (int kb = 0; kb < n_blocks; kb += 2) {
-    step(kb, rawA, rawB);
+  int kb = 0;
+#if LCD_H2OP_SPLITLOOP
+  for (; kb + 3 < n_blocks; kb += 2) {  // both steps prefetch a block that exists
+    step(std::true_type{}, kb, rawA, rawB);
+    step(std::true_type{}, kb + 1, rawB, rawA);
+  }
+#endif
+  for (; kb < n_blocks; kb += 2) {
+    step(std::false_type{}, kb, rawA, rawB);
     if (kb + 1 >= n_blocks) break;
-    step(kb + 1, rawB, rawA);
+    step(std::false_type{}, kb + 1, rawB, rawA);
   }
   // lanes l and l ^ 32 hold the same row (the two halves of every key tile)
 #pragma unroll
@@ -281,12 +311,26 @@ __global__ void __launch_bounds__(kThreads, 2) h2o_colsum_kernel(H2oPromptParams
       sraw = row0 + (int)threadIdx.x < p.N ? reinterpret_cast<const float2*>(p.rowstat)[bh * p.N + row0 + threadIdx.x]
                                            : make_float2(0.f, 0.f);
   };
+  // every load issued: rows past N read row N - 1 and get the statistics (+inf, 0), so
+  // their weights 2^(x - inf) * 0 are 0
+  auto load_unit_all = [&](int u, uint4 (&raw)[P], float2& sraw) {
+    const int row0 = (rb_first + u / G) * BR;
+    const size_t bh = (size_t)b * p.Hq + g * G + u % G;
+    block_load_all<D>(reinterpret_cast<const uint16_t*>(p.q) + bh * p.N * D, row0, p.N, raw);
+    const int row = row0 + min((int)threadIdx.x, BR - 1);
+    const float2 st = reinterpret_cast<const float2*>(p.rowstat)[bh * p.N + min(row, p.N - 1)];
+    sraw = row < p.N ? st : make_float2(INFINITY, 0.f);
+  };
   auto store_unit = [&](int buf, const uint4 (&raw)[P], float2 sraw) {
     block_store<D>(qblk[buf], raw);
     if ((int)threadIdx.x < BR) qstat[buf][threadIdx.x] = sraw;
   };
-  auto step = [&](int u, uint4 (&load_into)[P], float2& s_into, const uint4 (&store_from)[P], float2 s_from) {
-    if (u + 2 < units) load_unit(u + 2, load_into, s_into);
+  auto step = [&](auto all, int u, uint4 (&load_into)[P], float2& s_into, const uint4 (&store_from)[P],
+                  float2 s_from) {
+    if constexpr (decltype(all)::value)
+      load_unit_all(u + 2, load_into, s_into);  // u + 2 < units: no branch
+    else if (u + 2 < units)
+      load_unit(u + 2, load_into, s_into);
     __syncthreads();  // unit u is in buffer u & 1; every wave is done with unit u - 1
     const int row0 = (rb_first + u / G) * BR;
     const char* ql = qblk[u & 1];
@@ -309,7 +353,7 @@ __global__ void __launch_bounds__(kThreads, 2) h2o_colsum_kernel(H2oPromptParams
         }
 #pragma unroll
       for (int t = 0; t < BT; ++t) {
-        const float2 st = qstat[u & 1][t * 32 + (lane & 31)];  // rows past N carry (0, 0): weight 0
+        const float2 st = qstat[u & 1][t * 32 + (lane & 31)];  // rows past N carry (0, 0) or (+inf, 0): weight 0
         const int rt0 = row0 + t * 32;
 #pragma unroll
         for (int i = 0; i < TW; ++i) {
@@ -333,10 +377,17 @@ __global__ void __launch_bounds__(kThreads, 2) h2o_colsum_kernel(H2oPromptParams
   load_unit(0, rawA, sA);
   if (units > 1) load_unit(1, rawB, sB);
   store_unit(0, rawA, sA);
-  for (int u = 0; u < units; u += 2) {
-    step(u, rawA, sA, rawB, sB);
+  int u = 0;
+#if LCD_H2OP_SPLITLOOP
+  for (; u + 3 < units; u += 2) {  // both steps prefetch a unit that exists
+    step(std::true_type{}, u, rawA, sA, rawB, sB);
+    step(std::true_type{}, u + 1, rawB, sB, rawA, sA);
+  }
+#endif
+  for (; u < units; u += 2) {
+    step(std::false_type{}, u, rawA, sA, rawB, sB);
     if (u + 1 >= units) break;
-    step(u + 1, rawB, sB, rawA, sA);
+    step(std::false_type{}, u + 1, rawB, sB, rawA, sA);
   }
   // lanes of one half (lane / 32 fixed) hold the same 16 keys for different rows
 #pragma unroll
