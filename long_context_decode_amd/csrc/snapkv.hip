@@ -47,7 +47,10 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaveBlocks = 4;   // 32-key blocks per wave in the scoring kernels
+#ifndef LCD_SNAPKV_WAVE_BLOCKS
+#define LCD_SNAPKV_WAVE_BLOCKS 4
+#endif
+constexpr int kWaveBlocks = LCD_SNAPKV_WAVE_BLOCKS;  // 32-key blocks per wave in the scoring kernels
 constexpr int kTileKeys = 4 * kWaveBlocks * 32;  // keys per scoring workgroup
 constexpr int kMaxRows = 64;      // observation rows supported (two 32-row MFMA blocks)
 constexpr int kSelectThreads = 1024;
