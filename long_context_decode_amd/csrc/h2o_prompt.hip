@@ -193,14 +193,29 @@ __global__ void __launch_bounds__(kThreads, 2) h2o_rowstats_kernel(H2oPromptPara
       for (int t = 0; t < BT; ++t)
 #pragma unroll
         for (int i = 0; i < TW; ++i) acc[t][i] = f32x16{};
+      // the next k-step's fragments are read while this step's MFMAs run
+      bf16x8 fa[2][BT];
 #pragma unroll
-      for (int s = 0; s < KS; ++s)
+      for (int t = 0; t < BT; ++t) fa[0][t] = frag_lds<D>(kl + t * tile_bytes<D>(), 0, lane);
 #pragma unroll
-        for (int t = 0; t < BT; ++t) {
-          const bf16x8 a = frag_lds<D>(kl + t * tile_bytes<D>(), s, lane);
+      for (int s = 0; s < KS; ++s) {
+        if (s + 1 < KS) {
 #pragma unroll
-          for (int i = 0; i < TW; ++i) acc[t][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[i][s], acc[t][i], 0, 0, 0);
+          for (int t = 0; t < BT; ++t) fa[(s + 1) & 1][t] = frag_lds<D>(kl + t * tile_bytes<D>(), s + 1, lane);
         }
+#pragma unroll
+        for (int t = 0; t < BT; ++t)
+#pragma unroll
+          for (int i = 0; i < TW; ++i)
+            acc[t][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s & 1][t], qf[i][s], acc[t][i], 0, 0, 0);
+      }
+      // order: the reads of k-step s + 1 go ahead of the MFMAs of k-step s
+      __builtin_amdgcn_sched_group_barrier(0x100, BT, 0);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        if (s + 1 < KS) __builtin_amdgcn_sched_group_barrier(0x100, BT, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, BT * TW, 0);
+      }
       // fold the block into each row's (max, sum): the maximum on the raw products (the
       // scale is positive), masked keys set to -inf, then 2^(acc * scale - max)
 #pragma unroll
@@ -343,14 +358,27 @@ __global__ void __launch_bounds__(kThreads, 2) h2o_colsum_kernel(H2oPromptParams
       for (int t = 0; t < BT; ++t)
 #pragma unroll
         for (int i = 0; i < TW; ++i) acc[t][i] = f32x16{};
+      bf16x8 fb[2][BT];
 #pragma unroll
-      for (int s = 0; s < KS; ++s)
+      for (int t = 0; t < BT; ++t) fb[0][t] = frag_lds<D>(ql + t * tile_bytes<D>(), 0, lane);
 #pragma unroll
-        for (int t = 0; t < BT; ++t) {
-          const bf16x8 bq = frag_lds<D>(ql + t * tile_bytes<D>(), s, lane);
+      for (int s = 0; s < KS; ++s) {
+        if (s + 1 < KS) {
 #pragma unroll
-          for (int i = 0; i < TW; ++i) acc[t][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i][s], bq, acc[t][i], 0, 0, 0);
+          for (int t = 0; t < BT; ++t) fb[(s + 1) & 1][t] = frag_lds<D>(ql + t * tile_bytes<D>(), s + 1, lane);
         }
+#pragma unroll
+        for (int t = 0; t < BT; ++t)
+#pragma unroll
+          for (int i = 0; i < TW; ++i)
+            acc[t][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i][s], fb[s & 1][t], acc[t][i], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, BT, 0);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        if (s + 1 < KS) __builtin_amdgcn_sched_group_barrier(0x100, BT, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, BT * TW, 0);
+      }
 #pragma unroll
       for (int t = 0; t < BT; ++t) {
         const float2 st = qstat[u & 1][t * 32 + (lane & 31)];  // rows past N carry (0, 0) or (+inf, 0): weight 0
