@@ -213,3 +213,24 @@ def test_h2o_block_validation(L, kw, status):
     assert e.value.name == status
     ok = dict(base, block_size=32, capacity=128, n_recent=96)
     assert L.cache_sizes(L.cache_config(**ok))[0] > 0
+
+
+def test_header_compiles_as_c_and_links(tmp_path):
+    """A plain C99 client (tests/c/abi_smoke.c) compiles against include/lcd.h with
+    -pedantic -Werror, links against the library and gets error statuses back from
+    calls that fail validation, with no GPU present."""
+    import shutil
+    import subprocess
+
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    lib_dir = os.path.join(ROOT, "long_context_decode_amd")
+    exe = str(tmp_path / "abi_smoke")
+    r = subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", f"-I{os.path.join(ROOT, 'include')}",
+                        os.path.join(ROOT, "tests", "c", "abi_smoke.c"), f"-L{lib_dir}", "-llcd",
+                        f"-Wl,-rpath,{lib_dir}", "-o", exe], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
+    assert r.stdout.startswith("ok: abi ")
