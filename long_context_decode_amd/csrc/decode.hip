@@ -54,7 +54,7 @@ struct bf16_t {
 #define LCD_U2_G4 4
 #endif
 #ifndef LCD_U2_G4R
-#define LCD_U2_G4R 2  // G = 4 with RoPE (4 keys leave one wave per SIMD)
+#define LCD_U2_G4R 3  // G = 4 with RoPE (4 keys leave one wave per SIMD)
 #endif
 #ifndef LCD_U2_G6
 #define LCD_U2_G6 2
