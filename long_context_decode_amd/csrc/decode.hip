@@ -443,35 +443,58 @@ __device__ inline void split_finish(const DecodeParams& p, float* ored, const fl
     // from per-split weights staged in LDS, 64 splits at a time, with the loads of
     // SU splits of each thread's EPT elements issued before their arithmetic.
     const int wave = threadIdx.x >> 6;
-    for (int j = wave; j < G; j += kDecodeThreads / 64) {
-      float mx = -INFINITY;
-      for (int s = lane; s < n_splits; s += 64) mx = fmaxf(mx, load_dev(&p.part_ml[((size_t)s * BH + bh0 + j) * 2]));
-      mx = wave_max(mx);
-      float lt = 0.f;
-      for (int s = lane; s < n_splits; s += 64) {
-        const float* ml = p.part_ml + ((size_t)s * BH + bh0 + j) * 2;
-        lt += load_dev(&ml[1]) * exp2f(load_dev(&ml[0]) - mx);
+    float* wsp = ored;  // [64][G] weights of the current group of splits (the partial is published)
+    const bool one_group = n_splits <= 64;
+    if (one_group) {
+      // each lane loads its split's (m, l) once, unconditionally (lanes past the splits
+      // read the last one and drop it): totals and weights come from the same registers,
+      // one round trip instead of three
+      for (int j = wave; j < G; j += kDecodeThreads / 64) {
+        const bool in = lane < n_splits;
+        const float* ml = p.part_ml + ((size_t)min(lane, n_splits - 1) * BH + bh0 + j) * 2;
+        const float m = load_dev(&ml[0]), l = load_dev(&ml[1]);
+        const float mx = wave_max(in ? m : -INFINITY);
+        const float e = in ? exp2f(m - mx) : 0.f;
+        const float lt = wave_sum(in ? l * e : 0.f);
+        const float linv = 1.f / lt;
+        if (in) wsp[lane * G + j] = e * linv;
+        if (lane == 0) {
+          Mtot[j] = mx;
+          Linv[j] = linv;
+        }
       }
-      lt = wave_sum(lt);
-      if (lane == 0) {
-        Mtot[j] = mx;
-        Linv[j] = 1.f / lt;
+    } else {
+      for (int j = wave; j < G; j += kDecodeThreads / 64) {
+        float mx = -INFINITY;
+        for (int s = lane; s < n_splits; s += 64) mx = fmaxf(mx, load_dev(&p.part_ml[((size_t)s * BH + bh0 + j) * 2]));
+        mx = wave_max(mx);
+        float lt = 0.f;
+        for (int s = lane; s < n_splits; s += 64) {
+          const float* ml = p.part_ml + ((size_t)s * BH + bh0 + j) * 2;
+          lt += load_dev(&ml[1]) * exp2f(load_dev(&ml[0]) - mx);
+        }
+        lt = wave_sum(lt);
+        if (lane == 0) {
+          Mtot[j] = mx;
+          Linv[j] = 1.f / lt;
+        }
       }
     }
     __syncthreads();
     constexpr int EPT = (G * D + kDecodeThreads - 1) / kDecodeThreads;  // output elements per thread
     constexpr int SU = LCD_MERGE_SU;
-    float* wsp = ored;  // [64][G] weights of the current group of splits (the partial is published)
     float acc[EPT];
 #pragma unroll
     for (int k = 0; k < EPT; ++k) acc[k] = 0.f;
     for (int s0 = 0; s0 < n_splits; s0 += 64) {
       const int ns = min(64, n_splits - s0);
-      for (int e = threadIdx.x; e < ns * G; e += kDecodeThreads) {
-        const int j = e % G;
-        wsp[e] = exp2f(load_dev(&p.part_ml[((size_t)(s0 + e / G) * BH + bh0 + j) * 2]) - Mtot[j]) * Linv[j];
+      if (!one_group) {  // (one group: staged above)
+        for (int e = threadIdx.x; e < ns * G; e += kDecodeThreads) {
+          const int j = e % G;
+          wsp[e] = exp2f(load_dev(&p.part_ml[((size_t)(s0 + e / G) * BH + bh0 + j) * 2]) - Mtot[j]) * Linv[j];
+        }
+        __syncthreads();
       }
-      __syncthreads();
       for (int s1 = 0; s1 < ns; s1 += SU) {
         float x[SU][EPT];
 #pragma unroll
