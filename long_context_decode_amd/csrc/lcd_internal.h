@@ -118,7 +118,6 @@ struct SnapkvParams {
   int* idx_out;        // [B][H][out_rows]
   float* scores_out;   // [B][H][N - Lobs] or null
   float* rowstat;      // ws: [B][H][tiles][Lobs][2]
-  float* rowfinal;     // ws: [B][H][Lobs][2] (max, 1/sum) log2 domain
   float* colscore;     // ws: [B][H][sstride] raw mean scores (N - Lobs used)
   float* pooled;       // ws: [B][H][sstride]
   int B, H, D, N, Lobs, ksize, k_keep, pool, out_rows, tiles;

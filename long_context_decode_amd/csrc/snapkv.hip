@@ -3,23 +3,24 @@
 // 1-D pooling, per-head top-k and the gather of the kept K/V rows.
 //
 // Pipeline on one stream, no host round trip:
-//   1. snapkv_rowstats   per (row, head, 256-key tile): logits of the L_obs window
+//   1. snapkv_rowstats   per (512-key tile, head, row): logits of the L_obs window
 //                        queries against the tile's keys on MFMA (bf16 in, fp32
 //                        accumulate), causal mask, per-row (max, sum of 2^(x-max)).
-//   2. snapkv_rowfinal   per (row, head): merge the tiles -> (M_t, 1/L_t).
-//   3. snapkv_colscore   per tile of prefix keys: the same MFMA product, weights
+//   2. snapkv_colscore   per tile of prefix keys: merges the head's tile statistics into
+//                        (M_t, 1/L_t), then the same MFMA product, weights
 //                        2^(x - M_t) / L_t summed over the window rows -> s_i
-//                        (times 1/L_obs: the mean of step 2).
-//   4. snapkv_select     one workgroup per head: pooled scores, 4-pass radix select
-//                        of the k-th largest on the float bits (scores are >= 0, so
-//                        the bit patterns order like the values), then a stable
-//                        compaction that lists the kept positions in ascending order
-//                        (ties at the threshold keep the lower indices), followed by
-//                        the observation window.
-//   5. snapkv_gather     copy the kept K and V rows.
+//                        (times 1/L_obs: the mean over the window).
+//   3. snapkv_select     one workgroup per head: pooled scores (kernel_size > 9: pooled
+//                        by snapkv_pool_kernel first), radix select (11-bit
+//                        digits over the range-relative float bits; scores are >= 0,
+//                        so the bit patterns order like the values) of the k-th
+//                        largest, then a stable compaction that lists the kept
+//                        positions in ascending order (ties at the threshold keep the
+//                        lower indices), followed by the observation window.
+//   4. snapkv_gather     copy the kept K and V rows.
 // The contraction is L_obs x N x D per head: 32 rows against every key, i.e. 32 flops
 // per byte of K read.  It is a dense product, so it runs on MFMA, but it remains
-// HBM-bound (K is read twice: steps 1 and 3).
+// HBM-bound (K is read twice: steps 1 and 2).
 #include <hip/hip_runtime.h>
 
 #include "lcd_internal.h"
@@ -229,46 +230,7 @@ __global__ void __launch_bounds__(256) snapkv_rowstats_kernel(SnapkvParams p) {
   }
 }
 
-// ---------------------------------------------------------------------------- 2. rowfinal
-// One workgroup per (head of the group, batch row): threads stride over (tile,
-// observation row) pairs, then each row's partial maxima / sums are merged through LDS.
-constexpr int kFinalThreads = 1024;
-__global__ void __launch_bounds__(kFinalThreads) snapkv_rowfinal_kernel(SnapkvParams p) {
-  __shared__ float pm[kFinalThreads], pl[kFinalThreads];
-  const size_t bh = (size_t)blockIdx.y * p.H + p.h0 + blockIdx.x;
-  const int rows = ((p.Lobs + 31) / 32) * 32;
-  const int t = threadIdx.x % rows, part = threadIdx.x / rows, parts = kFinalThreads / rows;
-  float M = -INFINITY, L = 0.f;
-  for (int i = part; i < p.tiles; i += parts) {
-    const float* st = p.rowstat + ((bh * p.tiles + i) * kMaxRows + t) * 2;
-    const float m = st[0], l = st[1];
-    const float mn = fmaxf(M, m);
-    if (mn > -INFINITY) {
-      L = L * exp2f(M - mn) + l * exp2f(m - mn);
-      M = mn;
-    }
-  }
-  pm[threadIdx.x] = M;
-  pl[threadIdx.x] = L;
-  __syncthreads();
-  if (threadIdx.x < rows) {
-    float mm = -INFINITY;
-    for (int q = 0; q < parts; ++q) mm = fmaxf(mm, pm[q * rows + t]);
-    float ll = 0.f;
-    if (mm > -INFINITY)
-      for (int q = 0; q < parts; ++q) ll += pl[q * rows + t] * exp2f(pm[q * rows + t] - mm);
-    // rows past L_obs get zero weight (their logits are exactly 0: 2^(0 - 0) * 0 = 0)
-    const bool real = t < p.Lobs && ll > 0.f;
-    p.rowfinal[(bh * kMaxRows + t) * 2] = real ? mm : 0.f;
-    p.rowfinal[(bh * kMaxRows + t) * 2 + 1] = real ? 1.f / ll : 0.f;
-  }
-  if (threadIdx.x >= rows && threadIdx.x < kMaxRows) {
-    p.rowfinal[(bh * kMaxRows + threadIdx.x) * 2] = 0.f;
-    p.rowfinal[(bh * kMaxRows + threadIdx.x) * 2 + 1] = 0.f;
-  }
-}
-
-// ---------------------------------------------------------------------------- 3. colscore
+// ---------------------------------------------------------------------------- 2. colscore
 template <int D, int RB>
 __global__ void __launch_bounds__(256) snapkv_colscore_kernel(SnapkvParams p) {
   __shared__ float sM[kMaxRows], sI[kMaxRows];
@@ -279,17 +241,54 @@ __global__ void __launch_bounds__(256) snapkv_colscore_kernel(SnapkvParams p) {
             b = gridDim.z - 1 - blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const size_t bh = (size_t)b * p.H + h;
-  if (threadIdx.x < kMaxRows) {
-    sM[threadIdx.x] = p.rowfinal[(bh * kMaxRows + threadIdx.x) * 2];
-    sI[threadIdx.x] = p.rowfinal[(bh * kMaxRows + threadIdx.x) * 2 + 1];
+  // the rows' (M_t, 1/L_t) from the row-statistics partials of every tile of the head:
+  // thread = (row t, part); each part merges every PARTS-th tile, 8 tiles' loads issued
+  // together, then the parts are merged through LDS
+  {
+    constexpr int R = RB * 32, PARTS = 256 / R, TU = 8;
+    __shared__ float pm[256], pl[256];
+    const int t = threadIdx.x % R, part = threadIdx.x / R;
+    float M = -INFINITY, L = 0.f;
+    for (int i0 = part; i0 < p.tiles; i0 += PARTS * TU) {
+      float2 st[TU];
+#pragma unroll
+      for (int u = 0; u < TU; ++u) {
+        const int i = min(i0 + u * PARTS, p.tiles - 1);  // in range; extra tiles are dropped below
+        st[u] = *reinterpret_cast<const float2*>(p.rowstat + ((bh * p.tiles + i) * kMaxRows + t) * 2);
+      }
+#pragma unroll
+      for (int u = 0; u < TU; ++u) {
+        const float m = i0 + u * PARTS < p.tiles ? st[u].x : -INFINITY;
+        const float mn = fmaxf(M, m);
+        if (mn > -INFINITY) {
+          L = L * exp2f(M - mn) + (m > -INFINITY ? st[u].y * exp2f(m - mn) : 0.f);
+          M = mn;
+        }
+      }
+    }
+    pm[threadIdx.x] = M;
+    pl[threadIdx.x] = L;
+    __syncthreads();
+    if (threadIdx.x < kMaxRows) {
+      float mm = -INFINITY, ll = 0.f;
+      if (threadIdx.x < R) {
+        for (int q = 0; q < PARTS; ++q) mm = fmaxf(mm, pm[q * R + threadIdx.x]);
+        if (mm > -INFINITY)
+          for (int q = 0; q < PARTS; ++q) ll += pl[q * R + threadIdx.x] * exp2f(pm[q * R + threadIdx.x] - mm);
+      }
+      // rows past L_obs get zero weight
+      const bool real = (int)threadIdx.x < p.Lobs && ll > 0.f;
+      sM[threadIdx.x] = real ? mm : 0.f;
+      sI[threadIdx.x] = real ? 1.f / ll : 0.f;
+    }
+    __syncthreads();
   }
-  __syncthreads();
   const uint16_t* q = reinterpret_cast<const uint16_t*>(p.q_obs) + bh * p.Lobs * D;
   const uint16_t* k = reinterpret_cast<const uint16_t*>(p.k) + bh * (size_t)p.N * D;
   const int Np = p.N - p.Lobs;  // prefix keys: visible to every observation row
   const float inv_rows = 1.f / (float)p.Lobs;
   const int wkey0 = tile * kTileKeys + wave * kWaveBlocks * 32;
-  if (wkey0 >= Np) return;  // after the only __syncthreads
+  if (wkey0 >= Np) return;  // after the last __syncthreads
   bf16x8 qf[RB][D / 16];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) load_q_frags<D>(q, p.Lobs, rb, lane, qf[rb]);
@@ -335,7 +334,7 @@ __global__ void __launch_bounds__(256) snapkv_colscore_kernel(SnapkvParams p) {
   }
 }
 
-// ---------------------------------------------------------------------------- 4. select
+// ---------------------------------------------------------------------------- 3. select
 // Exclusive prefix sum over the 1024 threads of the block; *total receives the sum.
 // Each wave scans its lanes with DPP-free shuffles, publishes its total, and after one
 // barrier every wave adds the totals of the waves before it itself (16 broadcast LDS
@@ -581,7 +580,7 @@ __global__ void __launch_bounds__(kSelectThreads) snapkv_select_kernel(SnapkvPar
   for (int t = threadIdx.x; t < p.Lobs; t += kSelectThreads) idx[k + t] = Np + t;
 }
 
-// ---------------------------------------------------------------------------- 5. gather
+// ---------------------------------------------------------------------------- 4. gather
 // Row copies of the kept K and V rows as 16-byte pieces: each thread moves kGatherU
 // pieces of K and of V per iteration, all loads issued before the stores.
 constexpr int kGatherU = LCD_GATHER_U;
@@ -631,7 +630,7 @@ __global__ void __launch_bounds__(256) snapkv_gather_kernel(SnapkvParams p, int 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-  size_t rowstat, rowfinal, colscore, pooled, total;
+  size_t rowstat, colscore, pooled, total;
 };
 
 // Rows of the column-score and pooled buffers are padded to a multiple of 4 floats
@@ -647,8 +646,7 @@ WsLayout ws_layout(int B, int H, int N, int Lobs) {
   const size_t st = score_stride(N, Lobs);
   WsLayout w;
   w.rowstat = 0;
-  w.rowfinal = align256(w.rowstat + bh * tiles * kMaxRows * 2 * sizeof(float));
-  w.colscore = align256(w.rowfinal + bh * kMaxRows * 2 * sizeof(float));
+  w.colscore = align256(w.rowstat + bh * tiles * kMaxRows * 2 * sizeof(float));
   w.pooled = align256(w.colscore + bh * st * sizeof(float));
   w.total = align256(w.pooled + bh * st * sizeof(float));
   return w;
@@ -664,7 +662,6 @@ hipError_t launch_d(SnapkvParams p, hipStream_t s) {
     hipLaunchKernelGGL((snapkv_rowstats_kernel<D, 2>), sgrid, dim3(256), 0, s, p);
   else
     hipLaunchKernelGGL((snapkv_rowstats_kernel<D, 1>), sgrid, dim3(256), 0, s, p);
-  hipLaunchKernelGGL(snapkv_rowfinal_kernel, dim3(p.H, p.B), dim3(kFinalThreads), 0, s, p);
   if (np > 0) {
     const dim3 cgrid((np + kTileKeys - 1) / kTileKeys, p.H, p.B);
     if (two)
@@ -714,7 +711,6 @@ hipError_t launch_snapkv(const SnapkvParams& in, hipStream_t s) {
   const WsLayout w = ws_layout(p.B, p.H, p.N, p.Lobs);
   char* base = reinterpret_cast<char*>(p.rowstat);
   p.rowstat = reinterpret_cast<float*>(base + w.rowstat);
-  p.rowfinal = reinterpret_cast<float*>(base + w.rowfinal);
   p.colscore = reinterpret_cast<float*>(base + w.colscore);
   p.pooled = reinterpret_cast<float*>(base + w.pooled);
   p.tiles = (p.N + kTileKeys - 1) / kTileKeys;
