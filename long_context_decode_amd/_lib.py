@@ -9,8 +9,7 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-# LCD_LIB_PATH selects another build of the same library (e.g. a kernel variant).
-LIB_PATH = os.environ.get("LCD_LIB_PATH") or os.path.join(PKG, "liblcd.so")
+LIB_PATH = os.path.join(PKG, "liblcd.so")  # the in-tree build, the only library this binding loads
 
 LCD_F32, LCD_BF16 = 0, 1
 LCD_SINK_RING, LCD_APPEND, LCD_H2O, LCD_DUO = 0, 1, 2, 3

@@ -48,12 +48,6 @@ bool mul_ok(uint64_t* acc, uint64_t f) { return !__builtin_mul_overflow(*acc, f,
 
 constexpr int64_t kMaxSlots = int64_t(1) << 24;
 
-int env_int(const char* name, int dflt) {
-  const char* s = std::getenv(name);
-  if (!s || !*s) return dflt;
-  return std::atoi(s);
-}
-
 struct Layout {
   int C = 0, esize = 0, G = 0;
   uint64_t layer_bytes = 0;  // one of K or V of one layer
@@ -61,7 +55,7 @@ struct Layout {
   uint64_t aux_bytes = 0, off_cos = 0, off_sin = 0, off_pos = 0, off_score = 0, off_victim = 0, off_arrive = 0;
   uint64_t off_open = 0;
   uint64_t ws_bytes = 0, ws_off_ml = 0, ws_off_logits = 0;
-  int max_splits = 0, chunk_cap = 0, chunk_force = 0, target_wgs = 0;
+  int max_splits = 0, chunk_cap = 0;
   // mixed retrieval / streaming heads (DUO): streaming capacity, per-layer retrieval
   // head count, byte offset of each layer's K block and size of its K (= V) block,
   // and the per-layer head map (>= 0 retrieval index, < 0: -1 - streaming index)
@@ -190,10 +184,6 @@ lcd_status check_config(const lcd_cache_config* c, Layout* L) {
   L->aux_bytes = aux;
 
   L->chunk_cap = lcd::decode_chunk_cap(G);
-  const int force = env_int("LCD_DECODE_CHUNK", 0);
-  L->chunk_force = (force >= 64 && force % 64 == 0 && force <= L->chunk_cap) ? force : 0;
-  const int target = env_int("LCD_DECODE_TARGET_WGS", lcd::kResidentWorkgroups);
-  L->target_wgs = target > 0 ? target : lcd::kResidentWorkgroups;
   {
     // Bound on the split count of any plan with n <= C: plan_splits never exceeds
     // max(ceil(n / chunk_cap), 4 * target / bg) splits nor ceil(n / 64), all
@@ -202,10 +192,7 @@ lcd_status check_config(const lcd_cache_config* c, Layout* L) {
     const int64_t bg = duo ? (int64_t)c->batch : (int64_t)c->batch * c->n_kv_heads;
     const int64_t by_min = (Cp + 63) / 64;
     const int64_t s_cap = (Cp + L->chunk_cap - 1) / L->chunk_cap;
-    if (L->chunk_force)
-      L->max_splits = (int)((Cp + L->chunk_force - 1) / L->chunk_force);
-    else
-      L->max_splits = (int)std::min<int64_t>(by_min, std::max<int64_t>(s_cap, 4 * (int64_t)L->target_wgs / bg));
+    L->max_splits = (int)std::min<int64_t>(by_min, std::max<int64_t>(s_cap, 4 * (int64_t)lcd::kResidentWorkgroups / bg));
   }
   const int smax = L->max_splits;
 
@@ -220,34 +207,28 @@ lcd_status check_config(const lcd_cache_config* c, Layout* L) {
 }
 
 // Split plan for n attended slots of bg (row, KV head) pairs.  Cost model: workgroups
-// run in rounds of target_wgs, each as long as its chunk, so a plan costs
+// run in rounds of kResidentWorkgroups, each as long as its chunk, so a plan costs
 // rounds * chunk.  Candidates are the most splits that fit r rounds, r = 1..4, raised to
 // the fewest the chunk cap allows and capped at ceil(n / 64); the cheapest wins, ties
-// going to fewer splits.  LCD_DECODE_CHUNK forces the chunk.
+// going to fewer splits.
 void plan_splits(const Layout& L, int n, int bg, int* n_splits, int* chunk) {
-  int ch;
-  if (L.chunk_force) {
-    ch = L.chunk_force;
-  } else {
-    const int64_t target = L.target_wgs;
-    const int64_t by_min = (n + 63) / 64;
-    const int64_t s_cap = (n + L.chunk_cap - 1) / L.chunk_cap;
-    int64_t best_ch = 0, best_cost = -1;
-    for (int64_t r = 1; r <= 4; ++r) {
-      const int64_t sp = std::min<int64_t>(by_min, std::max<int64_t>(s_cap, r * target / bg));
-      const int64_t c = ((n + sp - 1) / sp + 63) / 64 * 64;
-      if (c > L.chunk_cap) continue;
-      const int64_t wgs = (n + c - 1) / c * (int64_t)bg;
-      const int64_t cost = (wgs + target - 1) / target * c;
-      if (best_cost < 0 || cost < best_cost || (cost == best_cost && c > best_ch)) {
-        best_cost = cost;
-        best_ch = c;
-      }
+  const int64_t target = lcd::kResidentWorkgroups;
+  const int64_t by_min = (n + 63) / 64;
+  const int64_t s_cap = (n + L.chunk_cap - 1) / L.chunk_cap;
+  int64_t best_ch = 0, best_cost = -1;
+  for (int64_t r = 1; r <= 4; ++r) {
+    const int64_t sp = std::min<int64_t>(by_min, std::max<int64_t>(s_cap, r * target / bg));
+    const int64_t c = ((n + sp - 1) / sp + 63) / 64 * 64;
+    if (c > L.chunk_cap) continue;
+    const int64_t wgs = (n + c - 1) / c * (int64_t)bg;
+    const int64_t cost = (wgs + target - 1) / target * c;
+    if (best_cost < 0 || cost < best_cost || (cost == best_cost && c > best_ch)) {
+      best_cost = cost;
+      best_ch = c;
     }
-    ch = (int)best_ch;
   }
-  *chunk = ch;
-  *n_splits = (n + ch - 1) / ch;
+  *chunk = (int)best_ch;
+  *n_splits = (n + *chunk - 1) / *chunk;
 }
 
 }  // namespace

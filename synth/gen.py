@@ -168,17 +168,25 @@ class NormalStream:
         return st.astype(np.float64)
 
     # -- GPU (torch) ----------------------------------------------------------------
-    def torch_stored(self, index, scale=1.0):
+    def torch_stored(self, index, scale=1.0, *, span=None):
         """Same bits as :meth:`stored`, computed by torch on ``index.device``.
 
         Returns a torch tensor of dtype float32 or bfloat16.  ``scale`` must be a
         python scalar here (planting is done by the caller with a second call).
+        ``span = (lo, hi)`` promises lo <= index < hi; when the whole span shares its
+        upper 32 index bits the keyed inner hash of those bits is one host constant, so
+        the tensor goes through one hash pass instead of two (same bits).
         """
         import torch
 
-        j = uniform_bits(self.key, index.to(torch.int64)) >> (32 - TABLE_BITS)
+        index = index.to(torch.int64)
+        if span is not None and span[1] > span[0] and (span[0] >> 32) == ((span[1] - 1) >> 32):
+            inner = int(mix32((int(span[0] >> 32) + self.key) & MASK32))
+            u = mix32((index & MASK32) ^ inner)
+        else:
+            u = uniform_bits(self.key, index)
         tab = _torch_table(float(scale), self.dtype, str(index.device))
-        return tab[j]
+        return tab[u >> (32 - TABLE_BITS)]
 
 
 @functools.lru_cache(maxsize=None)

@@ -18,6 +18,9 @@ import numpy as np
 from .gen import NormalStream, hash_positions, stream_key, uniform_bits
 
 SEED = 0
+# Elements per generation chunk on the device (int64 indices and hash temporaries of a
+# chunk take a few GiB).
+TORCH_CHUNK = 1 << 27
 
 
 @dataclasses.dataclass(frozen=True)
@@ -113,27 +116,30 @@ class Workload:
         out = st.values(idx, scale) if f64 else st.stored(idx, scale)
         return np.ascontiguousarray(np.transpose(out, (1, 2, 0, 3)))
 
-    def token_block_torch(self, tensor: str, layer: int, t0: int, t1: int, device):
+    def token_block_torch(self, tensor: str, layer: int, t0: int, t1: int, device, max_elems=TORCH_CHUNK):
         """Tokens [t0, t1) of a token-major tensor on ``device`` as [b][h][token][d]
-        (the bulk-append layout); generated one batch row at a time."""
+        (the bulk-append layout); generated in a few chunks of up to ``max_elems``
+        elements, each a handful of whole-tensor operations."""
         import torch
 
         T, B, H, D = self.token_shape(tensor)
         st = self.stream(tensor, layer)
         out = torch.empty((B, H, t1 - t0, D), device=device,
                           dtype=torch.float32 if self.dtype == "f32" else torch.bfloat16)
-        t = torch.arange(t0, t1, device=device, dtype=torch.int64)
-        h = torch.arange(H, device=device, dtype=torch.int64)
-        d = torch.arange(D, device=device, dtype=torch.int64)
-        for b in range(B):
-            idx = ((t[None, :, None] * B + b) * H + h[:, None, None]) * D + d[None, None, :]
-            out[b] = st.torch_stored(idx)
-            if tensor == "k" and self.sink_key_scale != 1.0 and t0 < 4:
-                m = min(4, t1) - t0
-                out[b, :, :m] = st.torch_stored(idx[:, :m], self.sink_key_scale)
+        per = B * H * D  # elements of one token
+        bhd = (torch.arange(B * H, device=device, dtype=torch.int64) * D).view(B, H, 1, 1) + \
+            torch.arange(D, device=device, dtype=torch.int64).view(1, 1, 1, D)
+        for a, e in _chunks(t0, t1, per, max_elems):
+            idx = torch.arange(a, e, device=device, dtype=torch.int64).view(1, 1, -1, 1) * per + bhd
+            out[:, :, a - t0:e - t0] = st.torch_stored(idx, span=(a * per, e * per))
+            if tensor == "k" and self.sink_key_scale != 1.0 and a < 4:
+                m = min(4, e) - a
+                out[:, :, a - t0:a - t0 + m] = st.torch_stored(idx[:, :, :m], self.sink_key_scale,
+                                                               span=(a * per, (a + m) * per))
+            del idx
         return out
 
-    def token_major_torch(self, tensor: str, layer: int, t0: int, t1: int, device, chunk_tokens=None):
+    def token_major_torch(self, tensor: str, layer: int, t0: int, t1: int, device, max_elems=TORCH_CHUNK):
         """Tokens [t0, t1) on ``device`` as [token][b][h][d]: each token's slice is a
         contiguous [b][h][d] block (the single-token append / query layout)."""
         import torch
@@ -143,14 +149,14 @@ class Workload:
         st = self.stream(tensor, layer)
         out = torch.empty((t1 - t0, B, H, D), device=device,
                           dtype=torch.float32 if self.dtype == "f32" else torch.bfloat16)
-        step = chunk_tokens or max(1, (1 << 25) // per)
-        for a in range(t0, t1, step):
-            e = min(t1, a + step)
+        for a, e in _chunks(t0, t1, per, max_elems):
             idx = torch.arange(a * per, e * per, device=device, dtype=torch.int64)
-            out[a - t0: e - t0] = st.torch_stored(idx).view(e - a, B, H, D)
+            out[a - t0: e - t0] = st.torch_stored(idx, span=(a * per, e * per)).view(e - a, B, H, D)
             if tensor == "k" and self.sink_key_scale != 1.0 and a < 4:
                 m = min(4, e) - a
-                out[a - t0: a - t0 + m] = st.torch_stored(idx[: m * per], self.sink_key_scale).view(m, B, H, D)
+                out[a - t0: a - t0 + m] = st.torch_stored(idx[: m * per], self.sink_key_scale,
+                                                          span=(a * per, (a + m) * per)).view(m, B, H, D)
+            del idx
         return out
 
     # ------------------------------------------------------------------ snapkv
@@ -179,16 +185,14 @@ class Workload:
         rows = self.l_obs if tensor == "q_obs" else self.n_prompt
         B, H, D = self.batch, self.n_q_heads, self.head_dim
         st = NormalStream(self.seed, f"{self.name}/{tensor}", self.dtype)
-        out = torch.empty((B, H, rows, D), device=device,
-                          dtype=torch.float32 if self.dtype == "f32" else torch.bfloat16)
-        for b in range(B):
-            for h in range(H):
-                base = (b * H + h) * rows * D
-                idx = base + torch.arange(rows * D, device=device, dtype=torch.int64).view(rows, D)
-                out[b, h] = st.torch_stored(idx)
-                if tensor == "k" and self.plant_frac > 0:
-                    p = torch.from_numpy(self.snapkv_plants(b, h)).to(device)
-                    out[b, h, p] = st.torch_stored(idx[p], self.plant_scale)
+        out = _flat_stream_torch(st, B * H * rows * D, device).view(B, H, rows, D)
+        if tensor == "k" and self.plant_frac > 0:
+            # every planted row of every head in one call: flat row ids (b * H + h) * rows + p
+            prow = np.concatenate([(b * H + h) * rows + self.snapkv_plants(b, h)
+                                   for b in range(B) for h in range(H)])
+            pr = torch.from_numpy(prow).to(device)
+            idx = pr.view(-1, 1) * D + torch.arange(D, device=device, dtype=torch.int64).view(1, D)
+            out.view(B * H * rows, D)[pr] = st.torch_stored(idx, self.plant_scale, span=(0, B * H * rows * D))
         return out
 
     # ------------------------------------------------------------------ h2o prompt phase
@@ -202,20 +206,10 @@ class Workload:
 
     def prompt_tensor_torch(self, tensor: str, device):
         """The whole [B][H][N][D] prompt tensor on ``device`` (H = query or KV heads)."""
-        import torch
-
         heads = self.n_q_heads if tensor == "q" else self.n_kv_heads
         B, N, D = self.batch, self.n_prompt, self.head_dim
         st = NormalStream(self.seed, f"{self.name}/prompt/{tensor}", self.dtype)
-        out = torch.empty((B, heads, N, D), device=device,
-                          dtype=torch.float32 if self.dtype == "f32" else torch.bfloat16)
-        per = N * D
-        for b in range(B):
-            for h in range(heads):
-                base = (b * heads + h) * per
-                out[b, h] = st.torch_stored(torch.arange(base, base + per, device=device,
-                                                         dtype=torch.int64)).view(N, D)
-        return out
+        return _flat_stream_torch(st, B * heads * N * D, device).view(B, heads, N, D)
 
     # ------------------------------------------------------------------ h2o
     def h2o_initial_state(self, b: int, g: int):
@@ -271,32 +265,61 @@ def h2o_state_torch(w: Workload, device):
 
     Returns (K, V [B][Hkv][C][D] in the cache dtype, positions int32 [B][Hkv][C],
     scores float32 [B][Hkv][C]) with slots in ascending position order, the layout an
-    H2O cache holds after being seeded in place.
+    H2O cache holds after being seeded in place.  Positions and scores come from
+    :meth:`Workload.h2o_initial_state` (host); the K / V rows of all heads are generated
+    in one pass each.
     """
     import torch
 
     B, H, C, D = w.batch, w.n_kv_heads, w.budget, w.head_dim
-    dt = torch.float32 if w.dtype == "f32" else torch.bfloat16
-    K = torch.empty((B, H, C, D), dtype=dt, device=device)
-    V = torch.empty_like(K)
-    P = torch.empty((B, H, C), dtype=torch.int32, device=device)
-    S = torch.empty((B, H, C), dtype=torch.float32, device=device)
     T = w.total_tokens
-    d = torch.arange(D, device=device, dtype=torch.int64)
+    pos = np.empty((B, H, C), np.int64)
+    sc = np.empty((B, H, C), np.float32)
+    planted = np.empty((B, H, C), bool)
     for b in range(B):
         for g in range(H):
-            pos, sc, planted = w.h2o_initial_state(b, g)
-            pt = torch.from_numpy(pos).to(device)
-            idx = ((pt[:, None] * B + b) * H + g) * D + d[None, :]
-            kk = w.stream("k", 0).torch_stored(idx)
-            pl = torch.from_numpy(np.flatnonzero(planted)).to(device)
-            kk[pl] = w.stream("k", 0).torch_stored(idx[pl], w.plant_scale)
-            K[b, g] = kk
-            V[b, g] = w.stream("v", 0).torch_stored(idx)
-            P[b, g] = pt.to(torch.int32)
-            S[b, g] = torch.from_numpy(sc).to(device)
-    assert T > int(P.max())
-    return K, V, P, S
+            pos[b, g], sc[b, g], planted[b, g] = w.h2o_initial_state(b, g)
+    assert T > int(pos.max())
+    pt = torch.from_numpy(pos).to(device)
+    bg = (torch.arange(B, device=device, dtype=torch.int64).view(B, 1, 1) * H +
+          torch.arange(H, device=device, dtype=torch.int64).view(1, H, 1))
+    rows = pt * (B * H) + bg  # token-major row index (t * B + b) * H + g
+    idx = rows.unsqueeze(-1) * D + torch.arange(D, device=device, dtype=torch.int64)
+    span = (0, T * B * H * D)
+    K = w.stream("k", 0).torch_stored(idx, span=span)
+    pl = torch.from_numpy(planted).to(device)
+    K[pl] = w.stream("k", 0).torch_stored(idx[pl], w.plant_scale, span=span)
+    V = w.stream("v", 0).torch_stored(idx, span=span)
+    return K, V, pt.to(torch.int32), torch.from_numpy(sc).to(device)
+
+
+def _chunks(t0, t1, per, max_elems):
+    """Token ranges [a, e) covering [t0, t1), each of at most max(1, max_elems // per)
+    tokens and never crossing a multiple of 2**32 elements (so each has one upper index
+    word)."""
+    step = max(1, max_elems // per)
+    a = t0
+    while a < t1:
+        e = min(t1, a + step)
+        wall = ((a * per >> 32) + 1) << 32  # next multiple of 2**32 elements
+        if e * per > wall and (wall // per) > a:
+            e = wall // per
+        yield a, e
+        a = e
+
+
+def _flat_stream_torch(st, n, device, max_elems=TORCH_CHUNK):
+    """Elements 0 .. n-1 of a stream as one flat tensor, in chunks of at most max_elems
+    that never cross a multiple of 2**32."""
+    import torch
+
+    out = torch.empty(n, device=device, dtype=torch.float32 if st.dtype == "f32" else torch.bfloat16)
+    a = 0
+    while a < n:
+        e = min(n, a + max_elems, ((a >> 32) + 1) << 32)
+        out[a:e] = st.torch_stored(torch.arange(a, e, device=device, dtype=torch.int64), span=(a, e))
+        a = e
+    return out
 
 
 def _streaming(name, title, **kw):

@@ -24,10 +24,10 @@ def _sources(top, exts):
                 yield os.path.join(d, f)
 
 
-def _run(code, env=None):
+def _run(code, env=None, cwd=ROOT):
     e = dict(os.environ)
     e.update(env or {})
-    return subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=e, capture_output=True, text=True,
+    return subprocess.run([sys.executable, "-c", code], cwd=cwd, env=e, capture_output=True, text=True,
                           timeout=120)
 
 
@@ -56,7 +56,16 @@ def test_oracle_never_uses_the_library():
         assert "liblcd" not in text, f
 
 
-def test_missing_library_fails_loudly():
-    r = _run("import long_context_decode_amd", env={"LCD_LIB_PATH": os.path.join(ROOT, "no_such_liblcd.so")})
+def test_missing_library_fails_loudly(tmp_path):
+    """A copy of the package's Python files without liblcd.so next to them: the import
+    raises and names the missing library (the binding loads only the in-tree build)."""
+    import shutil
+
+    dst = tmp_path / "long_context_decode_amd"
+    dst.mkdir()
+    for f in os.listdir(PKG):
+        if f.endswith(".py"):
+            shutil.copy(os.path.join(PKG, f), dst / f)
+    r = _run("import long_context_decode_amd", cwd=str(tmp_path), env={"PYTHONPATH": str(tmp_path)})
     assert r.returncode != 0
-    assert "no_such_liblcd.so" in r.stderr
+    assert "liblcd.so is missing" in r.stderr

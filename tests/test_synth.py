@@ -75,3 +75,54 @@ def test_token_block_torch_matches_numpy():
     t = w.token_block_torch("k", 1, 2, 7, "cpu")  # [b][h][t][d]
     n = w.token_block("k", 1, np.arange(2, 7), f64=False)
     assert np.array_equal(t.view(torch.int16).numpy().view(np.uint16), n)
+
+
+def test_chunked_torch_generators_match_numpy():
+    """Whole-tensor torch generation (few large chunks) gives the numpy bits, across chunk
+    edges, sink scaling, planted rows and seeded H2O state."""
+    from synth.workloads import h2o_state_torch, scaled
+
+    def u16(t):
+        return t.view(torch.int16).numpy().view(np.uint16)
+
+    w = WORKLOADS["gqa_long"]
+    t = w.token_block_torch("k", 1, 0, 9, "cpu", max_elems=3 * 16 * 4 * 256)  # 3 chunks, sinks inside
+    assert np.array_equal(u16(t), w.token_block("k", 1, np.arange(0, 9), f64=False))
+    t = w.token_major_torch("k", 2, 0, 9, "cpu", max_elems=2 * 16 * 4 * 256)
+    assert np.array_equal(u16(t), w.token_block("k", 2, np.arange(0, 9), f64=False).transpose(2, 0, 1, 3))
+    s = scaled(WORKLOADS["snapkv_32k"], name="sk", n_q_heads=3, n_kv_heads=3, n_prompt=500, l_obs=8, k_keep=40)
+    for tn in ("q_obs", "k", "v"):
+        tt = u16(s.snapkv_tensor_torch(tn, "cpu"))
+        for h in range(3):
+            assert np.array_equal(tt[0, h], s.snapkv_tensor(tn, 0, h, f64=False)), tn
+    p = scaled(WORKLOADS["h2o_prompt_128k"], name="pp", batch=2, n_q_heads=4, n_kv_heads=2, n_prompt=300)
+    for tn in ("q", "k"):
+        tt = u16(p.prompt_tensor_torch(tn, "cpu"))
+        for b in range(2):
+            for h in range(tt.shape[1]):
+                assert np.array_equal(tt[b, h], p.prompt_tensor(tn, b, h, f64=False))
+    hw = scaled(WORKLOADS["h2o_128k"], name="hh", batch=2, n_kv_heads=2, n_q_heads=8, n_prompt=3000, budget=256,
+                n_recent=32, steps=10)
+    K, V, P, S = h2o_state_torch(hw, "cpu")
+    for b in range(2):
+        for g in range(2):
+            pos, sc, _ = hw.h2o_initial_state(b, g)
+            assert np.array_equal(P[b, g].numpy(), pos) and np.array_equal(S[b, g].numpy(), sc)
+            assert np.array_equal(u16(K[b, g]), hw.h2o_kv("k", b, g, pos, f64=False))
+            assert np.array_equal(u16(V[b, g]), hw.h2o_kv("v", b, g, pos, f64=False))
+
+
+def test_chunks_never_cross_a_2pow32_element_boundary():
+    from synth.workloads import _chunks
+
+    per = 2**30 + 7
+    lst = list(_chunks(0, 100, per, 2**31))
+    assert lst[0][0] == 0 and lst[-1][1] == 100
+    assert all(lst[i][1] == lst[i + 1][0] for i in range(len(lst) - 1))
+    for a, e in lst:
+        assert e - a == 1 or (a * per) >> 32 == (e * per - 1) >> 32, (a, e)
+    st = NormalStream(0, "x", "bf16")
+    idx = torch.arange(2**32 - 50, 2**32 + 50)
+    two = torch.cat([st.torch_stored(idx[:50], span=(2**32 - 50, 2**32)),
+                     st.torch_stored(idx[50:], span=(2**32, 2**32 + 50))])
+    assert np.array_equal(two.view(torch.int16).numpy().view(np.uint16), st.stored(idx.numpy()))
