@@ -43,6 +43,6 @@ from .snapkv import (  # noqa: F401
     select_topk,
     snapkv_compress,
 )
-from .h2o import H2OBlockHead, H2OHead, h2o_prompt_select  # noqa: F401
+from .h2o import H2OBlockHead, H2OHead, h2o_prompt_scores, h2o_prompt_select  # noqa: F401
 from .pyramid import pyramid_budgets  # noqa: F401
 from .duo import duo_attended_tokens, duo_decode  # noqa: F401

@@ -14,9 +14,8 @@ Readings (the pages leave these open):
   and the new token receives its own weight in the step it arrives.
 * The recent partition includes the new token: at step t the tokens with
   position > t - L_local are protected; the victim is the smallest s among the
-  others, the decision taken on s rounded to float32 (the GPU's precision), ties
-  evicting the newer token (the same order as SnapKV's keep rule: higher score,
-  then lower index, is kept).
+  others (exact float64 s), ties evicting the newer token (the same order as
+  SnapKV's keep rule: higher score, then lower index, is kept).
 * With grouped-query attention one s is kept per KV head and is the sum of the
   weights of the G query heads that share it.
 * No positional rotation is applied: cached keys are used as given.
@@ -45,7 +44,7 @@ class H2OHead:
         cands = [i for i, p in enumerate(self.pos) if p <= t - self.n_recent]
         if not cands:
             raise ValueError("no eviction candidate")
-        return min(cands, key=lambda i: (float(np.float32(self.s[i])), -self.pos[i]))
+        return min(cands, key=lambda i: (self.s[i], -self.pos[i]))
 
     def step(self, t: int, q: np.ndarray, k_t: np.ndarray, v_t: np.ndarray, scale=None):
         """Decode token ``t`` with queries q[G][D]; returns (out[G][D], evicted position or None)."""
@@ -71,28 +70,43 @@ class H2OHead:
         return out, evicted
 
 
-def h2o_prompt_select(Q, K, budget: int, n_recent: int, scale=None):
-    """Prompt-phase selection for one KV head (small prompts only).
+def h2o_prompt_scores(Q, K, scale=None, rows_per_group=256, first_row=0):
+    """s_j of every prompt token for one KV head: the column sums, over the G query
+    heads, of the causal attention matrices A_h[t, j] = softmax over j <= t of
+    scale * <Q[t, h], K[j]> (zero for j > t).  Rows are formed ``rows_per_group`` at a
+    time, each row a full causal softmax, so memory stays bounded.
 
-    Q[T][G][D] are the prompt queries of the G heads sharing K[T][D].  Each prompt
-    token j accumulates s_j = sum over rows t >= j and heads of the causal
-    attention weight; the last ``n_recent`` tokens are kept, and of the older ones
-    the ``budget - n_recent`` best by (higher float32 s, lower position).
-    Returns (kept positions ascending, s of every prompt token).
-    """
+    With ``first_row`` > 0 only rows t >= first_row are summed: the result is then exact
+    for the keys j >= first_row (no earlier row attends them) and partial before."""
     Q = np.asarray(Q, np.float64)
     K = np.asarray(K, np.float64)
     T, G, D = Q.shape
     sc = 1.0 / np.sqrt(D) if scale is None else float(scale)
     s = np.zeros(T)
     for h in range(G):
-        for t in range(T):
-            s[: t + 1] += softmax((K[: t + 1] @ Q[t, h]) * sc)
+        for r0 in range(first_row, T, rows_per_group):
+            r1 = min(T, r0 + rows_per_group)
+            X = (Q[r0:r1, h] @ K[:r1].T) * sc  # rows r0 .. r1-1 against keys 0 .. r1-1
+            X[np.arange(r1)[None, :] > np.arange(r0, r1)[:, None]] = -np.inf  # key after row
+            s[:r1] += softmax(X, axis=1).sum(axis=0)
+    return s
+
+
+def h2o_prompt_select(Q, K, budget: int, n_recent: int, scale=None):
+    """Prompt-phase selection for one KV head.
+
+    Q[T][G][D] are the prompt queries of the G heads sharing K[T][D].  Each prompt
+    token j accumulates s_j = sum over rows t >= j and heads of the causal
+    attention weight; the last ``n_recent`` tokens are kept, and of the older ones
+    the ``budget - n_recent`` best by (higher s, lower position).
+    Returns (kept positions ascending, s of every prompt token).
+    """
+    s = h2o_prompt_scores(Q, K, scale)
+    T = s.shape[0]
     if budget >= T:
         return np.arange(T, dtype=np.int64), s
     old = T - n_recent
-    s32 = s[:old].astype(np.float32)
-    order = sorted(range(old), key=lambda j: (-float(s32[j]), j))
+    order = sorted(range(old), key=lambda j: (-float(s[j]), j))
     keep = sorted(order[: budget - n_recent]) + list(range(old, T))
     return np.array(keep, dtype=np.int64), s
 
@@ -110,7 +124,7 @@ class H2OBlockHead:
       freed first and becomes the new open block.
     * A block is an eviction candidate only if none of its tokens is among the n_recent
       newest (positions <= t - n_recent for the arriving token t, as in H2OHead).  Its
-      score is the float64 sum of its tokens' s, decided in float32; ties free the block
+      score is the float64 sum of its tokens' s; ties free the block
       holding the newer token.
     * Step order, scores and GQA as in H2OHead.
     """
@@ -136,7 +150,7 @@ class H2OBlockHead:
         return [p for blk in self.blocks for p in blk["pos"]]
 
     def block_score(self, blk) -> float:
-        return float(np.float32(sum(blk["s"])))
+        return float(sum(blk["s"]))
 
     def victim_block(self, t: int) -> int:
         """Index of the block freed before writing token ``t`` (budget full, open block full)."""

@@ -18,9 +18,10 @@ Readings (the pages leave these open):
 * Pooling is an average over a centred window of ``kernel_size`` with zero
   padding and divisor ``kernel_size`` at every position, over the prefix scores
   only; ``mode="max"`` takes the maximum over the in-range entries instead.
-* The top-k ranks by (higher score, lower index); the decision is taken on the
-  score rounded to float32, the precision the GPU kernel decides in, and the
-  kept positions are returned in ascending order.
+* The top-k ranks by (higher score, lower index) on the exact (float64) pooled
+  scores, and the kept positions are returned in ascending order.  An
+  implementation that decides on rounded scores can differ only where two scores
+  agree to within its rounding (a near-tie).
 """
 import numpy as np
 
@@ -65,9 +66,9 @@ def pool1d(s: np.ndarray, kernel_size: int, mode: str = "avg") -> np.ndarray:
 
 
 def select_topk(S: np.ndarray, k: int) -> np.ndarray:
-    """Step 4: ascending indices of the ``k`` best by (higher float32 score, lower index)."""
-    S32 = np.asarray(S, np.float64).astype(np.float32)
-    order = sorted(range(len(S32)), key=lambda i: (-float(S32[i]), i))
+    """Step 4: ascending indices of the ``k`` best by (higher score, lower index)."""
+    S = np.asarray(S, np.float64)
+    order = sorted(range(len(S)), key=lambda i: (-float(S[i]), i))
     return np.array(sorted(order[:k]), dtype=np.int64)
 
 

@@ -3,16 +3,18 @@
 [KVC] "Heavy-Hitter Oracle (H2O) e a esparsidade de cauda pesada": every prompt token's
 accumulated causal attention s_j (summed over the KV head's query heads), then the
 n_recent newest tokens plus the heaviest older ones.  Checks per (batch row, KV head):
-* s within 1e-4 relative (+1e-6 absolute) of oracle.h2o_prompt_select's float64 s (the
+* s within 1e-5 relative (+1e-9 absolute) of oracle.h2o_prompt_select's float64 s (the
   scores come from bf16 MFMA products with float32 accumulation and exponentials);
 * the kept heavy set is exactly the top-k of the GPU's own float32 s by (higher s,
   lower position), recent tokens appended, positions ascending;
-* against the oracle's kept set only near-ties differ (oracle s within 1e-4 relative of
+* against the oracle's kept set only near-ties differ (oracle s within 1e-6 relative of
   its k-th largest), each printed;
 * kept K / V rows and scores gathered bit-exactly.
-At the full 128k size the oracle's N^2 work is out of reach: there the scores of the last
-64 positions (which only the last 64 rows attend) are computed exactly from those rows,
-every row's weights summing to one pins the total, and the selection property is checked.
+Full oracle comparisons run up to N = 16384 (32 row tiles per workgroup span, the same
+tiling paths as 128k).  At the full 128k size the oracle's N^2 work is out of reach: there
+the scores of the last 2048 positions (which only the last 2048 rows attend) are compared
+with the oracle on two (row, KV head) pairs, every row's weights summing to one pins the
+total, and the selection property is checked on every pair.
 """
 import numpy as np
 import pytest
@@ -24,7 +26,7 @@ from synth.workloads import scaled
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-RTOL_S, NEAR_TIE = 1e-4, 1e-4
+RTOL_S, NEAR_TIE = 1e-5, 1e-6
 BASE = WORKLOADS["h2o_prompt_128k"]
 
 
@@ -87,6 +89,7 @@ def _check_selection(w, r, b, g):
     dict(batch=1, n_q_heads=2, n_kv_heads=1, head_dim=128, n_prompt=300, budget=512, n_recent=32),  # keep all
     dict(batch=1, n_q_heads=8, n_kv_heads=1, head_dim=128, n_prompt=4133, budget=700, n_recent=100),
     dict(batch=1, n_q_heads=6, n_kv_heads=1, head_dim=64, n_prompt=2050, budget=300, n_recent=1),
+    dict(batch=1, n_q_heads=4, n_kv_heads=1, head_dim=128, n_prompt=16384, budget=4096, n_recent=512),
 ])
 def test_h2o_prompt_small(L, case):
     w = scaled(BASE, name="h2o_prompt_" + "_".join(f"{k}{v}" for k, v in case.items()), **case)
@@ -98,11 +101,11 @@ def test_h2o_prompt_small(L, case):
             Q = np.stack([w.prompt_tensor("q", b, g * G + j) for j in range(G)], axis=1)  # [N][G][D]
             K = w.prompt_tensor("k", b, g)
             keep, S = oracle.h2o_prompt_select(Q, K, w.budget, w.n_recent)
-            np.testing.assert_allclose(r["s"][b, g], S, rtol=RTOL_S, atol=1e-6, err_msg=f"scores b={b} g={g}")
+            np.testing.assert_allclose(r["s"][b, g], S, rtol=RTOL_S, atol=1e-9, err_msg=f"scores b={b} g={g}")
             got, k = _check_selection(w, r, b, g)
             if k:
                 Np = w.n_prompt - min(w.n_recent, min(w.budget, w.n_prompt))
-                kth = np.sort(S[:Np].astype(np.float32).astype(np.float64))[::-1][k - 1]
+                kth = np.sort(S[:Np])[::-1][k - 1]
                 for i in sorted(set(got[:k].tolist()) ^ set(keep[:k].tolist())):
                     gap = abs(S[i] - kth) / kth
                     print(f"  near-tie b={b} g={g} pos={i} rel gap {gap:.2e}")
@@ -117,22 +120,13 @@ def test_h2o_prompt_full_size(L):
     r = _compress(L, w)
     G, N, D = w.n_q_heads // w.n_kv_heads, w.n_prompt, w.head_dim
     tot = r["s"].sum(axis=-1, dtype=np.float64)
-    np.testing.assert_allclose(tot, G * N, rtol=1e-4)  # each causal row's weights sum to one
+    np.testing.assert_allclose(tot, G * N, rtol=1e-5)  # each causal row's weights sum to one
     for b in range(w.batch):
         for g in range(w.n_kv_heads):
             _check_selection(w, r, b, g)
+    tail = 2048
     for (b, g) in [(0, 0), (9, 5)]:
-        print(f"[h2o prompt] exact tail scores b={b} g={g}", flush=True)
-        K = w.prompt_tensor("k", b, g)
-        tail = 64
-        ref = np.zeros(tail)
-        for j in range(G):
-            Qh = w.prompt_tensor("q", b, g * G + j)[N - tail:]
-            X = (Qh @ K.T) / np.sqrt(D)  # rows N-64 .. N-1 against every key
-            for i in range(tail):
-                t = N - tail + i
-                x = X[i, : t + 1]
-                a = np.exp(x - x.max())
-                a /= a.sum()
-                ref[: i + 1] += a[N - tail:]
-        np.testing.assert_allclose(r["s"][b, g, N - tail:], ref, rtol=RTOL_S, atol=1e-6)
+        print(f"[h2o prompt] exact scores of the last {tail} keys b={b} g={g}", flush=True)
+        Q = np.stack([w.prompt_tensor("q", b, g * G + j) for j in range(G)], axis=1)
+        ref = oracle.h2o_prompt_scores(Q, w.prompt_tensor("k", b, g), rows_per_group=128, first_row=N - tail)
+        np.testing.assert_allclose(r["s"][b, g, N - tail:], ref[N - tail:], rtol=RTOL_S, atol=1e-9)

@@ -69,8 +69,7 @@ def _run(L, w, pool=0, out_rows=0, check_heads=None):
         assert set(own.tolist()) == set(got[:K].tolist()), f"selection b={b} h={h} not the top-k of its scores"
         # kept set vs oracle, near-ties excepted
         if K:
-            S32 = S.astype(np.float32).astype(np.float64)
-            kth = np.sort(S32)[::-1][K - 1]
+            kth = np.sort(S)[::-1][K - 1]
             diff = set(got[:K].tolist()) ^ set(ref_idx[:K].tolist())
             for i in sorted(diff):
                 gap = abs(S[i] - kth) / kth

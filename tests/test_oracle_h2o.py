@@ -25,8 +25,7 @@ def _mask_simulation(Q, K, V, budget, n_recent, scale):
         ev = None
         if alive.sum() == budget:
             cand = np.flatnonzero(alive & (np.arange(T) <= t - n_recent))
-            s32 = s[cand].astype(np.float32)
-            order = np.lexsort((-cand, s32))  # primary: s (ascending), then newer first
+            order = np.lexsort((-cand, s[cand]))  # primary: s (ascending), then newer first
             ev = int(cand[order[0]])
             alive[ev] = False
             s[ev] = 0.0
@@ -117,7 +116,7 @@ def test_prompt_selection_pins():
     np.testing.assert_allclose(s, ref, atol=1e-12)
     keep, _ = oracle.h2o_prompt_select(Q, K, budget=8, n_recent=3)
     assert list(keep[-3:]) == [17, 18, 19] and len(keep) == 8
-    top = np.lexsort((np.arange(17), -ref[:17].astype(np.float32)))[:5]
+    top = np.lexsort((np.arange(17), -ref[:17]))[:5]
     assert sorted(top) == list(keep[:5])
 
 
@@ -143,7 +142,7 @@ def test_block_size_one_is_token_level_h2o():
 
 def test_block_eviction_frees_whole_blocks_by_summed_score():
     """Literal pin of the rule: at each boundary with the budget full, the freed block is
-    the candidate with the smallest float32 sum of its tokens' s (ties: newer block),
+    the candidate with the smallest sum of its tokens' s (ties: newer block),
     computed here from a separately tracked per-token score table."""
     T, G, D, NB, BS, R = 120, 2, 8, 4, 8, 5
     Q, K, V = _bstream(T, G, D, 12)
@@ -156,7 +155,7 @@ def test_block_eviction_frees_whole_blocks_by_summed_score():
         assert len(toks) <= NB * BS and len(head.blocks) <= NB
         if freed is not None:
             cands = [blk for blk in before if max(blk) <= t - R]
-            want = min(cands, key=lambda blk: (float(np.float32(sum(s_tab[p] for p in blk))), -max(blk)))
+            want = min(cands, key=lambda blk: (sum(s_tab[p] for p in blk), -max(blk)))
             assert freed == want and len(freed) == BS
             for p in freed:
                 del s_tab[p]
@@ -185,3 +184,28 @@ def test_block_recent_protection():
         _, freed = head.step(t, Q[t], K[t], V[t])
         if freed is not None:
             assert max(freed) <= t - R
+
+
+def test_prompt_scores_equal_a_scalar_brute_force():
+    """s_j written out element by element with math.exp (no arrays, no softmax helper):
+    for every head h and row t >= j, exp(x_tj) / sum_{i <= t} exp(x_ti), summed."""
+    import math
+
+    rng = np.random.default_rng(21)
+    T, G, D = 7, 3, 4
+    Q, K = rng.standard_normal((T, G, D)), rng.standard_normal((T, D))
+    sc = 0.7
+    want = [0.0] * T
+    for h in range(G):
+        for t in range(T):
+            x = [sc * sum(float(Q[t, h, d]) * float(K[i, d]) for d in range(D)) for i in range(t + 1)]
+            den = sum(math.exp(v) for v in x)
+            for j in range(t + 1):
+                want[j] += math.exp(x[j]) / den
+    got = oracle.h2o_prompt_scores(Q, K, scale=sc, rows_per_group=2)  # row groups split the rows
+    np.testing.assert_allclose(got, want, rtol=1e-13, atol=0)
+    np.testing.assert_allclose(oracle.h2o_prompt_scores(Q, K, scale=sc, rows_per_group=T), want, rtol=1e-13, atol=0)
+    # rows from t = 4 on: exact for keys 4.. (no earlier row sees them)
+    tail = oracle.h2o_prompt_scores(Q, K, scale=sc, rows_per_group=2, first_row=4)
+    np.testing.assert_allclose(tail[4:], want[4:], rtol=1e-13, atol=0)
+    assert np.all(tail[:4] < np.array(want[:4]))

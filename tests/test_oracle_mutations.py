@@ -92,21 +92,21 @@ def _pool_inrange_divisor(s, kernel_size, mode="avg"):
 
 
 def _topk_ties_high(S, k):
-    S32 = np.asarray(S).astype(np.float32)
-    order = sorted(range(len(S32)), key=lambda i: (-float(S32[i]), -i))
+    S = np.asarray(S, np.float64)
+    order = sorted(range(len(S)), key=lambda i: (-float(S[i]), -i))
     return np.array(sorted(order[:k]), dtype=np.int64)
 
 
 def _victim_ties_old(self, t):
     c = [i for i, p in enumerate(self.pos) if p <= t - self.n_recent]
-    return min(c, key=lambda i: (float(np.float32(self.s[i])), self.pos[i]))
+    return min(c, key=lambda i: (self.s[i], self.pos[i]))
 
 
 def _victim_recent_excludes_new(self, t):
     c = [i for i, p in enumerate(self.pos) if p < t - self.n_recent]
     if not c:
         c = list(range(len(self.pos)))
-    return min(c, key=lambda i: (float(np.float32(self.s[i])), -self.pos[i]))
+    return min(c, key=lambda i: (self.s[i], -self.pos[i]))
 
 
 def _run_all(tests):
@@ -176,3 +176,30 @@ def test_h2o_mutants_are_caught(monkeypatch, mut):
             (th2o.test_two_independent_simulations_agree, (8, 3, 1)),
             (th2o.test_two_independent_simulations_agree, (12, 4, 4))]
     assert _run_all(pins) >= 1
+
+
+def _prompt_scores_mask_diagonal(Q, K, scale=None, rows_per_group=256):
+    """Mutant: a row does not see its own key (strict causal mask)."""
+    Q, K = np.asarray(Q, np.float64), np.asarray(K, np.float64)
+    T, G, D = Q.shape
+    sc = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    s = np.zeros(T)
+    for h in range(G):
+        X = (Q[:, h] @ K.T) * sc
+        X[np.arange(T)[None, :] >= np.arange(T)[:, None]] = -np.inf
+        X[0, 0] = 0.0  # row 0 would be empty
+        s += att.softmax(X, axis=1).sum(axis=0)
+    return s
+
+
+def _prompt_scores_one_head(Q, K, scale=None, rows_per_group=256):
+    """Mutant: only the first query head of the group is summed."""
+    return h2o.__dict__["_orig_prompt_scores"](np.asarray(Q)[:, :1], K, scale, rows_per_group)
+
+
+@pytest.mark.parametrize("mut", [_prompt_scores_mask_diagonal, _prompt_scores_one_head])
+def test_h2o_prompt_score_mutants_are_caught(monkeypatch, mut):
+    monkeypatch.setitem(h2o.__dict__, "_orig_prompt_scores", h2o.h2o_prompt_scores)
+    monkeypatch.setattr(h2o, "h2o_prompt_scores", mut)
+    monkeypatch.setattr(oracle, "h2o_prompt_scores", mut)
+    assert _run_all([(th2o.test_prompt_scores_equal_a_scalar_brute_force, ())]) == 1

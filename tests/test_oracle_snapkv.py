@@ -55,8 +55,8 @@ def test_pool_rejects_even_kernel():
         oracle.pool1d(np.ones(4), 4)
 
 
-def _dominates(S32, i, j):
-    return (S32[i] > S32[j]) or (S32[i] == S32[j] and i < j)
+def _dominates(S, i, j):
+    return (S[i] > S[j]) or (S[i] == S[j] and i < j)
 
 
 @pytest.mark.parametrize("seed", range(6))
@@ -64,20 +64,21 @@ def test_topk_matches_brute_force_over_subsets(seed):
     rng = np.random.default_rng(seed)
     n, k = 9, 4
     S = rng.integers(0, 4, n).astype(np.float64) / 3.0  # many exact ties
-    S32 = S.astype(np.float32)
     winners = [set(c) for c in itertools.combinations(range(n), k)
-               if all(_dominates(S32, i, j) for i in c for j in set(range(n)) - set(c))]
+               if all(_dominates(S, i, j) for i in c for j in set(range(n)) - set(c))]
     assert len(winners) == 1
     got = oracle.select_topk(S, k)
     assert set(got) == winners[0] and list(got) == sorted(got)
 
 
-def test_topk_decides_in_float32():
-    # two scores equal in float32 but not in float64: the lower index wins
+def test_topk_ranks_exact_scores():
+    # two scores equal in float32 but not in float64: the higher exact score wins; an
+    # exact tie keeps the lower index
     a = 1.0
     b = 1.0 + 2.0**-30
     assert np.float32(a) == np.float32(b)
-    assert list(oracle.select_topk(np.array([a, b]), 1)) == [0]
+    assert list(oracle.select_topk(np.array([a, b]), 1)) == [1]
+    assert list(oracle.select_topk(np.array([b, b]), 1)) == [0]
 
 
 def test_equal_keys_keep_lowest_indices():
@@ -110,10 +111,9 @@ def test_compress_output_layout():
     assert np.all(np.diff(idx) > 0) and idx[k - 1] < N - L
     np.testing.assert_array_equal(Ko, K[idx])
     np.testing.assert_array_equal(Vo, V[idx])
-    # every kept prefix score is >= every dropped one (float32 decision)
-    S32 = S.astype(np.float32)
+    # every kept prefix score is >= every dropped one
     dropped = np.setdiff1d(np.arange(N - L), idx[:k])
-    assert S32[idx[:k]].min() >= S32[dropped].max()
+    assert S[idx[:k]].min() >= S[dropped].max()
 
 
 def test_keep_fraction_of_the_32k_example():
