@@ -13,7 +13,9 @@
  *               outputs) is allocated and owned by the caller.  The library
  *               allocates no device memory; a cache handle owns only host-side
  *               state (configuration, per-layer token counters) and
- *               lcd_kv_cache_destroy frees only that.
+ *               lcd_kv_cache_destroy frees only that.  The one piece of device
+ *               memory the library holds is the scratch array of
+ *               lcd_decode_step_noalloc, a static array of its code object.
  *   Pointers    "device" pointers must be device memory of the current HIP
  *               device, 16-byte aligned, laid out exactly as documented
  *               (row-major, innermost dimension last, no padding).
@@ -42,7 +44,7 @@
 extern "C" {
 #endif
 
-#define LCD_ABI_VERSION 3
+#define LCD_ABI_VERSION 4
 
 typedef enum lcd_status {
   LCD_OK = 0,
@@ -214,6 +216,21 @@ lcd_status lcd_decode_attn(lcd_cache* cache, int32_t layer, const void* q, float
  * are unchanged. */
 lcd_status lcd_decode_step(lcd_cache* cache, int32_t layer, const void* k, const void* v, const void* q,
                            float* out, void* ws, uint64_t ws_bytes, void* stream);
+
+/* decode_step_noalloc: lcd_decode_step for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * There is no workspace argument: the split partials go to a scratch buffer the library
+ * holds on each GPU, a 32 MiB file-scope device array resident until the process ends.
+ *   k, v, q, out  as lcd_decode_step; the scratch of the current device is used.
+ * Returns LCD_ESIZE, enqueueing nothing, when the cache's workspace (lcd_cache_sizes'
+ * ws_bytes) exceeds 32 MiB; otherwise the same checks, results and bookkeeping as
+ * lcd_decode_step, bit for bit.  The call allocates no memory (no hipMalloc / hipFree;
+ * the first call on a device resolves the array's address once).  Every call on a GPU
+ * shares that GPU's scratch and the scratch keeps the last call's contents (nothing in
+ * it needs clearing): calls that can overlap on one GPU (on different streams, or on
+ * streams not ordered with each other) race, and the caller must serialise them. */
+lcd_status lcd_decode_step_noalloc(lcd_cache* cache, int32_t layer, const void* k, const void* v, const void* q,
+                                   float* out, void* stream);
 
 /* Host-side queries (pure host functions, no HIP call; -1 on invalid arguments).
  *   lcd_kv_tokens   tokens appended so far to `layer` (int64 counter).

@@ -21,6 +21,7 @@ from ._lib import (  # noqa: F401
     cache_sizes,
     decode_attn,
     decode_step,
+    decode_step_noalloc,
     kv_append,
     kv_cache_destroy,
     kv_cache_init,

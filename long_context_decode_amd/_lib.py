@@ -78,6 +78,7 @@ _SIGS = {
     "lcd_kv_append": (_S, [_P, _I32, _P, _P, _I32, _P]),
     "lcd_decode_attn": (_S, [_P, _I32, _P, _P, _P, _U64, _P]),
     "lcd_decode_step": (_S, [_P, _I32, _P, _P, _P, _P, _P, _U64, _P]),
+    "lcd_decode_step_noalloc": (_S, [_P, _I32, _P, _P, _P, _P, _P]),
     "lcd_kv_tokens": (_I64, [_P, _I32]),
     "lcd_kv_filled": (_I64, [_P, _I32]),
     "lcd_kv_slot_of": (_I64, [_P, _I32, _I64]),
@@ -177,6 +178,11 @@ def decode_step(h, layer, k, v, q, out, ws, ws_bytes, stream=None):
     """Append one token (k, v: [B][H_kv][D]) and attend q over the cache, one launch."""
     _check(lib.lcd_decode_step(h, layer, _ptr(k), _ptr(v), _ptr(q), _ptr(out), _ptr(ws), ws_bytes,
                                _stream(stream)))
+
+
+def decode_step_noalloc(h, layer, k, v, q, out, stream=None):
+    """decode_step with the split partials in the library's device scratch (no workspace)."""
+    _check(lib.lcd_decode_step_noalloc(h, layer, _ptr(k), _ptr(v), _ptr(q), _ptr(out), _stream(stream)))
 
 
 def kv_tokens(h, layer):

@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -47,6 +48,8 @@ uint64_t align256(uint64_t x) { return (x + 255u) & ~uint64_t(255); }
 bool mul_ok(uint64_t* acc, uint64_t f) { return !__builtin_mul_overflow(*acc, f, acc); }
 
 constexpr int64_t kMaxSlots = int64_t(1) << 24;
+// Device scratch of lcd_decode_step_noalloc (split partials): 32 MiB per GPU.
+constexpr uint64_t kScratchBytes = uint64_t(32) << 20;
 
 struct Layout {
   int C = 0, esize = 0, G = 0;
@@ -277,6 +280,17 @@ struct lcd_cache {
   std::vector<int> open_fill;
 };
 
+namespace {
+
+lcd_status check_layer(const lcd_cache* c, int32_t layer) {
+  if (!c) return fail(LCD_EINVAL, "cache is NULL");
+  if (layer < 0 || layer >= c->cfg.n_layers)
+    return fail(LCD_EINVAL, "layer %d out of range [0, %d)", layer, c->cfg.n_layers);
+  return LCD_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int lcd_abi_version(void) { return LCD_ABI_VERSION; }
@@ -343,13 +357,6 @@ lcd_status lcd_kv_cache_init(const lcd_cache_config* cfg, void* kv_mem, uint64_t
 }
 
 void lcd_kv_cache_destroy(lcd_cache* cache) { delete cache; }
-
-static lcd_status check_layer(const lcd_cache* c, int32_t layer) {
-  if (!c) return fail(LCD_EINVAL, "cache is NULL");
-  if (layer < 0 || layer >= c->cfg.n_layers)
-    return fail(LCD_EINVAL, "layer %d out of range [0, %d)", layer, c->cfg.n_layers);
-  return LCD_OK;
-}
 
 lcd_status lcd_kv_append(lcd_cache* c, int32_t layer, const void* k, const void* v, int32_t n_new, void* stream) {
   lcd_status st = check_layer(c, layer);
@@ -563,21 +570,9 @@ lcd_status launch_decode(lcd_cache* c, int32_t layer, const void* q, float* out,
   return ok();
 }
 
-}  // namespace
-
-extern "C" {
-
-lcd_status lcd_decode_attn(lcd_cache* c, int32_t layer, const void* q, float* out, void* ws, uint64_t ws_bytes,
-                           void* stream) {
-  lcd_status st = check_layer(c, layer);
-  if (st) return st;
-  if ((st = check_decode_args(c, q, out, ws, ws_bytes))) return st;
-  if (c->tokens[layer] < 1 || c->filled[layer] < 1) return fail(LCD_EINVAL, "layer %d holds no token", layer);
-  return launch_decode(c, layer, q, out, ws, stream, nullptr, nullptr, -1);
-}
-
-lcd_status lcd_decode_step(lcd_cache* c, int32_t layer, const void* k, const void* v, const void* q, float* out,
-                           void* ws, uint64_t ws_bytes, void* stream) {
+// lcd_decode_step and lcd_decode_step_noalloc: one token appended and attended in one launch.
+lcd_status decode_step_impl(lcd_cache* c, int32_t layer, const void* k, const void* v, const void* q, float* out,
+                            void* ws, uint64_t ws_bytes, void* stream) {
   lcd_status st = check_layer(c, layer);
   if (st) return st;
   if (c->cfg.policy != LCD_SINK_RING && c->cfg.policy != LCD_APPEND)
@@ -609,6 +604,69 @@ lcd_status lcd_decode_step(lcd_cache* c, int32_t layer, const void* k, const voi
     c->filled[layer] = f_prev;
   }
   return st;
+}
+
+// ---------------------------------------------------------------- device scratch
+// The split partials of lcd_decode_step_noalloc live in this file-scope device array
+// (one copy per GPU, held until the process ends).  Host code never passes the array's
+// name to a kernel: its device address is resolved once per device with
+// hipGetSymbolAddress (with that device current) and cached here.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+}  // namespace
+
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+
+lcd_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(LCD_EUNSUPPORTED, "device %d beyond the scratch table", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p || (reinterpret_cast<uintptr_t>(p) & 255u)) return fail(LCD_EHIP, "scratch address not 256-byte aligned");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LCD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+lcd_status lcd_decode_attn(lcd_cache* c, int32_t layer, const void* q, float* out, void* ws, uint64_t ws_bytes,
+                           void* stream) {
+  lcd_status st = check_layer(c, layer);
+  if (st) return st;
+  if ((st = check_decode_args(c, q, out, ws, ws_bytes))) return st;
+  if (c->tokens[layer] < 1 || c->filled[layer] < 1) return fail(LCD_EINVAL, "layer %d holds no token", layer);
+  return launch_decode(c, layer, q, out, ws, stream, nullptr, nullptr, -1);
+}
+
+lcd_status lcd_decode_step(lcd_cache* c, int32_t layer, const void* k, const void* v, const void* q, float* out,
+                           void* ws, uint64_t ws_bytes, void* stream) {
+  return decode_step_impl(c, layer, k, v, q, out, ws, ws_bytes, stream);
+}
+
+lcd_status lcd_decode_step_noalloc(lcd_cache* c, int32_t layer, const void* k, const void* v, const void* q,
+                                   float* out, void* stream) {
+  lcd_status st = check_layer(c, layer);
+  if (st) return st;
+  if (c->L.ws_bytes > kScratchBytes)
+    return fail(LCD_ESIZE, "decode_step_noalloc: this cache needs %llu workspace bytes, above the %llu-byte "
+                "device scratch buffer (use lcd_decode_step with a caller workspace)",
+                (unsigned long long)c->L.ws_bytes, (unsigned long long)kScratchBytes);
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws))) return st;
+  return decode_step_impl(c, layer, k, v, q, out, ws, kScratchBytes, stream);
 }
 
 int64_t lcd_kv_tokens(const lcd_cache* c, int32_t layer) {

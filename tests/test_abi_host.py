@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported(L):
     for name in declared:
         assert hasattr(L.lib, name), name
     assert set(declared) == set(L._lib.EXPORTED)
-    assert L.abi_version() == 3
+    assert L.abi_version() == 4
 
 
 def test_sizes_follow_the_kv_size_model(L):
@@ -101,6 +101,7 @@ def test_null_handle_calls_fail_cleanly(L):
     with pytest.raises(L.LcdError):
         L.kv_set_filled(None, 0, 1, 1, 0)
     assert L.lib.lcd_decode_step(None, 0, None, None, None, None, None, 0, None) == 1  # LCD_EINVAL
+    assert L.lib.lcd_decode_step_noalloc(None, 0, None, None, None, None, None) == 1  # LCD_EINVAL
 
 
 def test_snapkv_param_validation(L):
