@@ -24,6 +24,9 @@
 // exponentials are single exp2 instructions.
 #include <hip/hip_runtime.h>
 
+#include <climits>
+#include <type_traits>
+
 #include "lcd_internal.h"
 
 namespace lcd {
@@ -50,15 +53,6 @@ struct bf16_t {
 #ifndef LCD_U_OP_BIG
 #define LCD_U_OP_BIG 1  // one-pass keys per lane group per iteration for G > 2
 #endif
-#ifndef LCD_U2_G4
-#define LCD_U2_G4 4
-#endif
-#ifndef LCD_U2_G4R
-#define LCD_U2_G4R 3  // G = 4 with RoPE (4 keys leave one wave per SIMD)
-#endif
-#ifndef LCD_U2_G6
-#define LCD_U2_G6 2
-#endif
 #ifndef LCD_H2O_EU
 #define LCD_H2O_EU 16  // token-level H2O epilogue: slots per thread per iteration
 #endif
@@ -68,9 +62,7 @@ struct bf16_t {
 #ifndef LCD_MERGE_SU
 #define LCD_MERGE_SU 4  // split merge: splits whose loads are issued together
 #endif
-#ifndef LCD_REC2
-#define LCD_REC2 1  // two-pass kernel: RoPE angles by angle addition within an iteration
-#endif
+
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -167,7 +159,54 @@ constexpr int kDppRowMirror = 0x140;      // lane i <-> 15 - i within each 16 la
 
 template <int CTRL>
 __device__ inline float dpp_mov(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+
+constexpr int kDppRowShr4 = 0x114;  // lane i <- i - 4 within each 16 lanes
+constexpr int kDppRowRor4 = 0x124;  // lane i <- (i + 4) mod 16 within each 16 lanes
+constexpr int kDppRowRor8 = 0x128;  // lane i <- (i + 8) mod 16 within each 16 lanes
+
+// Sums over aligned groups of N consecutive lanes (N in {4, 8, 16, 32}) of M values (M a
+// multiple of 4), leaving each lane M/4 of the totals.  The first two steps transpose:
+// partners (lanes i and i^1, then i and i^2) each keep half of their values and add the
+// partner's copy of that half, so a step costs half the adds of a plain butterfly step
+// (plus two selects per add); the remaining lane bits are summed in full.  Afterwards, with
+// b0 = lane & 1 and b1 = (lane >> 1) & 1, slot i < M/4 holds the group total of value
+// i + b0 * M/2 + b1 * M/4, in every lane for N = 4, 16 and 32 and in the lanes with bit 2
+// set for N = 8 (there the last step writes only those lanes).  Totals are identical in
+// every lane that holds them (each step adds a commutative pair).
+template <int N, int M>
+__device__ inline void group_sum_transposed(float (&x)[M], int lane) {
+  static_assert(M % 4 == 0 && (N == 4 || N == 8 || N == 16 || N == 32), "shape");
+  const bool b0 = (lane & 1) != 0, b1 = (lane & 2) != 0;
+  constexpr int H1 = M / 2, H2 = M / 4;
+#pragma unroll
+  for (int i = 0; i < H1; ++i) {
+    const float keep = b0 ? x[i + H1] : x[i];
+    const float send = b0 ? x[i] : x[i + H1];
+    x[i] = keep + dpp_mov<kDppXor1>(send);
+  }
+#pragma unroll
+  for (int i = 0; i < H2; ++i) {
+    const float keep = b1 ? x[i + H2] : x[i];
+    const float send = b1 ? x[i] : x[i + H2];
+    x[i] = keep + dpp_mov<kDppXor2>(send);
+  }
+  if constexpr (N == 8) {
+#pragma unroll
+    for (int i = 0; i < H2; ++i)  // lanes 4..7 (and 12..15) add lanes 0..3 (8..11)
+      x[i] += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x[i]), kDppRowShr4,
+                                                                    0xF, 0xA, false));
+  } else if constexpr (N >= 16) {
+#pragma unroll
+    for (int i = 0; i < H2; ++i) x[i] += dpp_mov<kDppRowRor4>(x[i]);
+#pragma unroll
+    for (int i = 0; i < H2; ++i) x[i] += dpp_mov<kDppRowRor8>(x[i]);
+    if constexpr (N == 32) {
+#pragma unroll
+      for (int i = 0; i < H2; ++i) x[i] += __shfl_xor(x[i], 16, 64);
+    }
+  }
 }
 
 // Sum over aligned groups of N consecutive lanes (N a power of two <= 64) of M
@@ -247,10 +286,11 @@ constexpr size_t onepass_lds_bytes() {
 // Dynamic LDS of the two-pass kernel: the logits [chunk][G] (reused for the 4 waves'
 // outputs [4][G][D] after the V pass), cross-wave reductions [4][G] and the
 // workgroup's (m, l) [2][G].
+constexpr int kTwopassRed = 64;  // cross-wave reduction floats: 4 waves x (U * G <= 16)
 template <int D, int G>
 inline size_t twopass_lds_floats(int chunk) {
   const size_t a = (size_t)chunk * G, o = (size_t)4 * G * D;
-  return (a > o ? a : o) + 6 * G;
+  return (a > o ? a : o) + kTwopassRed + 2 * G;
 }
 
 // The work item of linear index `item` (split, KV head g, batch row b), split slowest;
@@ -965,6 +1005,14 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_onepass_kernel(DecodePa
 // loaded once and accumulated with the G weights.  Registers then hold either the
 // queries (K pass) or the outputs (V pass), never both, which keeps G * D-sized state
 // within two waves per SIMD at 16-byte pieces.
+//
+// With G >= 4 this kernel is bound by VALU issue (G multiply-adds per key element in
+// each pass, against one byte loaded per 1/2 element), so the loops carry no per-key
+// work beyond that arithmetic: rows are addressed by 32-bit offsets from the range's
+// uniform base, a fused append's rows are written to the cache before the passes (so no
+// load selects between cache and input), in-cache positions come from the range's two
+// precomputed rank breakpoints, and only the last, partial iteration of each pass tests
+// keys against the end of the range.
 template <typename T, int D, int G, int MODE>
 __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodeParams p) {
   constexpr bool ROPE = MODE == kModeRope;
@@ -977,14 +1025,15 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
   constexpr int KPW = 64 / LPK;    // keys per wave per sub-step
   constexpr int KPI = 4 * KPW;     // keys per workgroup per sub-step
   constexpr int D2 = D / 2;
+  constexpr uint32_t ROW = D * sizeof(T);  // bytes per cache row
   static_assert(LPK >= 1 && LPK <= 64 && (64 % LPK) == 0, "lane mapping");
 
   extern __shared__ float smem[];
   const int region = (p.chunk * G > 4 * G * D ? p.chunk * G : 4 * G * D);
   float* xs = smem;                 // [chunk][G] logits, then weights
   float* ored = smem;               // [4][G][D] the waves' outputs (after the V pass), then [G][D]
-  float* red = smem + region;       // [4][G] cross-wave reductions
-  float* Mh = red + 4 * G;          // [G] the range's maxima
+  float* red = smem + region;       // [4][U * G] / [4][G] cross-wave reductions (kTwopassRed floats)
+  float* Mh = red + kTwopassRed;    // [G] the range's maxima
   float* Lh = Mh + G;               // [G] the range's sums
 
   // XCD-aware item order (see the one-pass kernel)
@@ -992,7 +1041,8 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
   const WorkItem wi = work_item(p, (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8));
   if (wi.split < 0) return;  // padding of the grid to a multiple of 8
   const int split = wi.split, g = wi.g, b = wi.b;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);  // wave-uniform
   const int sub = lane % LPK, kg = lane / LPK;
   const int i0 = sub * HALF;  // first pair index owned by this lane
   const HeadView hv = head_view<T, D>(p, b, g);
@@ -1000,14 +1050,20 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
   if (s_begin >= hv.n) return;  // never taken: every listed item holds at least one slot
   const int n_splits = (hv.n + p.chunk - 1) / p.chunk;
   const int cnt = min(hv.n - s_begin, p.chunk);
-  const char* kbase = hv.k;
-  const char* vbase = hv.v;
-  const size_t lo_off = (size_t)i0 * sizeof(T);
-  const size_t hi_off = (size_t)(D2 + i0) * sizeof(T);
-  // fused append: the new token's rows come from the input (the slot is written below)
-  const int new_key = p.new_slot - s_begin;  // key index of the new slot (outside 0..cnt-1 if none here)
-  const size_t new_row = ((size_t)b * p.Hkv + g) * D * sizeof(T);
-  write_new_rows<T, D>(p, b, g, s_begin, cnt);
+  // the range's rows: uniform bases and 32-bit offsets (a range spans at most
+  // chunk * ROW < 2^24 bytes)
+  const char* kw = hv.k + (size_t)s_begin * ROW;
+  const char* vw = hv.v + (size_t)s_begin * ROW;
+  const uint32_t lo_off = (uint32_t)i0 * sizeof(T);
+  const uint32_t hi_off = (uint32_t)(D2 + i0) * sizeof(T);
+  // fused append: the workgroup whose range holds the new token's slot writes its K and
+  // V rows into the cache first; after the barrier its loads read them like any other
+  // row (the stores have completed and the waves share the CU's caches)
+  if (p.new_slot >= s_begin && p.new_slot < s_begin + cnt) {  // workgroup-uniform
+    write_new_rows<T, D>(p, b, g, s_begin, cnt);
+    __threadfence_block();
+    __syncthreads();
+  }
 
   // ---- queries of the group: load, rotate at the query's position, pre-scale.  Without
   // RoPE, bf16 queries stay packed: the K pass takes exact bf16 x bf16 pair products
@@ -1017,7 +1073,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
   Words<4> qlo[G], qhi[G];
 #pragma unroll
   for (int j = 0; j < G; ++j) {
-    const char* qrow = reinterpret_cast<const char*>(p.q) + ((size_t)b * p.Hq + g * G + j) * D * sizeof(T);
+    const char* qrow = reinterpret_cast<const char*>(p.q) + ((size_t)b * p.Hq + g * G + j) * ROW;
     if constexpr (DOT2) {
       qlo[j] = load_words<4>(qrow + lo_off);
       qhi[j] = load_words<4>(qrow + hi_off);
@@ -1044,47 +1100,57 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
     }
   }
 
-  // ---- K pass: U keys per lane group per iteration; for up to 6 query heads the next
-  // iteration's loads are issued before this iteration's arithmetic (two register sets
-  // alternate).  RoPE angles as in the one-pass kernel: one table row per iteration and
-  // angle additions of (cos, sin)(KPI * theta_i) for the following keys, except in waves
-  // that straddle a rank discontinuity, which read every key's row.
-  constexpr int U = G <= 4 ? (ROPE ? LCD_U2_G4R : LCD_U2_G4) : (G <= 6 ? LCD_U2_G6 : 2);
-  constexpr bool REC = ROPE && LCD_REC2;
-  constexpr int NCS = ROPE ? (REC ? 1 : U) : 1;  // table rows held per iteration
+  // ---- in-cache positions.  A slot's position is its number, except in a wrapped ring:
+  // there rank = slot + (slot >= S ? W - head : 0) - (slot >= S + head ? W : 0) with head
+  // the ring index of the oldest window token, i.e. two breakpoints in the range's key
+  // index, kb1 at the sink boundary and kb2 at the oldest token's slot (with head = 0
+  // the two jumps cancel and there are none).
+  int kb1 = INT_MAX, kb2 = INT_MAX;
+  if (ROPE && p.full && p.ring_head > 0) {
+    kb1 = p.S - s_begin;
+    kb2 = p.S + p.ring_head - s_begin;
+  }
+  const int jump1 = p.W - p.ring_head;
+  auto rank_of_key = [&](int key) { return s_begin + key + (key >= kb1 ? jump1 : 0) - (key >= kb2 ? p.W : 0); };
+  // table rows by 32-bit byte offsets from the uniform table bases (the host keeps a
+  // rotated cache's table below 4 GiB)
+  const char* cos_b = reinterpret_cast<const char*>(p.cos_t);
+  const char* sin_b = reinterpret_cast<const char*>(p.sin_t);
+  auto load_cs = [&](int rank, float (&c)[HALF], float (&sn)[HALF]) {
+    const uint32_t off = ((uint32_t)rank * D2 + (uint32_t)i0) * (uint32_t)sizeof(float);
+    load_floats<HALF>(reinterpret_cast<const float*>(cos_b + off), c);
+    load_floats<HALF>(reinterpret_cast<const float*>(sin_b + off), sn);
+  };
+
+  // ---- K pass: U keys per lane group per iteration, the next iteration's loads issued
+  // before this iteration's arithmetic (two register sets alternate; G = 8 has room for
+  // one).  RoPE: one table row per iteration, the following keys' angles by angle
+  // addition of (cos, sin)(KPI * theta_i), except in a wave whose keys of the iteration
+  // straddle a rank breakpoint, which reads every key's row.
+  constexpr int U = G <= 4 ? (ROPE ? 3 : 4) : 2;
+  static_assert(U * G % 4 == 0 && U * G <= 16, "lane-group sums leave U * G / 4 values per lane");
+  constexpr bool REC = ROPE;  // (reading every key's table row instead measured 10-20% slower)
   constexpr int STEP = KPI * U;
   float dc[HALF], ds[HALF];
   if constexpr (REC) {
     load_floats<HALF>(p.cos_t + (size_t)KPI * D2 + i0, dc);
     load_floats<HALF>(p.sin_t + (size_t)KPI * D2 + i0, ds);
   }
-  auto rank_of = [&](int slot) {
-    int rank = slot;
-    if (p.full && slot >= p.S) {
-      int r = slot - p.S - p.ring_head;
-      if (r < 0) r += p.W;
-      rank = p.S + r;
-    }
-    return rank;
-  };
-  auto load_cs = [&](int rank, float (&c)[HALF], float (&sn)[HALF]) {
-    load_floats<HALF>(p.cos_t + (size_t)rank * D2 + i0, c);
-    load_floats<HALF>(p.sin_t + (size_t)rank * D2 + i0, sn);
-  };
+  constexpr int NC = REC ? 1 : (ROPE ? U : 1);  // table rows held per iteration
   struct KBuf {
     Words<4> lo[U], hi[U];
-    float c[NCS][HALF], sn[NCS][HALF];
-    int mp[U];  // H2O blocks: the slots' positions (< 0: empty)
+    float c[NC][HALF], sn[NC][HALF];  // RoPE: table rows (with angle additions: the first key's)
+    int mp[U];                        // H2O blocks: the slots' positions (< 0: empty)
   };
   auto load_iter = [&](int base, KBuf& bf) {
     const int key0 = base + wave * KPW + kg;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int key = min(key0 + u * KPI, cnt - 1);  // unconditional loads, as in the one-pass kernel
-      const char* row = key == new_key ? reinterpret_cast<const char*>(p.k_new) + new_row
-                                       : kbase + (size_t)(s_begin + key) * D * sizeof(T);
-      bf.lo[u] = load_words<4>(row + lo_off);
-      bf.hi[u] = load_words<4>(row + hi_off);
+      // keys past the range load the range's last row (masked in the last iteration), so
+      // no branch separates the loads from their use
+      const uint32_t off = (uint32_t)min(key0 + u * KPI, cnt - 1) * ROW;
+      bf.lo[u] = load_words<4>(kw + (off + lo_off));
+      bf.hi[u] = load_words<4>(kw + (off + hi_off));
     }
     if constexpr (MASKED) {  // an in-range index for every lane, then a select on the value
       const int* mrow = p.mask_pos + ((size_t)b * p.Hkv + g) * p.C + s_begin;
@@ -1097,25 +1163,34 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
     }
     if constexpr (ROPE) {
 #pragma unroll
-      for (int u = 0; u < NCS; ++u) load_cs(rank_of(s_begin + min(key0 + u * KPI, cnt - 1)), bf.c[u], bf.sn[u]);
+      for (int u = 0; u < NC; ++u) load_cs(rank_of_key(min(key0 + u * KPI, cnt - 1)), bf.c[u], bf.sn[u]);
     }
   };
-  float mx[G];
+  // does this wave's set of keys at `base` straddle a rank breakpoint (wave-uniform)?
+  auto straddles = [&](int base) {
+    const int lo = base + wave * KPW, hi = lo + KPW - 1 + (U - 1) * KPI;
+    return (kb1 > lo && kb1 <= hi) || (kb2 > lo && kb2 <= hi);
+  };
+  // after the lane-group sums a lane holds NF = U * G / 4 of the iteration's U * G logits:
+  // value index vbase + i, i.e. key step slot_u[i] and query head slot_j[i]; the lanes that
+  // hold totals and write them ("writers") are one per index class of each key group
+  constexpr int NV = U * G, NF = NV / 4;
+  const int vbase = (lane & 1) * (NV / 2) + ((lane >> 1) & 1) * (NV / 4);
+  const bool writer = LPK == 8 ? (sub & 4) != 0 : sub < 4;
+  int slot_u[NF], slot_j[NF];
 #pragma unroll
-  for (int j = 0; j < G; ++j) mx[j] = -INFINITY;
-  auto compute_iter = [&](int base, KBuf& bf) {
+  for (int i = 0; i < NF; ++i) {
+    slot_u[i] = (vbase + i) / G;
+    slot_j[i] = (vbase + i) % G;
+  }
+  float mxs[NF];  // running maxima of this lane's value slots
+#pragma unroll
+  for (int i = 0; i < NF; ++i) mxs[i] = -INFINITY;
+  auto compute_iter = [&](int base, KBuf& bf, auto tail) {
+    constexpr bool TAIL = decltype(tail)::value;  // keys may lie past the range
     const int key0 = base + wave * KPW + kg;
-    bool stepwise = false;  // REC: this wave straddles a rank discontinuity
-    if constexpr (REC) {
-      const int rank0 = rank_of(s_begin + min(key0, cnt - 1));
-      bool disc = false;
-#pragma unroll
-      for (int u = 1; u < U; ++u) {
-        const int key = key0 + u * KPI;
-        disc |= key < cnt && rank_of(s_begin + key) != rank0 + u * KPI;
-      }
-      stepwise = __any(disc);
-    }
+    bool stepwise = false;
+    if constexpr (REC) stepwise = straddles(base);
     float d[U * G];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -1144,7 +1219,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
           if constexpr (REC) {
             if (u > 0) {
               if (stepwise) {
-                load_cs(rank_of(s_begin + min(key0 + u * KPI, cnt - 1)), bf.c[0], bf.sn[0]);
+                load_cs(rank_of_key(min(key0 + u * KPI, cnt - 1)), bf.c[0], bf.sn[0]);
                 wait_loads();  // complete here, so the common path keeps the next set's loads in flight
               } else {
 #pragma unroll
@@ -1171,36 +1246,38 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
       }
 #pragma unroll
       for (int j = 0; j < G; ++j) {
-        float acc = 0.f;
+        float acc = qf[j][0] * kf[0];  // (starting from a product, not a zeroed register)
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc = fmaf(qf[j][e], kf[e], acc);
+        for (int e = 1; e < EPL; ++e) acc = fmaf(qf[j][e], kf[e], acc);
         d[u * G + j] = acc;
       }
     }
-    group_sum_n<LPK, U * G>(d);
-    if constexpr (DOT2) {
+    // keys past the range (last iteration) and empty slots of a block cache: logit -inf in
+    // every lane of the group, so their totals are -inf
+    if constexpr (TAIL || MASKED) {
 #pragma unroll
-      for (int i = 0; i < U * G; ++i) d[i] *= p.qscale;
-    }
+      for (int u = 0; u < U; ++u) {
+        bool dead = false;
+        if constexpr (TAIL) dead = key0 + u * KPI >= cnt;
+        if constexpr (MASKED) dead = dead || bf.mp[u] < 0;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int key = key0 + u * KPI;
-      const bool valid = key < cnt;
-      if constexpr (MASKED) {  // empty slots (H2O blocks): logit -inf, weight 0
-        if (bf.mp[u] < 0) {
-#pragma unroll
-          for (int j = 0; j < G; ++j) d[u * G + j] = -INFINITY;
-        }
+        for (int j = 0; j < G; ++j) d[u * G + j] = dead ? -INFINITY : d[u * G + j];
       }
+    }
+    group_sum_transposed<LPK, NV>(d, lane);
 #pragma unroll
-      for (int j = 0; j < G; ++j) mx[j] = fmaxf(mx[j], valid ? d[u * G + j] : -INFINITY);
-      if (valid && sub == 0) {
+    for (int i = 0; i < NF; ++i) {
+      if constexpr (DOT2) d[i] *= p.qscale;
+      mxs[i] = fmaxf(mxs[i], d[i]);
+    }
+    if (writer) {
 #pragma unroll
-        for (int j = 0; j < G; ++j) xs[key * G + j] = d[u * G + j];
-        if constexpr (LOGITS) {
-#pragma unroll
-          for (int j = 0; j < G; ++j)
-            store_dev(&p.logits[((size_t)b * p.Hq + g * G + j) * p.C + s_begin + key], d[u * G + j]);
+      for (int i = 0; i < NF; ++i) {
+        const int key = key0 + slot_u[i] * KPI;
+        if (!TAIL || key < cnt) {
+          xs[key * G + slot_j[i]] = d[i];
+          if constexpr (LOGITS)
+            store_dev(&p.logits[((size_t)b * p.Hq + g * G + slot_j[i]) * p.C + s_begin + key], d[i]);
         }
       }
     }
@@ -1210,49 +1287,71 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
     if constexpr (KPF) {
       KBuf A, B;
       load_iter(0, A);
-      for (int base = 0; base < cnt; base += 2 * STEP) {
-        load_iter(base + STEP, B);  // unconditional (past the range: clamped rows)
-        compute_iter(base, A);
-        if (base + STEP >= cnt) break;
-        load_iter(base + 2 * STEP, A);
-        compute_iter(base + STEP, B);
+      int base = 0;
+      for (; base + 2 * STEP <= cnt; base += 2 * STEP) {  // both iterations wholly inside the range
+        load_iter(base + STEP, B);
+        compute_iter(base, A, std::false_type{});
+        load_iter(base + 2 * STEP, A);  // unconditional (past the range: clamped rows)
+        compute_iter(base + STEP, B, std::false_type{});
+      }
+      if (base < cnt) {  // one or two more iterations, the last partial
+        load_iter(base + STEP, B);
+        compute_iter(base, A, std::true_type{});
+        if (base + STEP < cnt) compute_iter(base + STEP, B, std::true_type{});
       }
     } else {
-      for (int base = 0; base < cnt; base += STEP) {
+      int base = 0;
+      for (; base + STEP <= cnt; base += STEP) {
         KBuf A;
         load_iter(base, A);
-        compute_iter(base, A);
+        compute_iter(base, A, std::false_type{});
+      }
+      if (base < cnt) {
+        KBuf A;
+        load_iter(base, A);
+        compute_iter(base, A, std::true_type{});
       }
     }
   }
 
   // first V rows are requested before the softmax barriers (their latency overlaps them)
   constexpr int UV = G <= 6 ? 4 : 2;
+  constexpr int VSTEP = KPI * UV;
   Words<4> vlo[UV], vhi[UV];
   auto load_v = [&](int base) {
 #pragma unroll
     for (int u = 0; u < UV; ++u) {
-      const int key = min(base + u * KPI + wave * KPW + kg, cnt - 1);  // unconditional loads
-      const char* row = key == new_key ? reinterpret_cast<const char*>(p.v_new) + new_row
-                                       : vbase + (size_t)(s_begin + key) * D * sizeof(T);
-      vlo[u] = load_words<4>(row + lo_off);
-      vhi[u] = load_words<4>(row + hi_off);
+      const uint32_t off = (uint32_t)min(base + u * KPI + wave * KPW + kg, cnt - 1) * ROW;  // unconditional loads
+      vlo[u] = load_words<4>(vw + (off + lo_off));
+      vhi[u] = load_words<4>(vw + (off + hi_off));
     }
   };
   load_v(0);
 
-  // ---- range maximum per query head
+  // ---- range maximum per query head: each value slot across the wave's key groups, the
+  // slots of the writer lanes of key group 0 into LDS [4 waves][U * G], then across waves
+  // and key steps
 #pragma unroll
-  for (int j = 0; j < G; ++j) {
-    const float m = wave_max(mx[j]);
-    if (lane == 0) red[wave * G + j] = m;
+  for (int i = 0; i < NF; ++i) {
+#pragma unroll
+    for (int off = LPK; off < 64; off <<= 1) mxs[i] = fmaxf(mxs[i], __shfl_xor(mxs[i], off, 64));
+  }
+  if (writer && kg == 0) {
+#pragma unroll
+    for (int i = 0; i < NF; ++i) red[wave * NV + vbase + i] = mxs[i];
   }
   __syncthreads();
   float M[G];
 #pragma unroll
-  for (int j = 0; j < G; ++j) M[j] = fmaxf(fmaxf(red[j], red[G + j]), fmaxf(red[2 * G + j], red[3 * G + j]));
-  if (threadIdx.x < G) Mh[threadIdx.x] = fmaxf(fmaxf(red[threadIdx.x], red[G + threadIdx.x]),
-                                               fmaxf(red[2 * G + threadIdx.x], red[3 * G + threadIdx.x]));
+  for (int j = 0; j < G; ++j) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+#pragma unroll
+      for (int u = 0; u < U; ++u) m = fmaxf(m, red[w * NV + u * G + j]);
+    M[j] = m;
+  }
+  if (threadIdx.x < G) Mh[threadIdx.x] = M[threadIdx.x];
   __syncthreads();  // red is reused below
 
   // ---- weights p = 2^(x - m) and their sums
@@ -1283,18 +1382,19 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
   for (int j = 0; j < G; ++j)
 #pragma unroll
     for (int e = 0; e < EPL; ++e) o[j][e] = 0.f;
-  for (int base = 0; base < cnt; base += KPI * UV) {
+  auto v_iter = [&](int base, auto tail) {
+    constexpr bool TAIL = decltype(tail)::value;
     Words<4> clo[UV], chi[UV];
 #pragma unroll
     for (int u = 0; u < UV; ++u) {
       clo[u] = vlo[u];
       chi[u] = vhi[u];
     }
-    load_v(base + KPI * UV);  // unconditional (past the range: clamped rows)
+    load_v(base + VSTEP);  // unconditional (past the range: clamped rows)
 #pragma unroll
     for (int u = 0; u < UV; ++u) {
       const int key = base + u * KPI + wave * KPW + kg;
-      if (key < cnt) {
+      if (!TAIL || key < cnt) {
         float lo[HALF], hi[HALF];
         E::cvt(clo[u], lo);
         E::cvt(chi[u], hi);
@@ -1309,6 +1409,11 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
         }
       }
     }
+  };
+  {
+    int base = 0;
+    for (; base + VSTEP <= cnt; base += VSTEP) v_iter(base, std::false_type{});
+    if (base < cnt) v_iter(base, std::true_type{});
   }
   __syncthreads();  // xs is reused as the waves' output buffer below
 
@@ -1423,9 +1528,9 @@ static hipError_t launch_t(int D, int G, int mode, const DecodeParams& p, hipStr
 
 int decode_chunk_cap(int G) {
   if (G <= LCD_ONEPASS_MAXG) return 1 << 24;  // the one-pass kernel keeps no per-slot state in LDS
-  // two-pass: chunk * G logits + 6 * G floats within 64 KiB, 256 bytes kept for the
-  // static shared variables
-  return (16384 - 64 - 6 * G) / G / 64 * 64;
+  // two-pass: chunk * G logits + the reduction and (max, sum) floats within 64 KiB, 256
+  // bytes kept for the static shared variables
+  return (16384 - 64 - kTwopassRed - 2 * G) / G / 64 * 64;
 }
 
 bool decode_supported(int dtype, int D, int G) {

@@ -122,6 +122,8 @@ lcd_status check_config(const lcd_cache_config* c, Layout* L) {
   const bool duo = c->policy == LCD_DUO;
   if (c->rope == 1 && !(std::isfinite(c->rope_base) && c->rope_base > 1.0))
     return fail(LCD_EINVAL, "rope_base must be finite and > 1");
+  if (c->rope == 1 && std::max<int64_t>(C, 65) * c->head_dim >= (int64_t(1) << 31))
+    return fail(LCD_ESHAPE, "a rotated cache needs (n_sink + window) * head_dim < 2^31 (position table below 4 GiB)");
   if (!(std::isfinite(c->scale) && c->scale >= 0.0)) return fail(LCD_EINVAL, "scale must be finite and >= 0");
 
   L->C = (int)C;
