@@ -1,4 +1,5 @@
-"""Host logic of bench.py (no GPU): the counter-traffic record and its staleness check."""
+"""Host logic of bench.py (no GPU): the counter-traffic records and their staleness check,
+the oracle baseline workers, the one-GPU refusal."""
 import csv
 import os
 import sys
@@ -23,32 +24,49 @@ def _csv(path, counter, rows):
                                                   "Grid_Size": 256, "Counter_Name": counter, "Counter_Value": val})
 
 
-def test_counter_summary_scales_by_calibration_copy(tmp_path):
-    dec = f"void lcd::{bench.DECODE_KERNEL}<lcd::bf16_t, 128, 1, 0>(lcd::DecodeParams)"
+def test_counter_summary_scales_by_calibration_copy(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    kernel, fname = bench.TRAFFIC["gqa_long"]
+    dec = f"void lcd::{kernel}(lcd::DecodeParams)"
+    other = "void lcd::decode_twopass_kernel<lcd::bf16_t, 128, 4, 0>(lcd::DecodeParams)"
     copy = "__amd_rocclr_copyBuffer"
     gib_kib = (1 << 30) / 1024
-    # fetch reads half the copied bytes, write all of them; a later copy of another size is ignored
+    # fetch reads half the copied bytes, write all of them; a later copy of another size and
+    # another decode instantiation are ignored
     _csv(tmp_path / "f.csv", "FETCH_SIZE", [("fill", 1.0), (copy, gib_kib / 2), (copy, gib_kib / 2),
-                                           (copy, gib_kib / 2), (dec, 1000.0), (dec, 1200.0), (copy, 7.0)])
+                                           (copy, gib_kib / 2), (dec, 1000.0), (dec, 1200.0), (copy, 7.0),
+                                           (other, 9e9)])
     _csv(tmp_path / "w.csv", "WRITE_SIZE", [(copy, gib_kib), (copy, gib_kib), (copy, gib_kib), (dec, 256.0),
                                            (dec, 256.0)])
-    out = tmp_path / "record.md"
-    traffic = bench._counter_summary(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), out=str(out))
+    traffic = bench._counter_summary(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), "gqa_long")
     assert traffic == pytest.approx(1100.0 * 1024 * 2 + 256.0 * 1024)
-    assert bench._traffic(str(out)) == int(round(traffic))
+    assert bench._traffic("gqa_long") == int(round(traffic))
+    out = tmp_path / fname
+    assert "--kernel-include-regex" in out.read_text()
     # a record taken on other sources is stale
-    text = out.read_text().replace(bench._sources_digest(), "0" * 64)
-    out.write_text(text)
-    assert bench._traffic(str(out)) is None
-    assert bench._traffic(str(tmp_path / "missing.md")) is None
+    out.write_text(out.read_text().replace(bench._sources_digest(), "0" * 64))
+    assert bench._traffic("gqa_long") is None
+    assert bench._traffic("llama3_8b_layer") is None  # no record in tmp_path
+    assert bench._traffic("tiny_streaming") is None  # no record kept for this workload
 
 
-def test_counter_summary_needs_the_calibration_copy(tmp_path):
-    dec = f"void lcd::{bench.DECODE_KERNEL}<lcd::bf16_t, 128, 1, 0>(lcd::DecodeParams)"
+def test_counter_summary_needs_the_calibration_copy(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    dec = f"void lcd::{bench.TRAFFIC['gqa_long'][0]}(lcd::DecodeParams)"
     _csv(tmp_path / "f.csv", "FETCH_SIZE", [(dec, 1000.0)])
     _csv(tmp_path / "w.csv", "WRITE_SIZE", [(dec, 1000.0)])
     with pytest.raises(SystemExit):
-        bench._counter_summary(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), out=str(tmp_path / "r.md"))
+        bench._counter_summary(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), "gqa_long")
+
+
+def test_oracle_workers_time_their_share():
+    """The baseline workers run the oracle on disjoint shares and stop at their budget."""
+    done0, el0 = bench._worker_streaming(("tiny_streaming", 0, 2, 100, 3, 10.0))
+    done1, el1 = bench._worker_streaming(("tiny_streaming", 1, 2, 100, 3, 10.0))
+    assert done0 + done1 == 3 and el0 > 0  # 1 slice per step, three steps, split two ways
+    done, el = bench._worker_streaming(("tiny_streaming", 0, 1, 100, 50, 0.0))
+    assert done == 0 and el == 0.0  # no budget: nothing timed
+    assert 1 <= bench._oracle_cores() <= 16
 
 
 def test_more_than_one_gpu_is_refused(capsys):
