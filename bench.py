@@ -260,8 +260,8 @@ class _Stepper:
 
     @property
     def fused(self):
-        """Streaming caches run one lcd_decode_step launch per layer and token."""
-        return self.w.kind == "streaming"
+        """Streaming and H2O caches run one lcd_decode_step launch per layer and token."""
+        return self.w.kind in ("streaming", "h2o")
 
     def step(self):
         i = self.i
@@ -302,7 +302,8 @@ class _Stepper:
             state = w.batch * w.n_kv_heads * self.slots * (4 + 4 + 4)  # score read+write, pos read
             if w.block_size > 1:
                 state += w.batch * w.n_kv_heads * self.slots * 4  # positions read again to skip emptied slots
-            return kv + io + logits + state
+            new_rows = 2 * w.batch * w.n_kv_heads * w.head_dim * w.esize  # the fused append's rows written
+            return kv + io + logits + state + new_rows
         if self.fused:  # the new rows are read from the input instead of the cache, then written
             return kv + io + 2 * w.batch * w.n_kv_heads * w.head_dim * w.esize
         return kv + io

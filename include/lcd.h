@@ -208,12 +208,15 @@ lcd_status lcd_decode_attn(lcd_cache* cache, int32_t layer, const void* q, float
  *   k, v   device, [batch][n_kv_heads][head_dim] in the cache dtype: the new token's
  *          rows (un-rotated).
  *   q, out, ws  as lcd_decode_attn.
- * The workgroup whose slot range holds the new token's slot reads the rows from k and
- * v and writes them into that slot; the cache contents and the output equal those of
- * the two calls (the same arithmetic in the same order).  SINK_RING and APPEND only
- * (others LCD_EUNSUPPORTED); APPEND needs a free slot (else LCD_ECAPACITY).  Advances
- * the layer's token counter by one; on an error nothing is enqueued and the counters
- * are unchanged. */
+ * The workgroup whose slot range holds the new token's slot writes the rows from k and
+ * v into that slot before attending; the cache contents and the output equal those of
+ * the two calls (the same arithmetic in the same order).  SINK_RING, APPEND and H2O
+ * (DUO: LCD_EUNSUPPORTED); APPEND needs a free slot (else LCD_ECAPACITY).  For a full
+ * H2O cache the slot is the victim the previous step chose on the device ([KVC]
+ * "Heavy-Hitter Oracle (H2O)...": evict, write, attend, accumulate in one launch), or the
+ * next slot of the open block / a freed block (block_size 16 / 32), and the step picks
+ * the next victim.  Advances the layer's token counter by one; on an error nothing is
+ * enqueued and the counters are unchanged. */
 lcd_status lcd_decode_step(lcd_cache* cache, int32_t layer, const void* k, const void* v, const void* q,
                            float* out, void* ws, uint64_t ws_bytes, void* stream);
 

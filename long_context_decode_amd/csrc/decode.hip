@@ -422,12 +422,19 @@ __device__ inline Victim reduce_victim(Victim v, unsigned long long* wk, int* wa
 // Fused append: the workgroup whose slot range [s_begin, s_begin + cnt) holds the new
 // token's slot writes its K and V rows into the cache (16-byte pieces, one per thread).
 // The launch never reads that slot from the cache: its loads take the input rows.
+// The slot a fused append writes for (row, KV head) bg (-1: none).
+__device__ inline int new_slot_of(const DecodeParams& p, size_t bg) {
+  if (!p.h2o_step || p.new_slot >= 0) return p.new_slot;
+  if (p.bs <= 1) return p.victim[bg];
+  return p.new_block ? p.victim[bg] * p.bs : p.open[bg] * p.bs + p.offset;
+}
+
 template <typename T, int D>
-__device__ inline void write_new_rows(const DecodeParams& p, int b, int g, int s_begin, int cnt) {
-  if (p.new_slot < s_begin || p.new_slot >= s_begin + cnt) return;
+__device__ inline void write_new_rows(const DecodeParams& p, int b, int g, int slot, int s_begin, int cnt) {
+  if (slot < s_begin || slot >= s_begin + cnt) return;
   constexpr int PIECES = D * (int)sizeof(T) / 16;  // per row
   const size_t src = ((size_t)b * p.Hkv + g) * D * sizeof(T);
-  const size_t dst = (((size_t)b * p.Hkv + g) * p.C + p.new_slot) * D * sizeof(T);
+  const size_t dst = (((size_t)b * p.Hkv + g) * p.C + slot) * D * sizeof(T);
   for (int i = threadIdx.x; i < 2 * PIECES; i += kDecodeThreads) {
     const bool is_v = i >= PIECES;
     const int piece = is_v ? i - PIECES : i;
@@ -572,7 +579,12 @@ __device__ inline void split_finish(const DecodeParams& p, float* ored, const fl
     __shared__ unsigned long long wkey[4];
     __shared__ int wat[4];
     float* score = p.score + bg * p.C;
-    const int* pos = p.pos + bg * p.C;
+    int* pos = const_cast<int*>(p.pos) + bg * p.C;
+    // a fused append's slot holds the new token (score 0 before this step's weight) and a
+    // reopened block's other slots are empty: this workgroup is the only writer of the
+    // position and score arrays in the launch, so it takes those values as known
+    const int nslot = p.h2o_step ? new_slot_of(p, bg) : -1;
+    const int emp_end = p.h2o_step && p.new_block ? nslot + p.bs : -1;
     Victim best;
     const int bs = BLOCKS ? p.bs : 1;  // eviction granule
     constexpr int EU = BLOCKS ? LCD_H2O_EU_BLK : LCD_H2O_EU;  // slots per thread per iteration, all loads issued first
@@ -589,6 +601,13 @@ __device__ inline void split_finish(const DecodeParams& p, float* ored, const fl
         for (int j = 0; j < G; ++j) x[u][j] = load_dev(&p.logits[(bh0 + j) * p.C + ic]);
         sc[u] = score[ic];
         ps[u] = pos[ic];
+      }
+#pragma unroll
+      for (int u = 0; u < EU; ++u) {
+        const int ic = i0 + u * kDecodeThreads;
+        const bool fresh = ic == nslot, emptied = ic > nslot && ic < emp_end;
+        sc[u] = fresh || emptied ? 0.f : sc[u];
+        ps[u] = fresh ? (int)p.token : emptied ? -1 : ps[u];
       }
       // arithmetic and victim folds first, the score stores last: a store issued before
       // a later branch would make the compiler's wait at that branch cover it too
@@ -618,6 +637,13 @@ __device__ inline void split_finish(const DecodeParams& p, float* ored, const fl
     if (p.pick_victim) {
       const Victim v = reduce_victim(best, wkey, wat);
       if (threadIdx.x == 0 && v.key != ~0ull) p.victim[bg] = v.at;
+    }
+    if (p.h2o_step) {  // the fused append's position record (and a reopened block's)
+      if (threadIdx.x == 0) {
+        pos[nslot] = (int)p.token;
+        if (p.new_block) p.open[bg] = nslot / p.bs;
+      }
+      if (p.new_block && threadIdx.x > 0 && (int)threadIdx.x < p.bs) pos[nslot + threadIdx.x] = -1;
     }
   }
 }
@@ -665,9 +691,12 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_onepass_kernel(DecodePa
   const size_t lo_off = (size_t)i0 * sizeof(T);
   const size_t hi_off = (size_t)(D2 + i0) * sizeof(T);
   // fused append: the new token's rows come from the input (the slot is written below)
-  const int new_key = p.new_slot - s_begin;  // key index of the new slot (outside 0..cnt-1 if none here)
+  const int nslot = new_slot_of(p, (size_t)b * p.Hkv + g);
+  const int new_key = nslot - s_begin;  // key index of the new slot (outside 0..cnt-1 if none here)
   const size_t new_row = ((size_t)b * p.Hkv + g) * D * sizeof(T);
-  write_new_rows<T, D>(p, b, g, s_begin, cnt);
+  write_new_rows<T, D>(p, b, g, nslot, s_begin, cnt);
+  // H2O blocks: a freed block reopened by this step holds only the new token
+  const int emp_lo = p.new_block ? new_key : INT_MAX, emp_hi = p.new_block ? new_key + p.bs : INT_MIN;
 
   // ---- queries of the group: load, rotate at the query's position, pre-scale (without
   // RoPE, bf16 queries stay packed for v_dot2_f32_bf16, as in the two-pass kernel)
@@ -762,7 +791,8 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_onepass_kernel(DecodePa
       for (int u = 0; u < U; ++u) {
         const int key = key0 + u * KPI;
         const int v = mrow[min(key, cnt - 1)];
-        bf.mp[u] = key < cnt ? v : -1;
+        // the new token's slot is filled; the rest of a reopened block is empty
+        bf.mp[u] = key >= cnt ? -1 : key == new_key ? 0 : (key > emp_lo && key < emp_hi) ? -1 : v;
       }
     }
     if constexpr (ROPE) {
@@ -1059,11 +1089,15 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
   // fused append: the workgroup whose range holds the new token's slot writes its K and
   // V rows into the cache first; after the barrier its loads read them like any other
   // row (the stores have completed and the waves share the CU's caches)
-  if (p.new_slot >= s_begin && p.new_slot < s_begin + cnt) {  // workgroup-uniform
-    write_new_rows<T, D>(p, b, g, s_begin, cnt);
+  const int nslot = new_slot_of(p, (size_t)b * p.Hkv + g);
+  if (nslot >= s_begin && nslot < s_begin + cnt) {  // workgroup-uniform
+    write_new_rows<T, D>(p, b, g, nslot, s_begin, cnt);
     __threadfence_block();
     __syncthreads();
   }
+  // H2O blocks: a freed block reopened by this step holds only the new token
+  const int new_key = nslot - s_begin;
+  const int emp_lo = p.new_block ? new_key : INT_MAX, emp_hi = p.new_block ? new_key + p.bs : INT_MIN;
 
   // ---- queries of the group: load, rotate at the query's position, pre-scale.  Without
   // RoPE, bf16 queries stay packed: the K pass takes exact bf16 x bf16 pair products
@@ -1158,7 +1192,8 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
       for (int u = 0; u < U; ++u) {
         const int key = key0 + u * KPI;
         const int v = mrow[min(key, cnt - 1)];
-        bf.mp[u] = key < cnt ? v : -1;
+        // the new token's slot is filled; the rest of a reopened block is empty
+        bf.mp[u] = key >= cnt ? -1 : key == new_key ? 0 : (key > emp_lo && key < emp_hi) ? -1 : v;
       }
     }
     if constexpr (ROPE) {

@@ -488,8 +488,14 @@ lcd_status check_decode_args(const lcd_cache* c, const void* q, const float* out
 
 // One decode launch over the layer's current state; with new_slot >= 0 the kernel also
 // writes the token's rows k_new / v_new into that slot (fused append).
+// H2O fused append: the new token's slot is chosen on the device unless the cache is
+// still filling (new_slot >= 0); new_block / offset as in the H2O append.
+struct FusedH2o {
+  int on = 0, new_block = 0, offset = 0;
+};
+
 lcd_status launch_decode(lcd_cache* c, int32_t layer, const void* q, float* out, void* ws, void* stream,
-                         const void* k_new, const void* v_new, int new_slot) {
+                         const void* k_new, const void* v_new, int new_slot, FusedH2o h2o = FusedH2o()) {
   const lcd_cache_config& cfg = c->cfg;
   const Layout& L = c->L;
   const int n = (int)c->filled[layer];
@@ -555,6 +561,11 @@ lcd_status launch_decode(lcd_cache* c, int32_t layer, const void* q, float* out,
   p.k_new = k_new;
   p.v_new = v_new;
   p.new_slot = new_slot;
+  p.h2o_step = h2o.on;
+  p.new_block = h2o.new_block;
+  p.offset = h2o.offset;
+  p.open = c->open_block(layer);
+  p.token = c->tokens[layer] - 1;  // the appended token (the state is the one after the append)
   if (cfg.policy == LCD_H2O) {
     p.score = c->score(layer);
     p.pos = c->pos(layer);
@@ -577,33 +588,53 @@ lcd_status decode_step_impl(lcd_cache* c, int32_t layer, const void* k, const vo
                             void* ws, uint64_t ws_bytes, void* stream) {
   lcd_status st = check_layer(c, layer);
   if (st) return st;
-  if (c->cfg.policy != LCD_SINK_RING && c->cfg.policy != LCD_APPEND)
-    return fail(LCD_EUNSUPPORTED, "decode_step is defined for the SINK_RING and APPEND caches");
+  if (c->cfg.policy == LCD_DUO)
+    return fail(LCD_EUNSUPPORTED, "decode_step is defined for the SINK_RING, APPEND and H2O caches");
   if (!k || !v) return fail(LCD_EINVAL, "k or v is NULL");
   if (!aligned16(k) || !aligned16(v)) return fail(LCD_EALIGN, "k or v is not 16-byte aligned");
   if ((st = check_decode_args(c, q, out, ws, ws_bytes))) return st;
   const int64_t t = c->tokens[layer];
   const int C = c->L.C;
-  int slot;
+  int slot = -1;
   int64_t filled;
+  FusedH2o h2o;
+  int open_fill = c->open_fill[layer];
   if (c->cfg.policy == LCD_SINK_RING) {
     const int64_t S = c->cfg.n_sink, W = c->cfg.window;
     slot = (int)(t < S ? t : S + (t - S) % W);
     filled = std::min<int64_t>(t + 1, C);
-  } else {
+  } else if (c->cfg.policy == LCD_APPEND) {
     if (c->filled[layer] + 1 > C)
       return fail(LCD_ECAPACITY, "append of 1 row to %lld filled of capacity %d", (long long)c->filled[layer], C);
     slot = (int)c->filled[layer];
     filled = c->filled[layer] + 1;
+  } else {  // H2O: as lcd_kv_append, the slot of a full cache chosen on the device
+    if (t > INT32_MAX) return fail(LCD_ECAPACITY, "H2O token positions are int32");
+    const int bs = c->bs(), fill = (int)c->filled[layer];
+    h2o.on = 1;
+    if (fill < C) {
+      slot = fill;
+      open_fill = (fill % bs) + 1;
+    } else if (open_fill >= bs) {  // a full cache needs a new block: the victim
+      h2o.new_block = bs > 1 ? 1 : 0;
+      open_fill = 1;
+    } else {
+      h2o.offset = open_fill;
+      open_fill = open_fill + 1;
+    }
+    filled = std::min<int64_t>(fill + 1, C);
   }
   // the launch sees the state after the append
   const int64_t t_prev = c->tokens[layer], f_prev = c->filled[layer];
+  const int o_prev = c->open_fill[layer];
   c->tokens[layer] = t + 1;
   c->filled[layer] = filled;
-  st = launch_decode(c, layer, q, out, ws, stream, k, v, slot);
+  c->open_fill[layer] = open_fill;
+  st = launch_decode(c, layer, q, out, ws, stream, k, v, slot, h2o);
   if (st) {  // nothing was enqueued: keep the bookkeeping as it was
     c->tokens[layer] = t_prev;
     c->filled[layer] = f_prev;
+    c->open_fill[layer] = o_prev;
   }
   return st;
 }

@@ -58,12 +58,19 @@ struct DecodeParams {
   int16_t duo_ret[kMaxDuoHeads];
   int16_t duo_str[kMaxDuoHeads];
   int ring_head;       // ring index of the oldest window token (rope mode, full)
-  // fused append (new_slot >= 0): the token's K / V rows ([B][Hkv][D], cache dtype) are
-  // read from k_new / v_new for slot new_slot and written there by the workgroup whose
-  // range holds it; no workgroup reads that slot from the cache
+  // fused append: the token's K / V rows ([B][Hkv][D], cache dtype) are read from k_new /
+  // v_new and written into its slot by the workgroup whose range holds that slot.  The
+  // slot is new_slot when >= 0; for an H2O cache (h2o_step = 1) with new_slot < 0 it is
+  // chosen on the device per (row, KV head): victim[bg] (token granule), victim[bg] * bs (a
+  // freed block, new_block = 1, whose other slots are emptied) or open[bg] * bs + offset.
+  // The merging workgroup records the token's position and zero score (and the emptied
+  // slots), so no slot of the position / score arrays has two writers in one launch.
   const void* k_new;
   const void* v_new;
   int new_slot;
+  int h2o_step, new_block, offset;
+  int* open;
+  int64_t token;
   int q_rank;          // in-cache position of the query (rope mode)
   float qscale;        // logit scale * log2(e)
 };

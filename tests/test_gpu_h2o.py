@@ -26,7 +26,7 @@ def L():
     return lib
 
 
-def _run(L, w, steps, sample, seeded):
+def _run(L, w, steps, sample, seeded, fused=False):
     dev = "cuda"
     B, Hq, Hkv, D, C, R = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.budget, w.n_recent
     G = Hq // Hkv
@@ -58,8 +58,11 @@ def _run(L, w, steps, sample, seeded):
     evictions = 0
     for s in range(steps):
         t = t0 + s
-        cache.append(0, k_all[s].unsqueeze(2), v_all[s].unsqueeze(2))
-        cache.decode(0, q_all[s], out)
+        if fused:  # one lcd_decode_step launch: append into the device-chosen slot, attend, score
+            cache.step(0, k_all[s], v_all[s], q_all[s], out)
+        else:
+            cache.append(0, k_all[s].unsqueeze(2), v_all[s].unsqueeze(2))
+            cache.decode(0, q_all[s], out)
         got = out.cpu().numpy().astype(np.float64)
         pos_gpu = pview.cpu().numpy()
         for (b, g) in sample:
@@ -76,8 +79,8 @@ def _run(L, w, steps, sample, seeded):
             if gpu_set != set(hd.pos):
                 gone = sorted(set(before) - gpu_set)
                 assert ev is not None and len(gone) == 1, f"t={t} b={b} g={g}: cache sets differ"
-                a, o = np.float32(before[gone[0]]), np.float32(before[ev])
-                gap = abs(float(a) - float(o)) / max(float(o), 1e-30)
+                a, o = before[gone[0]], before[ev]
+                gap = abs(a - o) / max(o, 1e-30)
                 print(f"  near-tie at t={t} b={b} g={g}: gpu evicted {gone[0]}, oracle {ev}, rel gap {gap:.2e}")
                 assert gap <= 1e-6, f"eviction differs beyond a near-tie ({gap:.2e})"
                 live[(b, g)] = False
@@ -91,21 +94,23 @@ def _run(L, w, steps, sample, seeded):
     return compared, evictions
 
 
-def test_h2o_from_empty_small(L):
+@pytest.mark.parametrize("fused", [False, True])
+def test_h2o_from_empty_small(L, fused):
     w = scaled(WORKLOADS["h2o_128k"], name="h2o_small", batch=2, n_q_heads=8, n_kv_heads=2, n_prompt=0,
                budget=64, n_recent=8, steps=220)
     sample = [(b, g) for b in range(2) for g in range(2)]
-    compared, ev = _run(L, w, 220, sample, seeded=False)
+    compared, ev = _run(L, w, 220, sample, seeded=False, fused=fused)
     print(f"[h2o small] compared {compared} head-steps, {ev} evictions")
     assert compared >= 4 * 150 and ev > 100
 
 
-def test_h2o_one_pass_kernel_g2(L):
+@pytest.mark.parametrize("fused", [False, True])
+def test_h2o_one_pass_kernel_g2(L, fused):
     """G=2, bf16, D=128 (the one-pass kernel's logits path), budget 96 over 250 steps."""
     w = scaled(WORKLOADS["h2o_128k"], name="h2o_g2", batch=2, n_q_heads=4, n_kv_heads=2, n_prompt=0,
                budget=96, n_recent=12, steps=250)
     sample = [(b, g) for b in range(2) for g in range(2)]
-    compared, ev = _run(L, w, 250, sample, seeded=False)
+    compared, ev = _run(L, w, 250, sample, seeded=False, fused=fused)
     print(f"[h2o G=2] compared {compared} head-steps, {ev} evictions")
     assert compared >= 4 * 150 and ev > 100
 
@@ -119,9 +124,10 @@ def test_h2o_sliding_window_case(L):
 
 
 def test_h2o_full_size_seeded(L):
-    """B=16, 32/8 heads, D=128, budget 4096 (512 recent), seeded 128k state; 3 heads in lockstep."""
+    """B=16, 32/8 heads, D=128, budget 4096 (512 recent), seeded 128k state; 3 heads in
+    lockstep, stepped as the bench steps it (one fused lcd_decode_step launch per token)."""
     w = WORKLOADS["h2o_128k"]
     print(f"[h2o_128k] {w.title}", flush=True)
-    compared, ev = _run(L, w, 200, [(0, 0), (7, 5), (15, 7)], seeded=True)
+    compared, ev = _run(L, w, 200, [(0, 0), (7, 5), (15, 7)], seeded=True, fused=True)
     print(f"  compared {compared} head-steps, {ev} evictions")
     assert compared >= 3 * 100 and ev >= 100

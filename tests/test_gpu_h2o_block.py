@@ -30,7 +30,7 @@ def L():
     return lib
 
 
-def _run(L, w, bs, steps, sample, seeded):
+def _run(L, w, bs, steps, sample, seeded, fused=False):
     dev = "cuda"
     B, Hq, Hkv, D, C, R = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.budget, w.n_recent
     G = Hq // Hkv
@@ -62,8 +62,11 @@ def _run(L, w, bs, steps, sample, seeded):
     atol = 1e-4 if w.dtype == "f32" else 2e-3
     for s in range(steps):
         t = t0 + s
-        cache.append(0, k_all[s].unsqueeze(2), v_all[s].unsqueeze(2))
-        cache.decode(0, q_all[s], out)
+        if fused:  # one lcd_decode_step launch: append into the open / freed block, attend, score
+            cache.step(0, k_all[s], v_all[s], q_all[s], out)
+        else:
+            cache.append(0, k_all[s].unsqueeze(2), v_all[s].unsqueeze(2))
+            cache.decode(0, q_all[s], out)
         got = out.cpu().numpy().astype(np.float64)
         pos_gpu = pview.cpu().numpy()
         for (b, g) in sample:
@@ -96,20 +99,22 @@ def _run(L, w, bs, steps, sample, seeded):
     return compared, frees
 
 
-def test_h2o_blocks_from_empty_two_pass(L):
+@pytest.mark.parametrize("fused", [False, True])
+def test_h2o_blocks_from_empty_two_pass(L, fused):
     """G=4 (two-pass kernel), 4 blocks of 16, 10 recent: fill, then a block freed every 16 steps."""
     w = scaled(WORKLOADS["h2o_128k"], name="h2o_blk16", batch=2, n_q_heads=8, n_kv_heads=2, n_prompt=0,
                budget=64, n_recent=10, steps=300)
-    compared, frees = _run(L, w, 16, 300, [(b, g) for b in range(2) for g in range(2)], seeded=False)
+    compared, frees = _run(L, w, 16, 300, [(b, g) for b in range(2) for g in range(2)], seeded=False, fused=fused)
     print(f"[h2o blocks 16] compared {compared} head-steps, {frees} blocks freed")
     assert compared >= 4 * 200 and frees >= 4 * 10
 
 
-def test_h2o_blocks_one_pass_fp32(L):
+@pytest.mark.parametrize("fused", [False, True])
+def test_h2o_blocks_one_pass_fp32(L, fused):
     """G=1 (one-pass kernel), fp32, D=64, 4 blocks of 32, 40 recent (spanning two blocks)."""
     w = scaled(WORKLOADS["h2o_128k"], name="h2o_blk32", batch=1, n_q_heads=2, n_kv_heads=2, head_dim=64,
                dtype="f32", n_prompt=0, budget=128, n_recent=40, steps=400)
-    compared, frees = _run(L, w, 32, 400, [(0, 0), (0, 1)], seeded=False)
+    compared, frees = _run(L, w, 32, 400, [(0, 0), (0, 1)], seeded=False, fused=fused)
     print(f"[h2o blocks 32] compared {compared} head-steps, {frees} blocks freed")
     assert compared >= 2 * 300 and frees >= 2 * 6
 
@@ -117,6 +122,6 @@ def test_h2o_blocks_one_pass_fp32(L):
 def test_h2o_blocks_full_size_seeded(L):
     """The 128k H2O workload with blocks of 16 (256 blocks, 512 recent), seeded state."""
     w = WORKLOADS["h2o_128k"]
-    compared, frees = _run(L, w, 16, 96, [(0, 0), (9, 3), (15, 7)], seeded=True)
+    compared, frees = _run(L, w, 16, 96, [(0, 0), (9, 3), (15, 7)], seeded=True, fused=True)
     print(f"[h2o blocks 128k] compared {compared} head-steps, {frees} blocks freed")
     assert compared >= 3 * 40 and frees >= 3
