@@ -54,6 +54,8 @@ def _parse(argv=None):
                     help="first run a plain 1 GiB device copy (reference for HBM byte counters)")
     ap.add_argument("--snapkv-only", action="store_true",
                     help="time the SnapKV compression alone and print its record (for profiling)")
+    ap.add_argument("--l-obs", type=int, default=None,
+                    help="with --snapkv-only: observation window of the 32k compression (default 32)")
     ap.add_argument("--counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of 'bench.py --only "
                          "--copy-calibration --workload NAME' into the traffic record of NAME and exit (no GPU)")
@@ -610,7 +612,13 @@ def main(argv=None):
     from synth import WORKLOADS
 
     if a.snapkv_only:
-        print(json.dumps(_snapkv_bench(L, WORKLOADS["snapkv_32k"])), flush=True)
+        from synth.workloads import scaled
+
+        sk = WORKLOADS["snapkv_32k"]
+        if a.l_obs:
+            sk = scaled(sk, name=f"snapkv_32k_obs{a.l_obs}", l_obs=a.l_obs,
+                        title=sk.title.replace("L_obs=32", f"L_obs={a.l_obs}"))
+        print(json.dumps(_snapkv_bench(L, sk)), flush=True)
         return 0
     if a.copy_calibration:
         _copy_calibration()
@@ -650,6 +658,15 @@ def main(argv=None):
         line["snapkv"] = _snapkv_bench(L, WORKLOADS["snapkv_32k"])
         if "snapkv_oracle" in cpu:
             line["snapkv"]["oracle"] = cpu["snapkv_oracle"]
+        # the observation window swept: the scoring product grows with L_obs, K's bytes do not
+        from synth.workloads import scaled
+
+        sweep = []
+        for lo in (64, 128, 256):
+            rec = _snapkv_bench(L, scaled(WORKLOADS["snapkv_32k"], name=f"snapkv_32k_obs{lo}", l_obs=lo), reps=10)
+            sweep.append({"l_obs": lo, "compress_ms": rec["compress_ms"], "qk_tflops": rec["qk_tflops"],
+                          "mfma_frac_bf16": rec["mfma_frac_bf16"], "mfma_ceiling": round(min(1.0, lo / 312.0), 3)})
+        line["snapkv"]["l_obs_sweep"] = sweep
     if not a.only and not a.no_h2o_prompt:
         line["h2o_prompt"] = _h2o_prompt_bench(L, WORKLOADS["h2o_prompt_128k"])
     if not a.only:

@@ -283,7 +283,7 @@ typedef struct lcd_snapkv_params {
   int32_t n_heads;      /* >= 1 (q_obs, k and v have the same head count)         */
   int32_t head_dim;     /* D in {64, 128, 256}                                    */
   int32_t n_prompt;     /* N >= 1, N - l_obs <= 65536 (LCD_ESHAPE otherwise)       */
-  int32_t l_obs;        /* 1 <= l_obs <= min(N, 64)                               */
+  int32_t l_obs;        /* 1 <= l_obs <= min(N, 256) (128 when head_dim = 256)    */
   int32_t kernel_size;  /* odd, 1 <= kernel_size <= 31                            */
   int32_t k_keep;       /* 0 <= k_keep <= N - l_obs                               */
   int32_t pool;         /* 0 = average, 1 = max                                   */

@@ -785,8 +785,9 @@ lcd_status check_snapkv(const lcd_snapkv_params* p) {
   if (p->batch < 1 || p->n_heads < 1 || p->n_prompt < 1) return fail(LCD_ESHAPE, "batch, n_heads, n_prompt >= 1");
   if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 256)
     return fail(LCD_ESHAPE, "head_dim %d not in {64, 128, 256}", p->head_dim);
-  if (p->l_obs < 1 || p->l_obs > 64 || p->l_obs > p->n_prompt)
-    return fail(LCD_ESHAPE, "l_obs %d outside [1, min(N, 64)]", p->l_obs);
+  const int max_obs = p->head_dim <= 128 ? 256 : 128;  // window queries staged in LDS beyond 64 rows
+  if (p->l_obs < 1 || p->l_obs > max_obs || p->l_obs > p->n_prompt)
+    return fail(LCD_ESHAPE, "l_obs %d outside [1, min(N, %d)]", p->l_obs, max_obs);
   if (p->kernel_size < 1 || p->kernel_size > 31 || p->kernel_size % 2 == 0)
     return fail(LCD_ESHAPE, "kernel_size must be odd and in [1, 31]");
   if (p->k_keep < 0 || p->k_keep > p->n_prompt - p->l_obs)

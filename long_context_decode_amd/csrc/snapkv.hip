@@ -36,9 +36,6 @@
 #ifndef LCD_GATHER_NT_STORE
 #define LCD_GATHER_NT_STORE 0
 #endif
-#ifndef LCD_ROWSTATS_NT
-#define LCD_ROWSTATS_NT 1
-#endif
 
 namespace lcd {
 
@@ -53,7 +50,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 #endif
 constexpr int kWaveBlocks = LCD_SNAPKV_WAVE_BLOCKS;  // 32-key blocks per wave in the scoring kernels
 constexpr int kTileKeys = 4 * kWaveBlocks * 32;  // keys per scoring workgroup
-constexpr int kMaxRows = 64;      // observation rows supported (two 32-row MFMA blocks)
+
 constexpr int kSelectThreads = 1024;
 
 __device__ inline bf16x8 load_frag(const uint16_t* p) {
@@ -133,11 +130,48 @@ __device__ inline void wave_lds_order() { __asm__ volatile("" ::: "memory"); }
 // B-column lane%32.
 __device__ inline int mfma_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
+// ---------------------------------------------------------------------------- window queries
+// The observation rows are RB blocks of 32.  Up to two blocks (L_obs <= 64) the query
+// fragments stay in registers for the whole pass; beyond that the workgroup stages the
+// window queries in LDS once (rows padded by 16 bytes, zero past L_obs) and each K block
+// loops over the row blocks, reading their fragments from LDS, RG blocks' accumulators at
+// a time (RG = min(RB, 4)).
+template <int D>
+constexpr int q_row_bytes() { return 2 * D + 16; }
+
+template <int D, int RB>
+struct QRows {
+  static constexpr bool kRegs = RB <= 2;
+  static constexpr int kRG = RB < 4 ? RB : 4;  // row blocks whose accumulators are live at once
+  static constexpr int kLdsBytes = kRegs ? 16 : RB * 32 * q_row_bytes<D>();
+};
+
+template <int D, int RB>
+__device__ inline void stage_q_rows(const uint16_t* q, int Lobs, char* qs) {
+  constexpr int PPR = D * 2 / 16;  // 16-byte pieces per row
+  for (int i = threadIdx.x; i < RB * 32 * PPR; i += 256) {
+    const int row = i / PPR, col = i % PPR;
+    const u32x4 v = row < Lobs ? *reinterpret_cast<const u32x4*>(q + (size_t)row * D + col * 8) : u32x4{0, 0, 0, 0};
+    *reinterpret_cast<u32x4*>(qs + row * q_row_bytes<D>() + col * 16) = v;
+  }
+}
+
+// Fragment of row block rb, k-step s (over the whole row): lane l holds row rb * 32 + l % 32,
+// elements 16 s + 8 (l / 32) .. + 7.
+template <int D>
+__device__ inline bf16x8 q_frag_lds(const char* qs, int rb, int s, int lane) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qs + (rb * 32 + (lane & 31)) * q_row_bytes<D>() +
+                                                                     32 * s + 16 * (lane >> 5)));
+}
+
 // ---------------------------------------------------------------------------- 1. rowstats
 template <int D, int RB>
 __global__ void __launch_bounds__(256) snapkv_rowstats_kernel(SnapkvParams p) {
-  __shared__ float sm[4][kMaxRows], sl[4][kMaxRows];
+  using QR = QRows<D, RB>;
+  constexpr int R = RB * 32, RG = QR::kRG;
+  __shared__ float sm[4][R], sl[4][R];
   __shared__ __attribute__((aligned(16))) char stage[4][block_lds_bytes<D>()];
+  __shared__ __attribute__((aligned(16))) char qs[QR::kLdsBytes];
   const int tile = blockIdx.x, h = p.h0 + blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const size_t bh = (size_t)b * p.H + h;
@@ -145,9 +179,18 @@ __global__ void __launch_bounds__(256) snapkv_rowstats_kernel(SnapkvParams p) {
   const uint16_t* k = reinterpret_cast<const uint16_t*>(p.k) + bh * (size_t)p.N * D;
   const int last_visible0 = p.N - p.Lobs;  // row t sees keys <= last_visible0 + t
   const int wkey0 = tile * kTileKeys + wave * kWaveBlocks * 32;
-  bf16x8 qf[RB][D / 16];
+  bf16x8 qf[QR::kRegs ? RB : 1][D / 16];
+  if constexpr (QR::kRegs) {
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) load_q_frags<D>(q, p.Lobs, rb, lane, qf[rb]);
+    for (int rb = 0; rb < RB; ++rb) load_q_frags<D>(q, p.Lobs, rb, lane, qf[rb]);
+  } else {
+    stage_q_rows<D, RB>(q, p.Lobs, qs);
+    __syncthreads();
+  }
+  auto qfrag = [&](int rb, int s) {
+    if constexpr (QR::kRegs) return qf[rb][s];
+    else return q_frag_lds<D>(qs, rb, s, lane);
+  };
   float m[RB], l[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
@@ -156,56 +199,76 @@ __global__ void __launch_bounds__(256) snapkv_rowstats_kernel(SnapkvParams p) {
   }
   constexpr int NC = D / chunk_w<D>();
   constexpr int FS = chunk_w<D>() / 16;  // fragments per chunk
+  static_assert(NC == 1 || RG == RB, "a row of two column chunks keeps every row block's accumulator");
+  // fold of row block rb's 32 x 32 tile (acc[r]: key key0 + mfma_row(r), row rb * 32 + lane % 32)
+  // into the row's running (max, sum of 2^(x - max)), the max kept on the raw products (the
+  // scale is positive) and each weight one FMA and one exp2.  Keys past the prompt or after
+  // the row's own position are masked, tested only on tiles that reach either.
+  auto fold = [&](int rb, const f32x16& acc, int key0) {
+    const int t = rb * 32 + (lane & 31);
+    float a[16];
+    const bool edge = key0 + 31 >= p.N || key0 + 31 > last_visible0;  // wave-uniform
+    if (edge) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + mfma_row(r, lane);
+        a[r] = key < p.N && key <= last_visible0 + t ? acc[r] : -INFINITY;
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) a[r] = acc[r];
+    }
+    float bm = a[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) bm = fmaxf(bm, a[r]);
+    const float mn = fmaxf(m[rb], bm);  // raw units
+    if (mn > -INFINITY && t < p.Lobs) {
+      const float off = -mn * p.qscale;
+      float add = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) add += exp2f(fmaf(a[r], p.qscale, off));
+      l[rb] = fmaf(l[rb], exp2f((m[rb] - mn) * p.qscale), add);
+      m[rb] = mn;
+    }
+  };
   u32x4 raw[chunk_pieces<D>()];
-  chunk_load<D, LCD_ROWSTATS_NT != 0>(k, p.N, wkey0, 0, lane, raw);
+  chunk_load<D, true>(k, p.N, wkey0, 0, lane, raw);
   for (int blk = 0; blk < kWaveBlocks; ++blk) {
     const int key0 = wkey0 + blk * 32;
     if (key0 >= p.N) break;  // wave-uniform
-    f32x16 acc[RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) acc[rb] = f32x16{};
+    f32x16 acc[RG];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       chunk_store_lds<D>(stage[wave], lane, raw);
       // prefetch the next chunk (of this block or the next one)
-      if (c + 1 < NC) chunk_load<D, LCD_ROWSTATS_NT != 0>(k, p.N, key0, c + 1, lane, raw);
-      else if (blk + 1 < kWaveBlocks) chunk_load<D, LCD_ROWSTATS_NT != 0>(k, p.N, key0 + 32, 0, lane, raw);
+      if (c + 1 < NC) chunk_load<D, true>(k, p.N, key0, c + 1, lane, raw);
+      else if (blk + 1 < kWaveBlocks) chunk_load<D, true>(k, p.N, key0 + 32, 0, lane, raw);
       wave_lds_order();
       bf16x8 kf[FS];
       chunk_frags_lds<D>(stage[wave], lane, kf);
       wave_lds_order();
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
+      for (int g0 = 0; g0 < RB; g0 += RG) {
+        if (NC == 1 || c == 0) {
 #pragma unroll
-        for (int s = 0; s < FS; ++s)
-          acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[rb][c * FS + s], acc[rb], 0, 0, 0);
-      }
-    }
+          for (int r = 0; r < RG; ++r) acc[r] = f32x16{};
+        }
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      // acc[rb][r]: key key0 + mfma_row(r), observation row t
-      const int t = rb * 32 + (lane & 31);
-      float x[16];
-      float bm = -INFINITY;
+        for (int r = 0; r < RG; ++r) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = key0 + mfma_row(r, lane);
-        const bool vis = key < p.N && key <= last_visible0 + t && t < p.Lobs;
-        x[r] = vis ? acc[rb][r] * p.qscale : -INFINITY;
-        bm = fmaxf(bm, x[r]);
-      }
-      const float mn = fmaxf(m[rb], bm);
-      if (mn > -INFINITY) {
-        float add = 0.f;
+          for (int s = 0; s < FS; ++s)
+            acc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qfrag(g0 + r, c * FS + s), acc[r], 0, 0, 0);
+        }
+        if (NC == 1 || c == NC - 1) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) add += exp2f(x[r] - mn);
-        l[rb] = l[rb] * exp2f(m[rb] - mn) + add;
-        m[rb] = mn;
+          for (int r = 0; r < RG; ++r) fold(g0 + r, acc[r], key0);
+        }
       }
     }
   }
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
+    m[rb] *= p.qscale;  // log2 units from here on (the -inf of an empty row stays -inf)
     // lanes l and l ^ 32 hold the same row
     const float mo = __shfl_xor(m[rb], 32, 64), lo = __shfl_xor(l[rb], 32, 64);
     const float mm = fmaxf(m[rb], mo);
@@ -217,14 +280,13 @@ __global__ void __launch_bounds__(256) snapkv_rowstats_kernel(SnapkvParams p) {
     }
   }
   __syncthreads();
-  if (threadIdx.x < RB * 32) {
-    const int t = threadIdx.x;
+  for (int t = threadIdx.x; t < R; t += 256) {
     float mm = -INFINITY;
     for (int w = 0; w < 4; ++w) mm = fmaxf(mm, sm[w][t]);
     float ll = 0.f;
     if (mm > -INFINITY)
       for (int w = 0; w < 4; ++w) ll += sl[w][t] * exp2f(sm[w][t] - mm);
-    float* out = p.rowstat + ((bh * p.tiles + tile) * kMaxRows + t) * 2;
+    float* out = p.rowstat + ((bh * p.tiles + tile) * R + t) * 2;
     out[0] = mm;
     out[1] = ll;
   }
@@ -233,8 +295,11 @@ __global__ void __launch_bounds__(256) snapkv_rowstats_kernel(SnapkvParams p) {
 // ---------------------------------------------------------------------------- 2. colscore
 template <int D, int RB>
 __global__ void __launch_bounds__(256) snapkv_colscore_kernel(SnapkvParams p) {
-  __shared__ float sM[kMaxRows], sI[kMaxRows];
+  using QR = QRows<D, RB>;
+  constexpr int R = RB * 32, RG = QR::kRG;
+  __shared__ float sM[R], sI[R];
   __shared__ __attribute__((aligned(16))) char stage[4][block_lds_bytes<D>()];
+  __shared__ __attribute__((aligned(16))) char qs[QR::kLdsBytes];
   // Walk K in the reverse of the row-statistics pass: the rows read last there are the
   // likeliest still cached.
   const int tile = gridDim.x - 1 - blockIdx.x, h = p.h0 + (int)(gridDim.y - 1 - blockIdx.y),
@@ -245,63 +310,73 @@ __global__ void __launch_bounds__(256) snapkv_colscore_kernel(SnapkvParams p) {
   // thread = (row t, part); each part merges every PARTS-th tile, 8 tiles' loads issued
   // together, then the parts are merged through LDS
   {
-    constexpr int R = RB * 32, PARTS = 256 / R, TU = 8;
+    constexpr int PARTS = R < 256 ? 256 / R : 1, TU = 8;
     __shared__ float pm[256], pl[256];
     const int t = threadIdx.x % R, part = threadIdx.x / R;
     float M = -INFINITY, L = 0.f;
-    for (int i0 = part; i0 < p.tiles; i0 += PARTS * TU) {
-      float2 st[TU];
+    if (t < R && part < PARTS) {
+      for (int i0 = part; i0 < p.tiles; i0 += PARTS * TU) {
+        float2 st[TU];
 #pragma unroll
-      for (int u = 0; u < TU; ++u) {
-        const int i = min(i0 + u * PARTS, p.tiles - 1);  // in range; extra tiles are dropped below
-        st[u] = *reinterpret_cast<const float2*>(p.rowstat + ((bh * p.tiles + i) * kMaxRows + t) * 2);
-      }
+        for (int u = 0; u < TU; ++u) {
+          const int i = min(i0 + u * PARTS, p.tiles - 1);  // in range; extra tiles are dropped below
+          st[u] = *reinterpret_cast<const float2*>(p.rowstat + ((bh * p.tiles + i) * R + t) * 2);
+        }
 #pragma unroll
-      for (int u = 0; u < TU; ++u) {
-        const float m = i0 + u * PARTS < p.tiles ? st[u].x : -INFINITY;
-        const float mn = fmaxf(M, m);
-        if (mn > -INFINITY) {
-          L = L * exp2f(M - mn) + (m > -INFINITY ? st[u].y * exp2f(m - mn) : 0.f);
-          M = mn;
+        for (int u = 0; u < TU; ++u) {
+          const float m = i0 + u * PARTS < p.tiles ? st[u].x : -INFINITY;
+          const float mn = fmaxf(M, m);
+          if (mn > -INFINITY) {
+            L = L * exp2f(M - mn) + (m > -INFINITY ? st[u].y * exp2f(m - mn) : 0.f);
+            M = mn;
+          }
         }
       }
     }
     pm[threadIdx.x] = M;
     pl[threadIdx.x] = L;
     __syncthreads();
-    if (threadIdx.x < kMaxRows) {
+    if (threadIdx.x < R) {
       float mm = -INFINITY, ll = 0.f;
-      if (threadIdx.x < R) {
-        for (int q = 0; q < PARTS; ++q) mm = fmaxf(mm, pm[q * R + threadIdx.x]);
-        if (mm > -INFINITY)
-          for (int q = 0; q < PARTS; ++q) ll += pl[q * R + threadIdx.x] * exp2f(pm[q * R + threadIdx.x] - mm);
-      }
+      for (int q = 0; q < PARTS; ++q) mm = fmaxf(mm, pm[q * R + threadIdx.x]);
+      if (mm > -INFINITY)
+        for (int q = 0; q < PARTS; ++q) ll += pl[q * R + threadIdx.x] * exp2f(pm[q * R + threadIdx.x] - mm);
       // rows past L_obs get zero weight
       const bool real = (int)threadIdx.x < p.Lobs && ll > 0.f;
       sM[threadIdx.x] = real ? mm : 0.f;
       sI[threadIdx.x] = real ? 1.f / ll : 0.f;
     }
-    __syncthreads();
   }
   const uint16_t* q = reinterpret_cast<const uint16_t*>(p.q_obs) + bh * p.Lobs * D;
   const uint16_t* k = reinterpret_cast<const uint16_t*>(p.k) + bh * (size_t)p.N * D;
   const int Np = p.N - p.Lobs;  // prefix keys: visible to every observation row
   const float inv_rows = 1.f / (float)p.Lobs;
   const int wkey0 = tile * kTileKeys + wave * kWaveBlocks * 32;
-  if (wkey0 >= Np) return;  // after the last __syncthreads
-  bf16x8 qf[RB][D / 16];
+  bf16x8 qf[QR::kRegs ? RB : 1][D / 16];
+  if constexpr (QR::kRegs) {
+    __syncthreads();  // sM / sI complete
+    if (wkey0 >= Np) return;
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) load_q_frags<D>(q, p.Lobs, rb, lane, qf[rb]);
+    for (int rb = 0; rb < RB; ++rb) load_q_frags<D>(q, p.Lobs, rb, lane, qf[rb]);
+  } else {
+    stage_q_rows<D, RB>(q, p.Lobs, qs);
+    __syncthreads();  // sM / sI and the staged rows complete
+    if (wkey0 >= Np) return;
+  }
+  auto qfrag = [&](int rb, int s) {
+    if constexpr (QR::kRegs) return qf[rb][s];
+    else return q_frag_lds<D>(qs, rb, s, lane);
+  };
   constexpr int NC = D / chunk_w<D>();
   constexpr int FS = chunk_w<D>() / 16;
+  static_assert(NC == 1 || RG == RB, "a row of two column chunks keeps every row block's accumulator");
   u32x4 raw[chunk_pieces<D>()];
   chunk_load<D, true>(k, Np, wkey0, 0, lane, raw);
   for (int blk = 0; blk < kWaveBlocks; ++blk) {
     const int key0 = wkey0 + blk * 32;
     if (key0 >= Np) break;  // wave-uniform
-    f32x16 acc[RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) acc[rb] = f32x16{};
+    float sc = 0.f;
+    f32x16 acc[RG];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       chunk_store_lds<D>(stage[wave], lane, raw);
@@ -312,20 +387,29 @@ __global__ void __launch_bounds__(256) snapkv_colscore_kernel(SnapkvParams p) {
       chunk_frags_lds<D>(stage[wave], lane, kf);
       wave_lds_order();
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
+      for (int g0 = 0; g0 < RB; g0 += RG) {
+        if (NC == 1 || c == 0) {
 #pragma unroll
-        for (int st = 0; st < FS; ++st)
-          acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[rb][c * FS + st], kf[st], acc[rb], 0, 0, 0);
-      }
-    }
-    float sc = 0.f;
+          for (int r = 0; r < RG; ++r) acc[r] = f32x16{};
+        }
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      // acc[rb][r]: observation row rb*32 + mfma_row(r), key key0 + lane%32
+        for (int r = 0; r < RG; ++r) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = rb * 32 + mfma_row(r, lane);
-        sc += exp2f(acc[rb][r] * p.qscale - sM[t]) * sI[t];
+          for (int st = 0; st < FS; ++st)
+            acc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qfrag(g0 + r, c * FS + st), kf[st], acc[r], 0, 0, 0);
+        }
+        if (NC == 1 || c == NC - 1) {
+          // acc[r][e]: observation row (g0 + r) * 32 + mfma_row(e), key key0 + lane % 32;
+          // weight 2^(acc * scale - M_t) / L_t as FMA, exp2, FMA
+#pragma unroll
+          for (int r = 0; r < RG; ++r) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int t = (g0 + r) * 32 + mfma_row(e, lane);
+              sc = fmaf(exp2f(fmaf(acc[r][e], p.qscale, -sM[t])), sI[t], sc);
+            }
+          }
+        }
       }
     }
     sc += __shfl_xor(sc, 32, 64);
@@ -640,34 +724,47 @@ size_t score_stride(int N, int Lobs) {
   return np ? (np + 3) / 4 * 4 : 4;
 }
 
+// Observation row blocks of 32 the scoring kernels run: 1, 2, 4 or 8.
+int row_blocks(int Lobs) {
+  const int rb = (Lobs + 31) / 32;
+  return rb <= 1 ? 1 : rb <= 2 ? 2 : rb <= 4 ? 4 : 8;
+}
+
 WsLayout ws_layout(int B, int H, int N, int Lobs) {
   const size_t bh = (size_t)B * H;
   const size_t tiles = (size_t)(N + kTileKeys - 1) / kTileKeys;
   const size_t st = score_stride(N, Lobs);
+  const size_t rows = (size_t)row_blocks(Lobs) * 32;  // per-tile row statistics, padded rows
   WsLayout w;
   w.rowstat = 0;
-  w.colscore = align256(w.rowstat + bh * tiles * kMaxRows * 2 * sizeof(float));
+  w.colscore = align256(w.rowstat + bh * tiles * rows * 2 * sizeof(float));
   w.pooled = align256(w.colscore + bh * st * sizeof(float));
   w.total = align256(w.pooled + bh * st * sizeof(float));
   return w;
 }
 
-template <int D>
-hipError_t launch_d(SnapkvParams p, hipStream_t s) {
-  const bool two = p.Lobs > 32;
-  const int np = p.N - p.Lobs;
-  p.h0 = 0;
+template <int D, int RB>
+void launch_scores(const SnapkvParams& p, int np, hipStream_t s) {
   const dim3 sgrid(p.tiles, p.H, p.B);
-  if (two)
-    hipLaunchKernelGGL((snapkv_rowstats_kernel<D, 2>), sgrid, dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL((snapkv_rowstats_kernel<D, 1>), sgrid, dim3(256), 0, s, p);
+  hipLaunchKernelGGL((snapkv_rowstats_kernel<D, RB>), sgrid, dim3(256), 0, s, p);
   if (np > 0) {
     const dim3 cgrid((np + kTileKeys - 1) / kTileKeys, p.H, p.B);
-    if (two)
-      hipLaunchKernelGGL((snapkv_colscore_kernel<D, 2>), cgrid, dim3(256), 0, s, p);
-    else
-      hipLaunchKernelGGL((snapkv_colscore_kernel<D, 1>), cgrid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((snapkv_colscore_kernel<D, RB>), cgrid, dim3(256), 0, s, p);
+  }
+}
+
+template <int D>
+hipError_t launch_d(SnapkvParams p, hipStream_t s) {
+  const int np = p.N - p.Lobs;
+  p.h0 = 0;
+  switch (row_blocks(p.Lobs)) {
+    case 1: launch_scores<D, 1>(p, np, s); break;
+    case 2: launch_scores<D, 2>(p, np, s); break;
+    case 4: launch_scores<D, 4>(p, np, s); break;
+    default:
+      if constexpr (D <= 128) launch_scores<D, 8>(p, np, s);  // (the host admits 256 rows at D <= 128 only)
+      else return hipErrorInvalidValue;
+      break;
   }
   // pooling is fused into the select kernel for kernel_size <= 9
   const bool fused = p.ksize <= 9;

@@ -107,7 +107,10 @@ def test_null_handle_calls_fail_cleanly(L):
 def test_snapkv_param_validation(L):
     ok = dict(batch=1, n_heads=32, head_dim=128, n_prompt=32768, l_obs=32, kernel_size=5, k_keep=5243)
     assert L.snapkv_sizes(L.snapkv_params(**ok)) > 0
-    for kw, status in [(dict(kernel_size=4), "LCD_ESHAPE"), (dict(l_obs=65), "LCD_ESHAPE"),
+    for l_obs, D in [(65, 128), (256, 128), (256, 64), (128, 256)]:  # windows up to 256 rows (128 at D = 256)
+        assert L.snapkv_sizes(L.snapkv_params(**(ok | dict(l_obs=l_obs, head_dim=D)))) > 0
+    for kw, status in [(dict(kernel_size=4), "LCD_ESHAPE"), (dict(l_obs=257), "LCD_ESHAPE"),
+                       (dict(l_obs=129, head_dim=256), "LCD_ESHAPE"),
                        (dict(k_keep=32768 - 31), "LCD_ESHAPE"), (dict(dtype=0), "LCD_EUNSUPPORTED"),
                        (dict(pool=2), "LCD_EINVAL"), (dict(out_rows=100), "LCD_ESHAPE"),
                        (dict(head_dim=80), "LCD_ESHAPE")]:

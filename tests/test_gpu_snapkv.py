@@ -99,6 +99,11 @@ BASE = WORKLOADS["snapkv_32k"]
     dict(batch=2, n_q_heads=2, n_prompt=2048, l_obs=32, k_keep=328),
     dict(n_q_heads=2, n_prompt=901, l_obs=16, k_keep=120, kernel_size=11),        # pooling kernel path
     dict(n_q_heads=1, n_prompt=40000, l_obs=8, k_keep=4000),                      # 64 scores per thread
+    # observation windows past two row blocks: window queries staged in LDS
+    dict(n_q_heads=2, n_prompt=1500, l_obs=128, k_keep=200),                      # 4 row blocks
+    dict(n_q_heads=2, n_prompt=2100, l_obs=256, k_keep=300),                      # 8 row blocks
+    dict(n_q_heads=2, n_prompt=901, l_obs=100, k_keep=100, head_dim=256),         # 4 blocks, two column chunks
+    dict(n_q_heads=1, n_prompt=700, l_obs=200, k_keep=50, head_dim=64, kernel_size=7),  # 8 blocks, ragged window
 ])
 def test_snapkv_small(L, case):
     w = scaled(BASE, name="snapkv_small_" + "_".join(f"{k}{v}" for k, v in case.items()), **case)
@@ -117,6 +122,16 @@ def test_snapkv_full_size(L):
     print(f"[snapkv_32k] {BASE.title}", flush=True)
     flips = _run(L, BASE)
     print(f"  near-tie flips across 32 heads: {flips}")
+
+
+@pytest.mark.parametrize("l_obs", [128, 256])
+def test_snapkv_full_prompt_wide_window(L, l_obs):
+    """N=32768, D=128 with an L_obs of 128 or 256 (the regime where the window's product is
+    MFMA-heavy): four of the 32 heads against the oracle."""
+    w = scaled(BASE, name=f"snapkv_32k_obs{l_obs}", l_obs=l_obs)
+    print(f"[snapkv_32k] L_obs={l_obs}", flush=True)
+    flips = _run(L, w, check_heads=[(0, 0), (0, 11), (0, 22), (0, 31)])
+    print(f"  near-tie flips on 4 heads: {flips}")
 
 
 def test_decode_over_compressed_cache(L):
