@@ -267,6 +267,43 @@ lcd_status lcd_kv_layer_view(const lcd_cache* cache, int32_t layer, void** k, vo
  * Otherwise nothing is enqueued. */
 lcd_status lcd_kv_set_filled(lcd_cache* cache, int32_t layer, int32_t n, int64_t next_token, void* stream);
 
+/* Checkpoint / resume --------------------------------------------------------
+ * A layer's whole state is its device arrays (K and V; for H2O also the slot positions
+ * and scores, the per-(row, KV head) victim slot and open block) and three host counters.
+ * lcd_kv_save copies the device arrays into caller buffers on `stream` and returns the
+ * counters; lcd_kv_load copies them back into a cache of the same configuration and sets
+ * the counters, after which the layer continues exactly as the saved one would have
+ * (decode outputs and later state bit for bit).  The library keeps nothing else per
+ * layer: the position table is a function of the configuration and the split-merge
+ * counters are zero between calls.
+ *   k, v          device, lcd_kv_layer_bytes(layer) bytes each: the layer's K and V blocks
+ *                 in the cache layout ([batch][n_kv_heads][C][head_dim], or the DUO
+ *                 per-layer layout of lcd_cache_sizes).
+ *   pos, score    device int32 / float32 [batch][n_kv_heads][C] (H2O; NULL otherwise).
+ *   victim, open  device int32 [batch][n_kv_heads] (H2O; NULL otherwise).
+ *   state         host: tokens appended, slots filled, tokens in the open block (H2O
+ *                 blocks).  lcd_kv_load checks it against the configuration (filled <=
+ *                 capacity, tokens >= filled, SINK_RING: filled = min(tokens, n_sink +
+ *                 window), DUO: filled = tokens, open_fill in [0, block size] and 0
+ *                 without H2O blocks); LCD_EINVAL otherwise, nothing enqueued.  An H2O
+ *                 layer past 2^31 - 1 tokens is refused with LCD_ECAPACITY.
+ * Buffers must not overlap the cache.  Asynchronous: the copies are ordered on `stream`. */
+typedef struct lcd_layer_state {
+  int64_t tokens;
+  int64_t filled;
+  int32_t open_fill;
+  int32_t reserved;  /* 0 */
+} lcd_layer_state;
+
+/* Bytes of one layer's K block (= its V block); -1 on invalid arguments.  Host-only. */
+int64_t lcd_kv_layer_bytes(const lcd_cache* cache, int32_t layer);
+
+lcd_status lcd_kv_save(const lcd_cache* cache, int32_t layer, void* k, void* v, int32_t* pos, float* score,
+                       int32_t* victim, int32_t* open, lcd_layer_state* state, void* stream);
+lcd_status lcd_kv_load(lcd_cache* cache, int32_t layer, const void* k, const void* v, const int32_t* pos,
+                       const float* score, const int32_t* victim, const int32_t* open,
+                       const lcd_layer_state* state, void* stream);
+
 /* SnapKV ---------------------------------------------------------------------
  * [KVC] "SnapKV e a seleção de contexto no prefill": at the end of prefill each
  * head keeps the prompt positions with the highest smoothed observation-window

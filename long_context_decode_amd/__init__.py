@@ -26,7 +26,11 @@ from ._lib import (  # noqa: F401
     kv_cache_destroy,
     kv_cache_init,
     kv_filled,
+    kv_layer_bytes,
     kv_layer_view,
+    kv_load,
+    kv_save,
+    LayerState,
     kv_rank_of,
     kv_set_filled,
     kv_slot_of,

@@ -34,6 +34,11 @@ class CacheConfig(ctypes.Structure):
                 ("retrieval", ctypes.POINTER(ctypes.c_int32)), ("block_size", ctypes.c_int32)]
 
 
+class LayerState(ctypes.Structure):
+    _fields_ = [("tokens", ctypes.c_int64), ("filled", ctypes.c_int64), ("open_fill", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
 class SnapkvParams(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("n_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("n_prompt", ctypes.c_int32), ("l_obs", ctypes.c_int32), ("kernel_size", ctypes.c_int32),
@@ -86,6 +91,9 @@ _SIGS = {
     "lcd_kv_layer_view": (_S, [_P, _I32, ctypes.POINTER(_P), ctypes.POINTER(_P), ctypes.POINTER(_P),
                                ctypes.POINTER(_P)]),
     "lcd_kv_set_filled": (_S, [_P, _I32, _I32, _I64, _P]),
+    "lcd_kv_layer_bytes": (_I64, [_P, _I32]),
+    "lcd_kv_save": (_S, [_P, _I32, _P, _P, _P, _P, _P, _P, ctypes.POINTER(LayerState), _P]),
+    "lcd_kv_load": (_S, [_P, _I32, _P, _P, _P, _P, _P, _P, ctypes.POINTER(LayerState), _P]),
     "lcd_snapkv_sizes": (_S, [ctypes.POINTER(SnapkvParams), ctypes.POINTER(_U64)]),
     "lcd_snapkv_compress": (_S, [ctypes.POINTER(SnapkvParams), _P, _P, _P, _P, _P, _P, _P, _P, _U64, _P]),
     "lcd_pyramid_budgets": (_S, [_I32, _I32, _I32, ctypes.POINTER(_I32)]),
@@ -212,6 +220,22 @@ def kv_set_filled(h, layer, n, next_token, stream=None):
     _check(lib.lcd_kv_set_filled(h, layer, n, next_token, _stream(stream)))
 
 
+def kv_layer_bytes(h, layer):
+    return lib.lcd_kv_layer_bytes(h, layer)
+
+
+def kv_save(h, layer, k, v, pos=None, score=None, victim=None, open_=None, stream=None) -> LayerState:
+    st = LayerState()
+    _check(lib.lcd_kv_save(h, layer, _ptr(k), _ptr(v), _ptr(pos), _ptr(score), _ptr(victim), _ptr(open_),
+                           ctypes.byref(st), _stream(stream)))
+    return st
+
+
+def kv_load(h, layer, k, v, pos, score, victim, open_, state: LayerState, stream=None):
+    _check(lib.lcd_kv_load(h, layer, _ptr(k), _ptr(v), _ptr(pos), _ptr(score), _ptr(victim), _ptr(open_),
+                           ctypes.byref(state), _stream(stream)))
+
+
 def snapkv_params(batch, n_heads, head_dim, n_prompt, l_obs, kernel_size, k_keep, pool=0, dtype=LCD_BF16,
                   out_rows=0, scale=0.0):
     return SnapkvParams(batch, n_heads, head_dim, n_prompt, l_obs, kernel_size, k_keep, pool, dtype, out_rows,
@@ -310,6 +334,28 @@ class KVCache:
         P = self.aux_mem[po: po + 4 * n].view(torch.int32).view(c.batch, c.n_kv_heads, c.capacity)
         S = self.aux_mem[so: so + 4 * n].view(torch.float32).view(c.batch, c.n_kv_heads, c.capacity)
         return P, S
+
+    def save_state(self, layer, device=None):
+        """Copy one layer's state into new device tensors; returns (tensors dict, LayerState)."""
+        import torch
+
+        dev = device or self.kv_mem.device
+        nb = kv_layer_bytes(self.handle, layer)
+        t = {"k": torch.empty(nb, dtype=torch.uint8, device=dev), "v": torch.empty(nb, dtype=torch.uint8, device=dev)}
+        c = self.cfg
+        if c.policy == LCD_H2O:
+            n = c.batch * c.n_kv_heads
+            t["pos"] = torch.empty(n * c.capacity, dtype=torch.int32, device=dev)
+            t["score"] = torch.empty(n * c.capacity, dtype=torch.float32, device=dev)
+            t["victim"] = torch.empty(n, dtype=torch.int32, device=dev)
+            t["open"] = torch.empty(n, dtype=torch.int32, device=dev)
+        st = kv_save(self.handle, layer, t["k"], t["v"], t.get("pos"), t.get("score"), t.get("victim"),
+                     t.get("open"))
+        return t, st
+
+    def load_state(self, layer, tensors, state):
+        kv_load(self.handle, layer, tensors["k"], tensors["v"], tensors.get("pos"), tensors.get("score"),
+                tensors.get("victim"), tensors.get("open"), state)
 
     def close(self):
         if self.handle:

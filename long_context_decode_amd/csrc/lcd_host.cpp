@@ -770,6 +770,101 @@ lcd_status lcd_kv_set_filled(lcd_cache* c, int32_t layer, int32_t n, int64_t nex
   return ok();
 }
 
+int64_t lcd_kv_layer_bytes(const lcd_cache* c, int32_t layer) {
+  if (check_layer(c, layer)) return -1;
+  return (int64_t)(c->cfg.policy == LCD_DUO ? c->L.duo_bytes[layer] : c->L.layer_bytes);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Checks shared by lcd_kv_save and lcd_kv_load: the buffers a layer's state needs.
+lcd_status check_state_buffers(const lcd_cache* c, const void* k, const void* v, const void* pos,
+                               const void* score, const void* victim, const void* open) {
+  if (!k || !v) return fail(LCD_EINVAL, "k or v is NULL");
+  if (!aligned16(k) || !aligned16(v)) return fail(LCD_EALIGN, "k or v is not 16-byte aligned");
+  if (c->cfg.policy == LCD_H2O) {
+    if (!pos || !score || !victim || !open) return fail(LCD_EINVAL, "an H2O layer needs pos, score, victim and open");
+  } else if (pos || score || victim || open) {
+    return fail(LCD_EINVAL, "pos, score, victim and open are H2O state (pass NULL)");
+  }
+  return LCD_OK;
+}
+
+// Copies of one layer's device state between the cache and caller buffers, on the stream.
+lcd_status copy_layer_state(const lcd_cache* c, int32_t layer, void* k, void* v, int32_t* pos, float* score,
+                            int32_t* victim, int32_t* open, bool save, hipStream_t s) {
+  const uint64_t kvb = c->cfg.policy == LCD_DUO ? c->L.duo_bytes[layer] : c->L.layer_bytes;
+  struct Item {
+    void* buf;
+    void* dev;
+    uint64_t bytes;
+  };
+  const uint64_t per_bg = (uint64_t)c->cfg.batch * c->cfg.n_kv_heads;
+  std::vector<Item> items = {{k, c->k_layer(layer), kvb}, {v, c->v_layer(layer), kvb}};
+  if (c->cfg.policy == LCD_H2O) {
+    items.push_back({pos, c->pos(layer), per_bg * c->L.C * sizeof(int32_t)});
+    items.push_back({score, c->score(layer), per_bg * c->L.C * sizeof(float)});
+    items.push_back({victim, c->victim(layer), per_bg * sizeof(int32_t)});
+    items.push_back({open, c->open_block(layer), per_bg * sizeof(int32_t)});
+  }
+  for (const Item& it : items) {
+    const hipError_t e = save ? hipMemcpyAsync(it.buf, it.dev, it.bytes, hipMemcpyDeviceToDevice, s)
+                              : hipMemcpyAsync(it.dev, it.buf, it.bytes, hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return hip_fail(e, save ? "kv_save copy" : "kv_load copy");
+  }
+  return LCD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+lcd_status lcd_kv_save(const lcd_cache* c, int32_t layer, void* k, void* v, int32_t* pos, float* score,
+                       int32_t* victim, int32_t* open, lcd_layer_state* state, void* stream) {
+  lcd_status st = check_layer(c, layer);
+  if (st) return st;
+  if (!state) return fail(LCD_EINVAL, "state is NULL");
+  if ((st = check_state_buffers(c, k, v, pos, score, victim, open))) return st;
+  if ((st = copy_layer_state(c, layer, k, v, pos, score, victim, open, true, static_cast<hipStream_t>(stream))))
+    return st;
+  state->tokens = c->tokens[layer];
+  state->filled = c->filled[layer];
+  state->open_fill = c->open_fill[layer];
+  state->reserved = 0;
+  return ok();
+}
+
+lcd_status lcd_kv_load(lcd_cache* c, int32_t layer, const void* k, const void* v, const int32_t* pos,
+                       const float* score, const int32_t* victim, const int32_t* open, const lcd_layer_state* state,
+                       void* stream) {
+  lcd_status st = check_layer(c, layer);
+  if (st) return st;
+  if (!state) return fail(LCD_EINVAL, "state is NULL");
+  if ((st = check_state_buffers(c, k, v, pos, score, victim, open))) return st;
+  const lcd_cache_config& cfg = c->cfg;
+  const int64_t C = c->L.C;
+  if (state->filled < 0 || state->filled > C || state->tokens < state->filled)
+    return fail(LCD_EINVAL, "state: need 0 <= filled <= capacity %lld and tokens >= filled", (long long)C);
+  if (cfg.policy == LCD_SINK_RING && state->filled != std::min<int64_t>(state->tokens, C))
+    return fail(LCD_EINVAL, "state: a sink + ring layer holds min(tokens, n_sink + window) slots");
+  if (cfg.policy == LCD_DUO && state->filled != state->tokens)
+    return fail(LCD_EINVAL, "state: a mixed-head layer's retrieval heads hold every token");
+  const int bs = c->bs();
+  if (state->open_fill < 0 || state->open_fill > bs || (cfg.policy != LCD_H2O && state->open_fill != 0))
+    return fail(LCD_EINVAL, "state: open_fill outside [0, block size]");
+  if (cfg.policy == LCD_H2O && state->tokens > INT32_MAX) return fail(LCD_ECAPACITY, "H2O token positions are int32");
+  if ((st = copy_layer_state(c, layer, const_cast<void*>(k), const_cast<void*>(v), const_cast<int32_t*>(pos),
+                             const_cast<float*>(score), const_cast<int32_t*>(victim), const_cast<int32_t*>(open),
+                             false, static_cast<hipStream_t>(stream))))
+    return st;
+  c->tokens[layer] = state->tokens;
+  c->filled[layer] = state->filled;
+  c->open_fill[layer] = state->open_fill;
+  return ok();
+}
+
 lcd_status lcd_snapkv_sizes(const lcd_snapkv_params* p, uint64_t* ws_bytes);
 lcd_status lcd_snapkv_compress(const lcd_snapkv_params* p, const void* q_obs, const void* k, const void* v,
                                void* k_out, void* v_out, int32_t* idx_out, float* scores_out, void* ws,

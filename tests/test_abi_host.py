@@ -238,3 +238,13 @@ def test_header_compiles_as_c_and_links(tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
     assert r.stdout.startswith("ok: abi ")
+
+
+def test_kv_save_load_validation_without_a_gpu(L):
+    """Argument checks of the checkpoint calls run before any HIP call."""
+    fake = 1 << 20
+    st = L.LayerState(0, 0, 0, 0)
+    assert L.kv_layer_bytes(None, 0) == -1
+    for fn in (L.lib.lcd_kv_save, L.lib.lcd_kv_load):
+        assert fn(None, 0, fake, fake, None, None, None, None, ctypes.byref(st), None) == 1  # LCD_EINVAL
+    assert L.LayerState.reserved.offset == 20 and ctypes.sizeof(L.LayerState) == 24
