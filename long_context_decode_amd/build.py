@@ -74,7 +74,7 @@ def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--jobs", type=int, default=None)
     ap.add_argument("--verbose", action="store_true")
-    ap.add_argument("-D", dest="defines", action="append", default=[], help="extra macro, e.g. -D LCD_NT_KV=1")
+    ap.add_argument("-D", dest="defines", action="append", default=[], help="extra macro for an experimental build, e.g. -D NAME=1")
     ap.add_argument("--out", default=LIB, help="library path (default: the in-tree liblcd.so)")
     a = ap.parse_args(argv)
     print(build(a.jobs, a.verbose, tuple(a.defines), a.out))

@@ -35,34 +35,18 @@ struct bf16_t {
   uint16_t bits;
 };
 
-// K/V rows are streamed once per decode step; their loads are non-temporal so they
-// do not displace the position table in L2 (LCD_NT_KV=0 builds plain loads).
-#ifndef LCD_NT_KV
-#define LCD_NT_KV 1
-#endif
-
-// Keys per lane group per iteration, chosen by measurement on MI355X: the one-pass
-// kernel (G <= 2; two iterations in flight) and the two-pass kernel's K pass
-// (G = 4 and G = 6; two iterations in flight, 2 keys for G = 8).
-#ifndef LCD_U_G2
-#define LCD_U_G2 2
-#endif
-#ifndef LCD_ONEPASS_MAXG
-#define LCD_ONEPASS_MAXG 2  // largest G served by the one-pass kernel
-#endif
-#ifndef LCD_U_OP_BIG
-#define LCD_U_OP_BIG 1  // one-pass keys per lane group per iteration for G > 2
-#endif
-#ifndef LCD_H2O_EU
-#define LCD_H2O_EU 16  // token-level H2O epilogue: slots per thread per iteration
-#endif
-#ifndef LCD_H2O_EU_BLK
-#define LCD_H2O_EU_BLK 8  // the same for block-level eviction
-#endif
-#ifndef LCD_MERGE_SU
-#define LCD_MERGE_SU 4  // split merge: splits whose loads are issued together
-#endif
-
+// Constants chosen by measurement on MI355X.
+// Keys per lane group per iteration: the one-pass kernel for G <= 2 (two iterations in
+// flight) and for larger G; the two-pass kernel's K pass sets its own (see its Geo).
+constexpr int kUnrollG2 = 2;
+constexpr int kUnrollOnepassBig = 1;
+constexpr int kOnepassMaxG = 2;  // largest G served by the one-pass kernel
+// H2O epilogue: slots per thread per iteration (token-level, block-level eviction).  More
+// would keep more registers live in the merging workgroup than the main loop needs, and
+// the kernel's register count (its occupancy) is the larger of the two.
+constexpr int kH2oEu = 16;
+constexpr int kH2oEuBlk = 8;
+constexpr int kMergeSu = 4;  // split merge: splits whose loads are issued together
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -74,23 +58,17 @@ struct Words {
   uint32_t w[W];
 };
 
+// K/V rows are streamed once per decode step; their loads are non-temporal so they do
+// not displace the position table in L2.
 template <int W>
 __device__ inline Words<W> load_words(const void* p) {
   Words<W> r;
   if constexpr (W == 4) {
-#if LCD_NT_KV
     const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-#else
-    const u32x4 v = *reinterpret_cast<const u32x4*>(p);
-#endif
     r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
   } else {
     static_assert(W == 2, "row pieces are 8 or 16 bytes");
-#if LCD_NT_KV
     const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
-#else
-    const u32x2 v = *reinterpret_cast<const u32x2*>(p);
-#endif
     r.w[0] = v.x; r.w[1] = v.y;
   }
   return r;
@@ -271,7 +249,7 @@ struct Geo {
   static constexpr int LPK = D / EPL;         // lanes per key
   static constexpr int KPW = 64 / LPK;        // keys per wave per sub-step
   static constexpr int KPI = 4 * KPW;         // keys per workgroup per sub-step
-  static constexpr int U = G <= 2 ? LCD_U_G2 : LCD_U_OP_BIG;
+  static constexpr int U = G <= 2 ? kUnrollG2 : kUnrollOnepassBig;
   static constexpr int STEP = KPI * U;        // keys per workgroup per iteration
   static_assert(LPK >= 1 && LPK <= 64 && (64 % LPK) == 0, "lane mapping");
 };
@@ -529,7 +507,7 @@ __device__ inline void split_finish(const DecodeParams& p, float* ored, const fl
     }
     __syncthreads();
     constexpr int EPT = (G * D + kDecodeThreads - 1) / kDecodeThreads;  // output elements per thread
-    constexpr int SU = LCD_MERGE_SU;
+    constexpr int SU = kMergeSu;
     float acc[EPT];
 #pragma unroll
     for (int k = 0; k < EPT; ++k) acc[k] = 0.f;
@@ -587,7 +565,7 @@ __device__ inline void split_finish(const DecodeParams& p, float* ored, const fl
     const int emp_end = p.h2o_step && p.new_block ? nslot + p.bs : -1;
     Victim best;
     const int bs = BLOCKS ? p.bs : 1;  // eviction granule
-    constexpr int EU = BLOCKS ? LCD_H2O_EU_BLK : LCD_H2O_EU;  // slots per thread per iteration, all loads issued first
+    constexpr int EU = BLOCKS ? kH2oEuBlk : kH2oEu;  // slots per thread per iteration, all loads issued first
     for (int base = threadIdx.x - lane; base < p.n; base += kDecodeThreads * EU) {
       const int i0 = base + lane;
       float x[EU][G], sc[EU];
@@ -1509,7 +1487,7 @@ static hipError_t launch_tdg(int mode, const DecodeParams& p, hipStream_t s) {
   const int items = p.duo ? p.ret_splits * p.B * p.Hret + p.str_splits * p.B * p.Hstr
                          : p.n_splits * p.B * p.Hkv;
   const dim3 grid(((items + 7) / 8) * 8), block(kDecodeThreads);
-  if constexpr (G <= LCD_ONEPASS_MAXG) {
+  if constexpr (G <= kOnepassMaxG) {
     const size_t lds = onepass_lds_bytes<D, G>();
     switch (mode) {
       case kModeRope: hipLaunchKernelGGL((decode_onepass_kernel<T, D, G, kModeRope>), grid, block, lds, s, p); break;
@@ -1562,7 +1540,7 @@ static hipError_t launch_t(int D, int G, int mode, const DecodeParams& p, hipStr
 }
 
 int decode_chunk_cap(int G) {
-  if (G <= LCD_ONEPASS_MAXG) return 1 << 24;  // the one-pass kernel keeps no per-slot state in LDS
+  if (G <= kOnepassMaxG) return 1 << 24;  // the one-pass kernel keeps no per-slot state in LDS
   // two-pass: chunk * G logits + the reduction and (max, sum) floats within 64 KiB, 256
   // bytes kept for the static shared variables
   return (16384 - 64 - kTwopassRed - 2 * G) / G / 64 * 64;

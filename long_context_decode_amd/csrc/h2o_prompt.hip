@@ -37,15 +37,9 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-#ifndef LCD_H2OP_TW
-#define LCD_H2OP_TW 2  // register tiles per wave at D <= 128
-#endif
-#ifndef LCD_H2OP_SPLITLOOP
-#define LCD_H2OP_SPLITLOOP 1  // loop split: unconditional prefetches while both blocks exist
-#endif
-#ifndef LCD_H2OP_BT
-#define LCD_H2OP_BT 2  // 32-row tiles per staged block at D <= 128
-#endif
+// Tile shapes at D <= 128, chosen by measurement on MI355X.
+constexpr int kWaveTiles = 2;   // register tiles per wave
+constexpr int kBlockTiles = 2;  // 32-row tiles per staged block
 
 constexpr int kThreads = 256;
 constexpr int kTopkThreads = 1024;
@@ -89,7 +83,7 @@ __device__ inline int c_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >
 // wave (D <= 128) every iteration gives each wave 32 MFMAs (16 at D = 256, each twice as
 // long), enough to cover the global loads issued two iterations ahead.
 template <int D>
-constexpr int block_tiles() { return D == 256 ? 2 : LCD_H2OP_BT; }
+constexpr int block_tiles() { return D == 256 ? 2 : kBlockTiles; }
 template <int D>
 constexpr int block_rows() { return 32 * block_tiles<D>(); }
 template <int D>
@@ -138,7 +132,7 @@ __device__ inline void block_store(char* lds, const uint4 (&r)[block_pieces_per_
 // Row (pass 1) or key (pass 2) tiles a wave keeps in registers: every fragment read from
 // LDS then feeds that many MFMAs, which keeps the LDS reads below the MFMA rate.
 template <int D>
-constexpr int wave_tiles() { return D == 256 ? 1 : LCD_H2OP_TW; }
+constexpr int wave_tiles() { return D == 256 ? 1 : kWaveTiles; }
 
 // ------------------------------------------------------------------ 1. row statistics
 // Workgroup: 4 * 32 * TW prompt rows of one query head (Q fragments in registers).
@@ -252,12 +246,11 @@ __global__ void __launch_bounds__(kThreads, 2) h2o_rowstats_kernel(H2oPromptPara
   if (n_blocks > 1) block_load<D>(K, BR, p.N, rawB);
   block_store<D>(kblk[0], rawA);
   int kb = 0;
-#if LCD_H2OP_SPLITLOOP
-  for (; kb + 3 < n_blocks; kb += 2) {  // both steps prefetch a block that exists
+  // loop split: while both steps prefetch a block that exists, the prefetches are unconditional
+  for (; kb + 3 < n_blocks; kb += 2) {
     step(std::true_type{}, kb, rawA, rawB);
     step(std::true_type{}, kb + 1, rawB, rawA);
   }
-#endif
   for (; kb < n_blocks; kb += 2) {
     step(std::false_type{}, kb, rawA, rawB);
     if (kb + 1 >= n_blocks) break;
@@ -406,12 +399,11 @@ __global__ void __launch_bounds__(kThreads, 2) h2o_colsum_kernel(H2oPromptParams
   if (units > 1) load_unit(1, rawB, sB);
   store_unit(0, rawA, sA);
   int u = 0;
-#if LCD_H2OP_SPLITLOOP
-  for (; u + 3 < units; u += 2) {  // both steps prefetch a unit that exists
+  // loop split: while both steps prefetch a unit that exists, the prefetches are unconditional
+  for (; u + 3 < units; u += 2) {
     step(std::true_type{}, u, rawA, sA, rawB, sB);
     step(std::true_type{}, u + 1, rawB, sB, rawA, sA);
   }
-#endif
   for (; u < units; u += 2) {
     step(std::false_type{}, u, rawA, sA, rawB, sB);
     if (u + 1 >= units) break;

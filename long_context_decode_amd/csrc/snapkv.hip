@@ -25,18 +25,6 @@
 
 #include "lcd_internal.h"
 
-// Memory-access knobs, chosen by measurement on MI355X: pieces per thread of the gather
-// kernel and the load / store kinds of the gather and row-statistics passes.
-#ifndef LCD_GATHER_U
-#define LCD_GATHER_U 1
-#endif
-#ifndef LCD_GATHER_NT_LOAD
-#define LCD_GATHER_NT_LOAD 0
-#endif
-#ifndef LCD_GATHER_NT_STORE
-#define LCD_GATHER_NT_STORE 0
-#endif
-
 namespace lcd {
 
 namespace {
@@ -45,10 +33,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-#ifndef LCD_SNAPKV_WAVE_BLOCKS
-#define LCD_SNAPKV_WAVE_BLOCKS 4
-#endif
-constexpr int kWaveBlocks = LCD_SNAPKV_WAVE_BLOCKS;  // 32-key blocks per wave in the scoring kernels
+constexpr int kWaveBlocks = 4;  // 32-key blocks per wave in the scoring kernels (by measurement)
 constexpr int kTileKeys = 4 * kWaveBlocks * 32;  // keys per scoring workgroup
 
 constexpr int kSelectThreads = 1024;
@@ -666,8 +651,9 @@ __global__ void __launch_bounds__(kSelectThreads) snapkv_select_kernel(SnapkvPar
 
 // ---------------------------------------------------------------------------- 4. gather
 // Row copies of the kept K and V rows as 16-byte pieces: each thread moves kGatherU
-// pieces of K and of V per iteration, all loads issued before the stores.
-constexpr int kGatherU = LCD_GATHER_U;
+// pieces of K and of V per iteration, all loads issued before the stores (plain loads
+// and stores: non-temporal ones measured no faster on MI355X).
+constexpr int kGatherU = 1;
 __global__ void __launch_bounds__(256) snapkv_gather_kernel(SnapkvParams p, int rows) {
   const int h = blockIdx.y, b = blockIdx.z;
   const size_t bh = (size_t)b * p.H + h;
@@ -685,13 +671,8 @@ __global__ void __launch_bounds__(256) snapkv_gather_kernel(SnapkvParams p, int 
       const int e = e0 + u * 256;
       if (e < total) {
         const size_t src = (size_t)idx[e / chunks] * p.D * 2 + (size_t)(e % chunks) * 16;
-#if LCD_GATHER_NT_LOAD
-        kr[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k + src));
-        vr[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v + src));
-#else
         kr[u] = *reinterpret_cast<const u32x4*>(k + src);
         vr[u] = *reinterpret_cast<const u32x4*>(v + src);
-#endif
       }
     }
 #pragma unroll
@@ -699,13 +680,8 @@ __global__ void __launch_bounds__(256) snapkv_gather_kernel(SnapkvParams p, int 
       const int e = e0 + u * 256;
       if (e < total) {
         const size_t dst = (size_t)(e / chunks) * p.D * 2 + (size_t)(e % chunks) * 16;
-#if LCD_GATHER_NT_STORE
-        __builtin_nontemporal_store(kr[u], reinterpret_cast<u32x4*>(ko + dst));
-        __builtin_nontemporal_store(vr[u], reinterpret_cast<u32x4*>(vo + dst));
-#else
         *reinterpret_cast<u32x4*>(ko + dst) = kr[u];
         *reinterpret_cast<u32x4*>(vo + dst) = vr[u];
-#endif
       }
     }
   }
