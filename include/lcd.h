@@ -87,8 +87,8 @@ typedef enum lcd_dtype { LCD_F32 = 0, LCD_BF16 = 1 } lcd_dtype;
 typedef enum lcd_policy { LCD_SINK_RING = 0, LCD_APPEND = 1, LCD_H2O = 2, LCD_DUO = 3 } lcd_policy;
 
 typedef struct lcd_cache_config {
-  int32_t batch;       /* B >= 1 (all rows advance in lockstep)                   */
-  int32_t n_layers;    /* L >= 1 cached attention layers                           */
+  int32_t batch;       /* B >= 1 (all rows advance in lockstep); B * H_q <= 2^24  */
+  int32_t n_layers;    /* 1 <= L <= 65536 cached attention layers                  */
   int32_t n_q_heads;   /* H_q, a multiple of n_kv_heads; H_q / H_kv <= 8           */
   int32_t n_kv_heads;  /* H_kv >= 1; query head h reads KV head h / (H_q / H_kv)  */
   int32_t head_dim;    /* D in {64, 128, 256}                                      */

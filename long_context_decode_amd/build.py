@@ -23,7 +23,7 @@ LIB = os.path.join(PKG, "liblcd.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["lcd_host.cpp", "kv.hip", "decode.hip", "snapkv.hip", "h2o_prompt.hip"]
+SOURCES = ["lcd_host.cpp", "scratch.hip", "kv.hip", "decode.hip", "snapkv.hip", "h2o_prompt.hip"]
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

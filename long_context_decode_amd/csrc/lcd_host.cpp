@@ -48,8 +48,6 @@ uint64_t align256(uint64_t x) { return (x + 255u) & ~uint64_t(255); }
 bool mul_ok(uint64_t* acc, uint64_t f) { return !__builtin_mul_overflow(*acc, f, acc); }
 
 constexpr int64_t kMaxSlots = int64_t(1) << 24;
-// Device scratch of lcd_decode_step_noalloc (split partials): 32 MiB per GPU.
-constexpr uint64_t kScratchBytes = uint64_t(32) << 20;
 
 struct Layout {
   int C = 0, esize = 0, G = 0;
@@ -72,6 +70,10 @@ lcd_status check_config(const lcd_cache_config* c, Layout* L) {
   if (!c) return fail(LCD_EINVAL, "config is NULL");
   if (c->batch < 1 || c->n_layers < 1 || c->n_kv_heads < 1 || c->n_q_heads < 1)
     return fail(LCD_ESHAPE, "batch, n_layers, n_q_heads and n_kv_heads must be >= 1");
+  // bounds that keep every row-head count, grid size and index product of the launch
+  // planning inside 32-bit integers
+  if ((int64_t)c->batch * c->n_q_heads > (int64_t(1) << 24) || c->n_layers > 65536)
+    return fail(LCD_ESHAPE, "need batch * n_q_heads <= 2^24 and n_layers <= 65536");
   if (c->n_q_heads % c->n_kv_heads)
     return fail(LCD_ESHAPE, "n_q_heads (%d) must be a multiple of n_kv_heads (%d)", c->n_q_heads, c->n_kv_heads);
   const int G = c->n_q_heads / c->n_kv_heads;
@@ -640,34 +642,12 @@ lcd_status decode_step_impl(lcd_cache* c, int32_t layer, const void* k, const vo
 }
 
 // ---------------------------------------------------------------- device scratch
-// The split partials of lcd_decode_step_noalloc live in this file-scope device array
-// (one copy per GPU, held until the process ends).  Host code never passes the array's
-// name to a kernel: its device address is resolved once per device with
-// hipGetSymbolAddress (with that device current) and cached here.
-constexpr int kMaxDevices = 64;
-std::mutex g_scratch_mu;
-void* g_scratch_ptr[kMaxDevices] = {};
-
-}  // namespace
-
-static __device__ __align__(256) char scratch[kScratchBytes];
-
-namespace {
-
+// The split partials of lcd_decode_step_noalloc live in a file-scope device array of
+// scratch.hip (one copy per GPU); its device address comes from there.
 lcd_status scratch_address(void** out) {
-  int dev = -1;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  if (dev < 0 || dev >= kMaxDevices) return fail(LCD_EUNSUPPORTED, "device %d beyond the scratch table", dev);
-  std::lock_guard<std::mutex> lock(g_scratch_mu);
-  if (!g_scratch_ptr[dev]) {
-    void* p = nullptr;
-    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
-    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
-    if (!p || (reinterpret_cast<uintptr_t>(p) & 255u)) return fail(LCD_EHIP, "scratch address not 256-byte aligned");
-    g_scratch_ptr[dev] = p;
-  }
-  *out = g_scratch_ptr[dev];
+  const hipError_t e = lcd::scratch_device_address(out);
+  if (e == hipErrorInvalidDevice) return fail(LCD_EUNSUPPORTED, "current device beyond the scratch table");
+  if (e != hipSuccess) return hip_fail(e, "device scratch address");
   return LCD_OK;
 }
 
@@ -693,13 +673,13 @@ lcd_status lcd_decode_step_noalloc(lcd_cache* c, int32_t layer, const void* k, c
                                    float* out, void* stream) {
   lcd_status st = check_layer(c, layer);
   if (st) return st;
-  if (c->L.ws_bytes > kScratchBytes)
+  if (c->L.ws_bytes > lcd::kScratchBytes)
     return fail(LCD_ESIZE, "decode_step_noalloc: this cache needs %llu workspace bytes, above the %llu-byte "
                 "device scratch buffer (use lcd_decode_step with a caller workspace)",
-                (unsigned long long)c->L.ws_bytes, (unsigned long long)kScratchBytes);
+                (unsigned long long)c->L.ws_bytes, (unsigned long long)lcd::kScratchBytes);
   void* ws = nullptr;
   if ((st = scratch_address(&ws))) return st;
-  return decode_step_impl(c, layer, k, v, q, out, ws, kScratchBytes, stream);
+  return decode_step_impl(c, layer, k, v, q, out, ws, lcd::kScratchBytes, stream);
 }
 
 int64_t lcd_kv_tokens(const lcd_cache* c, int32_t layer) {

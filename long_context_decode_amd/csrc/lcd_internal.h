@@ -111,6 +111,14 @@ hipError_t launch_rope_table(float* cos_t, float* sin_t, int C, int D, double ba
 hipError_t launch_fill_i32(int* p, int value, int64_t n, hipStream_t s);
 hipError_t launch_fill_f32(float* p, float value, int64_t n, hipStream_t s);
 
+// Device scratch of lcd_decode_step_noalloc (split partials): a file-scope array of
+// kScratchBytes per GPU (scratch.hip).  scratch_device_address gives its address on the
+// current device, resolved once per device with that device current:
+// hipErrorInvalidDevice for a device id beyond the library's table, hipErrorInvalidValue
+// if the address is not 256-byte aligned, otherwise the runtime's error.
+constexpr uint64_t kScratchBytes = uint64_t(32) << 20;
+hipError_t scratch_device_address(void** out);
+
 bool decode_supported(int dtype, int D, int G);
 // Most slots one decode workgroup may own for G query heads per KV head (a multiple of 64).
 int decode_chunk_cap(int G);
