@@ -218,3 +218,38 @@ def test_decode_is_deterministic(L):
         cache.decode(0, q, out)
         outs.append(out.cpu())
     assert torch.equal(outs[0], outs[1])
+
+
+def test_gqa_long_full_size_bit_identical_reruns(L):
+    """The full-size split merge is deterministic: one layer of the B=16, 24/4 heads,
+    D=256, 4 + 32764 cache (the decode plan's full split count), decoded by two caches
+    filled with the same tokens -- once with lcd_decode_attn after an append, once with
+    the fused lcd_decode_step -- and re-decoded three times with different workspace
+    buffers, gives bit-identical outputs every time."""
+    w = scaled(WORKLOADS["gqa_long"], n_layers=1)
+    dev = "cuda"
+    pre = w.prefill
+    print(f"[gqa_long determinism] one layer of {w.title}", flush=True)
+    k = w.token_block_torch("k", 0, 0, pre, dev)
+    v = w.token_block_torch("v", 0, 0, pre, dev)
+    a, b = L.KVCache(_cfg(L, w)), L.KVCache(_cfg(L, w))
+    a.append(0, k, v)
+    b.append(0, k, v)
+    del k, v
+    q = w.token_major_torch("q", 0, pre, pre + 1, dev)[0]
+    kn = w.token_major_torch("k", 0, pre, pre + 1, dev)[0]
+    vn = w.token_major_torch("v", 0, pre, pre + 1, dev)[0]
+    outs = []
+    a.append(0, kn.unsqueeze(2), vn.unsqueeze(2))
+    for i in range(3):
+        ws = torch.empty(a.ws_bytes, dtype=torch.uint8, device=dev)  # a fresh workspace each time
+        out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+        L.decode_attn(a.handle, 0, q, out, ws, a.ws_bytes)
+        outs.append(out)
+    ob = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    b.step(0, kn, vn, q, ob)
+    outs.append(ob)
+    torch.cuda.synchronize()
+    for i, o in enumerate(outs[1:], 1):
+        assert torch.equal(outs[0].view(torch.int32), o.view(torch.int32)), f"run {i} differs"
+    assert torch.isfinite(outs[0]).all()
