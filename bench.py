@@ -43,7 +43,8 @@ def _parse(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None, help="timed steps of the headline workload")
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default=HEADLINE, choices=sorted(DEFAULTS))
+    ap.add_argument("--workload", default=HEADLINE, choices=sorted(DEFAULTS) + ["snapkv_32k"],
+                    help="decode workload to time (snapkv_32k: only with --counters)")
     ap.add_argument("--only", action="store_true", help="skip the secondary workloads and SnapKV")
     ap.add_argument("--no-snapkv", action="store_true", help="skip the SnapKV compression timing")
     ap.add_argument("--no-h2o-prompt", action="store_true", help="skip the H2O prompt-phase compression timing")
@@ -56,6 +57,10 @@ def _parse(argv=None):
                     help="time the SnapKV compression alone and print its record (for profiling)")
     ap.add_argument("--l-obs", type=int, default=None,
                     help="with --snapkv-only: observation window of the 32k compression (default 32)")
+    ap.add_argument("--mfma-counters", nargs="+", metavar="LOBS=CSV",
+                    help="summarise rocprofv3 --pmc runs of 'bench.py --snapkv-only --l-obs LOBS' (MFMA and "
+                         "activity counters, one CSV per observation window) into the SnapKV MFMA record "
+                         "and exit (no GPU)")
     ap.add_argument("--counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of 'bench.py --only "
                          "--copy-calibration --workload NAME' into the traffic record of NAME and exit (no GPU)")
@@ -170,6 +175,119 @@ def _counter_summary(fetch_csv, write_csv, workload):
         fh.write("\n".join(lines))
     print(f"traffic {traffic:.0f} B per launch -> {out}")
     return traffic
+
+
+SNAPKV_FILTER = "snapkv_|copyBuffer"
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
+N_SIMD = 1024  # 256 CUs x 4 SIMDs
+N_XCD = 8
+
+
+def _snapkv_alg_bytes(w):
+    B, H, D, N, Lo, K = w.batch, w.n_q_heads, w.head_dim, w.n_prompt, w.l_obs, w.k_keep
+    return B * H * N * D * 2 + 2 * 2 * B * H * (K + Lo) * D * 2 + B * H * Lo * D * 2 + B * H * (K + Lo) * 4
+
+
+def _snapkv_counter_summary(fetch_csv, write_csv):
+    """FETCH_SIZE / WRITE_SIZE of the SnapKV kernels (mean per dispatch of each, summed over
+    one compress), scaled by the calibration copy; writes the SnapKV traffic record."""
+    import statistics
+    from synth import WORKLOADS
+
+    w = WORKLOADS["snapkv_32k"]
+    per = {}
+    scale = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = _read_counter_csv(path, counter)
+        copies = [rows[d][2] for d in sorted(rows) if "copyBuffer" in rows[d][0]][:3]
+        if len(copies) < 3 or max(copies) > 1.05 * min(copies):
+            raise SystemExit(f"{path}: no consistent calibration copy (run the bench with --copy-calibration)")
+        scale[counter] = COPY_BYTES / (statistics.median(copies) * 1024.0)
+        kern = {}
+        for (n, g, v) in rows.values():
+            if "snapkv_" in n:
+                kern.setdefault(n, []).append(v)
+        for n, vals in kern.items():
+            per.setdefault(n, {})[counter] = (statistics.mean(vals) * 1024.0 * scale[counter], len(vals))
+    total = sum(c.get("FETCH_SIZE", (0, 0))[0] + c.get("WRITE_SIZE", (0, 0))[0] for c in per.values())
+    alg = _snapkv_alg_bytes(w)
+    run = "python3 bench.py --snapkv-only --copy-calibration"
+    lines = [f"# SnapKV compression kernels, HBM traffic — {w.title}", "",
+             "Two rocprofv3 counter runs of the same command, one counter each, counters collected on the "
+             "SnapKV kernels and the calibration copies only:", "", "```",
+             "cd /tmp && export TMPDIR=/tmp && cd $REPO",
+             f"rocprofv3 --pmc FETCH_SIZE --kernel-include-regex '{SNAPKV_FILTER}' --output-format csv "
+             f"-d {os.path.dirname(fetch_csv)} -o run -- {run}",
+             f"rocprofv3 --pmc WRITE_SIZE --kernel-include-regex '{SNAPKV_FILTER}' --output-format csv "
+             f"-d {os.path.dirname(write_csv)} -o run -- {run}",
+             f"python3 bench.py --counters {fetch_csv} {write_csv} --workload snapkv_32k", "```", "",
+             f"Scales from the 1 GiB calibration copy: FETCH_SIZE x{scale['FETCH_SIZE']:.4f}, "
+             f"WRITE_SIZE x{scale['WRITE_SIZE']:.4f}.", "",
+             "| kernel | dispatches | read bytes (mean per dispatch) | written bytes (mean per dispatch) |",
+             "|---|---:|---:|---:|"]
+    for n in sorted(per, key=lambda n: -per[n].get("FETCH_SIZE", (0, 0))[0]):
+        f_, w_ = per[n].get("FETCH_SIZE", (0, 0)), per[n].get("WRITE_SIZE", (0, 0))
+        lines.append(f"| `{n}` | {f_[1]} | {f_[0]:.0f} | {w_[0]:.0f} |")
+    lines += ["", f"Per compress (one dispatch of each kernel): {total:.0f} B against {alg} algorithmic bytes "
+              f"(K read once, the kept K / V rows read and written, q and indices): {total / alg:.3f}x.",
+              f"traffic-bytes-per-compress: {total:.0f}", ""]
+    out = os.path.join(PROFILES, "snapkv_kernels_32k_traffic.md")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines))
+    print(f"traffic {total:.0f} B per compress ({total / alg:.3f}x) -> {out}")
+    return total
+
+
+def _mfma_summary(entries):
+    """MFMA counters of the two SnapKV scoring kernels over observation windows: per pass,
+    flops (MOPS_BF16 x 512), the MFMA pipes' busy fraction (busy cycles over every SIMD's
+    cycles) and the ceiling min(1, L_obs / 312) that K's bytes impose at 8 TB/s."""
+    import csv
+    import statistics
+
+    lines = ["# SnapKV scoring kernels — MFMA counters over the observation window", "",
+             "One rocprofv3 counter run per observation window L_obs (32-key prompt N=32768, 32 heads, "
+             "D=128, bf16), counters on the SnapKV kernels only:", "", "```",
+             "cd /tmp && export TMPDIR=/tmp && cd $REPO"]
+    table = []
+    for e in entries:
+        lo, path = e.split("=", 1)
+        lo = int(lo)
+        lines.append(f"rocprofv3 --pmc {' '.join(MFMA_COUNTERS)} --kernel-include-regex 'snapkv_' "
+                     f"--output-format csv -d {os.path.dirname(path)} -o run -- "
+                     f"python3 bench.py --snapkv-only --l-obs {lo}")
+        vals = {}
+        with open(path, newline="") as f:
+            for row in csv.DictReader(f):
+                n = row["Kernel_Name"]
+                kind = "rowstats" if "rowstats" in n else "colscore" if "colscore" in n else None
+                if kind is None:
+                    continue
+                key = (kind, int(row["Dispatch_Id"]))
+                vals.setdefault(key, {}).setdefault(row["Counter_Name"], 0.0)
+                vals[key][row["Counter_Name"]] += float(row["Counter_Value"])
+        for kind in ("rowstats", "colscore"):
+            ds = [v for (k, _), v in vals.items() if k == kind and all(c in v for c in MFMA_COUNTERS)]
+            if not ds:
+                raise SystemExit(f"{path}: no complete {kind} dispatch")
+            mops = statistics.mean(d["SQ_INSTS_VALU_MFMA_MOPS_BF16"] for d in ds)
+            busy = statistics.mean(d["SQ_VALU_MFMA_BUSY_CYCLES"] for d in ds)
+            gui = statistics.mean(d["GRBM_GUI_ACTIVE"] for d in ds)
+            frac = busy / (N_SIMD * gui / N_XCD)
+            table.append((lo, kind, len(ds), mops * 512, gui / N_XCD, frac, min(1.0, lo / 312.0)))
+    lines += [f"python3 bench.py --mfma-counters {' '.join(entries)}", "```", "",
+              "| L_obs | pass | dispatches | flops per dispatch | cycles (per XCD) | MFMA busy | ceiling min(1, L_obs/312) | busy / ceiling |",
+              "|---:|---|---:|---:|---:|---:|---:|---:|"]
+    for lo, kind, n, fl, cyc, frac, ceil in table:
+        lines.append(f"| {lo} | {kind} | {n} | {fl:.4g} | {cyc:.0f} | {frac:.4f} | {ceil:.3f} | {frac / ceil:.3f} |")
+    lines += ["", "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs); a "
+              "32x32x16 bf16 MFMA keeps its pipe busy 32 cycles for 32768 flops, so a busy fraction f "
+              "is f x 2.5 PFLOP/s.  The ceiling: each pass reads K once, L_obs flop per byte, so at 8 TB/s "
+              "it can use at most 8 L_obs TFLOP/s of the 2500.", ""]
+    out = os.path.join(PROFILES, "snapkv_mfma_lobs_sweep.md")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines))
+    print(f"-> {out}")
 
 
 def _traffic(workload):
@@ -595,8 +713,17 @@ def _cpu_baselines(headline, budget_s):
 def main(argv=None):
     a = _parse(argv)
     if a.counters:
-        _counter_summary(*a.counters, workload=a.workload)
+        if a.workload == "snapkv_32k":
+            _snapkv_counter_summary(*a.counters)
+        else:
+            _counter_summary(*a.counters, workload=a.workload)
         return 0
+    if a.mfma_counters:
+        _mfma_summary(a.mfma_counters)
+        return 0
+    if a.workload not in DEFAULTS:
+        print(json.dumps({"error": f"{a.workload} is not a decode workload (use --snapkv-only)"}))
+        return 2
     if a.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only (one MI355X per box here); "
                                    "--gpus must be 1", "n_gpus_requested": a.gpus}))
@@ -614,6 +741,8 @@ def main(argv=None):
     if a.snapkv_only:
         from synth.workloads import scaled
 
+        if a.copy_calibration:
+            _copy_calibration()
         sk = WORKLOADS["snapkv_32k"]
         if a.l_obs:
             sk = scaled(sk, name=f"snapkv_32k_obs{a.l_obs}", l_obs=a.l_obs,

@@ -59,6 +59,41 @@ def test_counter_summary_needs_the_calibration_copy(tmp_path, monkeypatch):
         bench._counter_summary(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), "gqa_long")
 
 
+def test_snapkv_counter_summary_sums_the_kernels(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    copy = "__amd_rocclr_copyBuffer"
+    gib_kib = (1 << 30) / 1024
+    rs = "void lcd::(anonymous namespace)::snapkv_rowstats_kernel<128, 1>(lcd::SnapkvParams)"
+    ga = "lcd::(anonymous namespace)::snapkv_gather_kernel(lcd::SnapkvParams, int)"
+    _csv(tmp_path / "f.csv", "FETCH_SIZE", [(copy, gib_kib / 2)] * 3 + [(rs, 100.0), (rs, 300.0), (ga, 50.0)])
+    _csv(tmp_path / "w.csv", "WRITE_SIZE", [(copy, gib_kib)] * 3 + [(rs, 1.0), (rs, 1.0), (ga, 40.0)])
+    total = bench._snapkv_counter_summary(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"))
+    # per compress: the mean dispatch of each kernel, fetch scaled x2, write x1
+    assert total == pytest.approx((200.0 + 50.0) * 1024 * 2 + (1.0 + 40.0) * 1024)
+    text = (tmp_path / "snapkv_kernels_32k_traffic.md").read_text()
+    assert "traffic-bytes-per-compress" in text and "snapkv_rowstats_kernel" in text
+
+
+def test_mfma_summary_busy_fraction(tmp_path, monkeypatch):
+    """busy / (1024 SIMDs x GRBM cycles / 8 XCDs), per scoring pass and window."""
+    import csv
+
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    path = tmp_path / "m.csv"
+    with open(path, "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        wr.writeheader()
+        for d, name in ((1, "snapkv_rowstats_kernel<128, 4>"), (2, "snapkv_colscore_kernel<128, 4>")):
+            for c, v in (("SQ_INSTS_VALU_MFMA_MOPS_BF16", 1000.0), ("SQ_VALU_MFMA_BUSY_CYCLES", 1024 * 500.0),
+                         ("SQ_BUSY_CYCLES", 1.0), ("GRBM_GUI_ACTIVE", 8 * 1000.0)):
+                wr.writerow(dict(Dispatch_Id=d, Kernel_Name=name, Counter_Name=c, Counter_Value=v))
+    bench._mfma_summary([f"128={path}"])
+    text = (tmp_path / "snapkv_mfma_lobs_sweep.md").read_text()
+    rows = [line for line in text.splitlines() if line.startswith("| 128 |")]
+    assert len(rows) == 2 and all("| 0.5000 |" in r for r in rows)  # 500 busy of 1000 cycles
+    assert all("| 0.410 |" in r for r in rows)  # ceiling 128 / 312
+
+
 def test_oracle_workers_time_their_share():
     """The baseline workers run the oracle on disjoint shares and stop at their budget."""
     done0, el0 = bench._worker_streaming(("tiny_streaming", 0, 2, 100, 3, 10.0))
