@@ -291,6 +291,15 @@ __global__ void __launch_bounds__(256) snapkv_colscore_kernel(SnapkvParams p) {
             b = gridDim.z - 1 - blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const size_t bh = (size_t)b * p.H + h;
+  const uint16_t* q = reinterpret_cast<const uint16_t*>(p.q_obs) + bh * p.Lobs * D;
+  const uint16_t* k = reinterpret_cast<const uint16_t*>(p.k) + bh * (size_t)p.N * D;
+  const int Np = p.N - p.Lobs;  // prefix keys: visible to every observation row
+  const float inv_rows = 1.f / (float)p.Lobs;
+  const int wkey0 = tile * kTileKeys + wave * kWaveBlocks * 32;
+  // the wave's first K chunk is requested before the statistics merge below, so that its
+  // latency overlaps the merge's loads (keys past the prefix load nothing)
+  u32x4 raw[chunk_pieces<D>()];
+  chunk_load<D, true>(k, Np, wkey0, 0, lane, raw);
   // the rows' (M_t, 1/L_t) from the row-statistics partials of every tile of the head:
   // thread = (row t, part); each part merges every PARTS-th tile, 8 tiles' loads issued
   // together, then the parts are merged through LDS
@@ -332,11 +341,6 @@ __global__ void __launch_bounds__(256) snapkv_colscore_kernel(SnapkvParams p) {
       sI[threadIdx.x] = real ? 1.f / ll : 0.f;
     }
   }
-  const uint16_t* q = reinterpret_cast<const uint16_t*>(p.q_obs) + bh * p.Lobs * D;
-  const uint16_t* k = reinterpret_cast<const uint16_t*>(p.k) + bh * (size_t)p.N * D;
-  const int Np = p.N - p.Lobs;  // prefix keys: visible to every observation row
-  const float inv_rows = 1.f / (float)p.Lobs;
-  const int wkey0 = tile * kTileKeys + wave * kWaveBlocks * 32;
   bf16x8 qf[QR::kRegs ? RB : 1][D / 16];
   if constexpr (QR::kRegs) {
     __syncthreads();  // sM / sI complete
@@ -355,8 +359,6 @@ __global__ void __launch_bounds__(256) snapkv_colscore_kernel(SnapkvParams p) {
   constexpr int NC = D / chunk_w<D>();
   constexpr int FS = chunk_w<D>() / 16;
   static_assert(NC == 1 || RG == RB, "a row of two column chunks keeps every row block's accumulator");
-  u32x4 raw[chunk_pieces<D>()];
-  chunk_load<D, true>(k, Np, wkey0, 0, lane, raw);
   for (int blk = 0; blk < kWaveBlocks; ++blk) {
     const int key0 = wkey0 + blk * 32;
     if (key0 >= Np) break;  // wave-uniform
