@@ -79,6 +79,8 @@ TRAFFIC = {
     "llama3_8b_layer": ("decode_twopass_kernel<lcd::bf16_t, 128, 4, 0>",
                         "decode_twopass_kernel_llama3_b16_c8192_traffic.md"),
     "h2o_128k": ("decode_twopass_kernel<lcd::bf16_t, 128, 4, 2>", "decode_twopass_kernel_h2o4096_b16_traffic.md"),
+    "h2o_blocks_128k": ("decode_twopass_kernel<lcd::bf16_t, 128, 4, 3>",
+                        "decode_twopass_kernel_h2o4096_blocks16_b16_traffic.md"),
     "duo_128k": ("decode_twopass_kernel<lcd::bf16_t, 128, 4, 1>", "decode_twopass_kernel_duo128k_b16_traffic.md"),
 }
 TRAFFIC_SOURCES = ("long_context_decode_amd/csrc/decode.hip", "long_context_decode_amd/csrc/lcd_internal.h",
