@@ -131,6 +131,14 @@ struct QRows {
   static constexpr int kLdsBytes = kRegs ? 16 : RB * 32 * q_row_bytes<D>();
 };
 
+// Chunks of K a scoring wave keeps in flight (two while the window queries fit registers;
+// wider windows keep one so as not to lose occupancy), and the occupancy asked of the
+// compiler for the narrow shapes (three waves per SIMD, which the second set fits into).
+template <int D, int RB>
+constexpr int prefetch_depth() { return QRows<D, RB>::kRegs && D <= 128 ? 2 : 1; }
+template <int D, int RB>
+constexpr int scoring_min_waves() { return RB == 1 && D <= 128 ? 3 : 1; }
+
 template <int D, int RB>
 __device__ inline void stage_q_rows(const uint16_t* q, int Lobs, char* qs) {
   constexpr int PPR = D * 2 / 16;  // 16-byte pieces per row
@@ -151,7 +159,7 @@ __device__ inline bf16x8 q_frag_lds(const char* qs, int rb, int s, int lane) {
 
 // ---------------------------------------------------------------------------- 1. rowstats
 template <int D, int RB>
-__global__ void __launch_bounds__(256) snapkv_rowstats_kernel(SnapkvParams p) {
+__global__ void __launch_bounds__(256, (scoring_min_waves<D, RB>())) snapkv_rowstats_kernel(SnapkvParams p) {
   using QR = QRows<D, RB>;
   constexpr int R = RB * 32, RG = QR::kRG;
   __shared__ float sm[4][R], sl[4][R];
@@ -216,18 +224,22 @@ __global__ void __launch_bounds__(256) snapkv_rowstats_kernel(SnapkvParams p) {
       m[rb] = mn;
     }
   };
-  u32x4 raw[chunk_pieces<D>()];
-  chunk_load<D, true>(k, p.N, wkey0, 0, lane, raw);
+  // the wave's kWaveBlocks * NC chunks in order, PF in flight: chunk i + PF is requested
+  // into the register set that chunk i leaves when it moves to LDS
+  constexpr int T = kWaveBlocks * NC, PF = prefetch_depth<D, RB>();
+  u32x4 raw[PF][chunk_pieces<D>()];
+#pragma unroll
+  for (int i = 0; i < PF && i < T; ++i) chunk_load<D, true>(k, p.N, wkey0 + 32 * (i / NC), i % NC, lane, raw[i]);
+#pragma unroll
   for (int blk = 0; blk < kWaveBlocks; ++blk) {
     const int key0 = wkey0 + blk * 32;
     if (key0 >= p.N) break;  // wave-uniform
     f32x16 acc[RG];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      chunk_store_lds<D>(stage[wave], lane, raw);
-      // prefetch the next chunk (of this block or the next one)
-      if (c + 1 < NC) chunk_load<D, true>(k, p.N, key0, c + 1, lane, raw);
-      else if (blk + 1 < kWaveBlocks) chunk_load<D, true>(k, p.N, key0 + 32, 0, lane, raw);
+      const int i = blk * NC + c;
+      chunk_store_lds<D>(stage[wave], lane, raw[i % PF]);
+      if (i + PF < T) chunk_load<D, true>(k, p.N, wkey0 + 32 * ((i + PF) / NC), (i + PF) % NC, lane, raw[i % PF]);
       wave_lds_order();
       bf16x8 kf[FS];
       chunk_frags_lds<D>(stage[wave], lane, kf);
@@ -279,7 +291,7 @@ __global__ void __launch_bounds__(256) snapkv_rowstats_kernel(SnapkvParams p) {
 
 // ---------------------------------------------------------------------------- 2. colscore
 template <int D, int RB>
-__global__ void __launch_bounds__(256) snapkv_colscore_kernel(SnapkvParams p) {
+__global__ void __launch_bounds__(256, (scoring_min_waves<D, RB>())) snapkv_colscore_kernel(SnapkvParams p) {
   using QR = QRows<D, RB>;
   constexpr int R = RB * 32, RG = QR::kRG;
   __shared__ float sM[R], sI[R];
@@ -298,8 +310,10 @@ __global__ void __launch_bounds__(256) snapkv_colscore_kernel(SnapkvParams p) {
   const int wkey0 = tile * kTileKeys + wave * kWaveBlocks * 32;
   // the wave's first K chunk is requested before the statistics merge below, so that its
   // latency overlaps the merge's loads (keys past the prefix load nothing)
-  u32x4 raw[chunk_pieces<D>()];
-  chunk_load<D, true>(k, Np, wkey0, 0, lane, raw);
+  constexpr int NCK = D / chunk_w<D>(), T = kWaveBlocks * NCK, PF = prefetch_depth<D, RB>();
+  u32x4 raw[PF][chunk_pieces<D>()];
+#pragma unroll
+  for (int i = 0; i < PF && i < T; ++i) chunk_load<D, true>(k, Np, wkey0 + 32 * (i / NCK), i % NCK, lane, raw[i]);
   // the rows' (M_t, 1/L_t) from the row-statistics partials of every tile of the head:
   // thread = (row t, part); each part merges every PARTS-th tile, 8 tiles' loads issued
   // together, then the parts are merged through LDS
@@ -359,6 +373,7 @@ __global__ void __launch_bounds__(256) snapkv_colscore_kernel(SnapkvParams p) {
   constexpr int NC = D / chunk_w<D>();
   constexpr int FS = chunk_w<D>() / 16;
   static_assert(NC == 1 || RG == RB, "a row of two column chunks keeps every row block's accumulator");
+#pragma unroll
   for (int blk = 0; blk < kWaveBlocks; ++blk) {
     const int key0 = wkey0 + blk * 32;
     if (key0 >= Np) break;  // wave-uniform
@@ -366,9 +381,9 @@ __global__ void __launch_bounds__(256) snapkv_colscore_kernel(SnapkvParams p) {
     f32x16 acc[RG];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      chunk_store_lds<D>(stage[wave], lane, raw);
-      if (c + 1 < NC) chunk_load<D, true>(k, Np, key0, c + 1, lane, raw);
-      else if (blk + 1 < kWaveBlocks) chunk_load<D, true>(k, Np, key0 + 32, 0, lane, raw);
+      const int i = blk * NC + c;  // PF chunks in flight, as in the row-statistics pass
+      chunk_store_lds<D>(stage[wave], lane, raw[i % PF]);
+      if (i + PF < T) chunk_load<D, true>(k, Np, wkey0 + 32 * ((i + PF) / NC), (i + PF) % NC, lane, raw[i % PF]);
       wave_lds_order();
       bf16x8 kf[FS];
       chunk_frags_lds<D>(stage[wave], lane, kf);
