@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define LCD_ABI_VERSION 4
+#define LCD_ABI_VERSION 5  /* 5: checkpoint calls (lcd_kv_save, lcd_kv_load, lcd_kv_layer_bytes) */
 
 typedef enum lcd_status {
   LCD_OK = 0,

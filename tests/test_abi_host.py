@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported(L):
     for name in declared:
         assert hasattr(L.lib, name), name
     assert set(declared) == set(L._lib.EXPORTED)
-    assert L.abi_version() == 4
+    assert L.abi_version() == 5
 
 
 def test_sizes_follow_the_kv_size_model(L):
