@@ -128,10 +128,12 @@ def test_cache_calls_stay_in_bounds(L, policy):
         b.check(f"checkpoint {x}")
 
 
-def test_snapkv_stays_in_bounds(L):
-    """The compress writes k_keep + l_obs rows of out_rows and nothing else."""
-    w = scaled(WORKLOADS["snapkv_32k"], name="guard_snapkv", n_q_heads=3, n_kv_heads=3, n_prompt=2000, l_obs=40,
-               k_keep=300)
+@pytest.mark.parametrize("l_obs", [40, 24])
+def test_snapkv_stays_in_bounds(L, l_obs):
+    """The compress writes k_keep + l_obs rows of out_rows and nothing else (a window of 40
+    rows runs two 32-row blocks, one of 24 a single partial block)."""
+    w = scaled(WORKLOADS["snapkv_32k"], name=f"guard_snapkv_{l_obs}", n_q_heads=3, n_kv_heads=3, n_prompt=2000,
+               l_obs=l_obs, k_keep=300)
     B, H, D, N, Lo, K = w.batch, w.n_q_heads, w.head_dim, w.n_prompt, w.l_obs, w.k_keep
     out_rows = K + Lo + 17
     print(f"[guards] snapkv: N={N} l_obs={Lo} keep={K} out_rows={out_rows}", flush=True)

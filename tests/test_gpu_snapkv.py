@@ -104,6 +104,11 @@ BASE = WORKLOADS["snapkv_32k"]
     dict(n_q_heads=2, n_prompt=2100, l_obs=256, k_keep=300),                      # 8 row blocks
     dict(n_q_heads=2, n_prompt=901, l_obs=100, k_keep=100, head_dim=256),         # 4 blocks, two column chunks
     dict(n_q_heads=1, n_prompt=700, l_obs=200, k_keep=50, head_dim=64, kernel_size=7),  # 8 blocks, ragged window
+    # tile edges: one key past two 512-key scoring tiles, one key past a 32-key MFMA block,
+    # and a prompt shorter than one block
+    dict(n_q_heads=2, n_prompt=1025, l_obs=32, k_keep=100),
+    dict(n_q_heads=1, n_prompt=33, l_obs=2, k_keep=10, kernel_size=3),
+    dict(n_q_heads=2, n_prompt=20, l_obs=4, k_keep=8, kernel_size=3),
 ])
 def test_snapkv_small(L, case):
     w = scaled(BASE, name="snapkv_small_" + "_".join(f"{k}{v}" for k, v in case.items()), **case)
@@ -115,6 +120,14 @@ def test_snapkv_small(L, case):
 def test_snapkv_max_pool_and_out_rows(L, ksize):
     w = scaled(BASE, name=f"snapkv_max_k{ksize}", n_q_heads=2, n_prompt=700, l_obs=16, k_keep=64, kernel_size=ksize)
     _run(L, w, pool=1, out_rows=100)
+
+
+def test_snapkv_many_heads(L):
+    """140 heads (2 x 70) of 2048 keys: a grid of many heads, the first and last heads of
+    both batch rows and the heads around the 128th checked."""
+    w = scaled(BASE, name="snapkv_rounds", batch=2, n_q_heads=70, n_prompt=2048, l_obs=32, k_keep=300)
+    print("[snapkv] 140 heads x 2048 keys", flush=True)
+    _run(L, w, check_heads=[(0, 0), (0, 69), (1, 57), (1, 58), (1, 69)])
 
 
 def test_snapkv_full_size(L):
