@@ -46,6 +46,8 @@ constexpr int kOnepassMaxG = 2;  // largest G served by the one-pass kernel
 // the kernel's register count (its occupancy) is the larger of the two.
 constexpr int kH2oEu = 16;
 constexpr int kH2oEuBlk = 8;
+template <bool BLOCKS>
+constexpr int EU_OF() { return BLOCKS ? kH2oEuBlk : kH2oEu; }
 constexpr int kMergeSu = 4;  // split merge: splits whose loads are issued together
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -429,8 +431,10 @@ __device__ inline void write_new_rows(const DecodeParams& p, int b, int g, int s
 // the last workgroup of (b, g) to arrive merges every split (deterministic), reusing ored
 // for per-split weights.  In
 // logits mode the merging workgroup then runs the H2O epilogue, evicting whole blocks of
-// p.bs slots when BLOCKS is set.
-template <int D, int G, bool LOGITS, bool BLOCKS>
+// p.bs slots when BLOCKS is set, from what each split stored per slot and query head: its
+// weight 2^(x - m_s) relative to the split's maximum (WEIGHTS: the two-pass kernel, after its
+// V pass) or the logit x itself (the one-pass kernel, which keeps no weights).
+template <int D, int G, bool LOGITS, bool BLOCKS, bool WEIGHTS>
 __device__ inline void split_finish(const DecodeParams& p, float* ored, const float* Mh, const float* Lh,
                                     int split, int n_splits, int b, int g) {
   const int lane = threadIdx.x & 63;
@@ -556,6 +560,20 @@ __device__ inline void split_finish(const DecodeParams& p, float* ored, const fl
     // newer token.  The loop bound is wave-uniform so block reductions see whole waves.
     __shared__ unsigned long long wkey[4];
     __shared__ int wat[4];
+    // The stored values are the splits' weights 2^(x - m_s) (WEIGHTS) or the logits x.
+    // Split s's weight for query head j, 2^(m_s - M) / L, is read from LDS at
+    // ored[(s - s_lo) * G + j]: the merge left those of up to 64 splits there (s_lo = 0);
+    // one split has 1 / L; with more than 64 each iteration stages those of its own slots'
+    // splits (at most 65) from the published (m, l).
+    constexpr int IT = kDecodeThreads * EU_OF<BLOCKS>();  // slots per iteration
+    if (n_splits == 1) {
+      __builtin_amdgcn_s_waitcnt(0);  // this workgroup's stores of the values have completed
+      __syncthreads();                // (and every thread is done with ored)
+      if constexpr (WEIGHTS) {
+        if (threadIdx.x < G) ored[threadIdx.x] = Linv[threadIdx.x];
+        __syncthreads();
+      }
+    }
     float* score = p.score + bg * p.C;
     int* pos = const_cast<int*>(p.pos) + bg * p.C;
     // a fused append's slot holds the new token (score 0 before this step's weight) and a
@@ -565,9 +583,26 @@ __device__ inline void split_finish(const DecodeParams& p, float* ored, const fl
     const int emp_end = p.h2o_step && p.new_block ? nslot + p.bs : -1;
     Victim best;
     const int bs = BLOCKS ? p.bs : 1;  // eviction granule
-    constexpr int EU = BLOCKS ? kH2oEuBlk : kH2oEu;  // slots per thread per iteration, all loads issued first
-    for (int base = threadIdx.x - lane; base < p.n; base += kDecodeThreads * EU) {
+    constexpr int EU = EU_OF<BLOCKS>();  // slots per thread per iteration, all loads issued first
+    // the iteration count is the workgroup's (waves past n run with every slot out of range),
+    // so that weight staging can use barriers and block reductions see whole waves
+    for (int it0 = 0; it0 < p.n; it0 += IT) {
+      const int base = it0 + (int)threadIdx.x - lane;
       const int i0 = base + lane;
+      int s_lo = 0;
+      if constexpr (WEIGHTS) {
+        if (n_splits > 64) {  // workgroup-uniform
+          s_lo = it0 / p.chunk;
+          const int ns = min(n_splits, (it0 + IT - 1) / p.chunk + 1) - s_lo;
+          const size_t BHq = (size_t)p.B * p.Hq;
+          __syncthreads();  // the previous iteration's reads are done
+          for (int e = threadIdx.x; e < ns * G; e += kDecodeThreads) {
+            const int sp = s_lo + e / G, j = e % G;
+            ored[e] = exp2f(load_dev(&p.part_ml[((size_t)sp * BHq + bh0 + j) * 2]) - Mtot[j]) * Linv[j];
+          }
+          __syncthreads();
+        }
+      }
       float x[EU][G], sc[EU];
       int ps[EU];
 #pragma unroll
@@ -594,8 +629,14 @@ __device__ inline void split_finish(const DecodeParams& p, float* ored, const fl
       for (int u = 0; u < EU; ++u) {
         const bool in = i0 + u * kDecodeThreads < p.n;
         float a = 0.f;
+        if constexpr (WEIGHTS) {
+          const float* w = ored + (min(i0 + u * kDecodeThreads, p.n - 1) / p.chunk - s_lo) * G;
 #pragma unroll
-        for (int j = 0; j < G; ++j) a += exp2f(x[u][j] - Mtot[j]) * Linv[j];
+          for (int j = 0; j < G; ++j) a += x[u][j] * w[j];
+        } else {
+#pragma unroll
+          for (int j = 0; j < G; ++j) a += exp2f(x[u][j] - Mtot[j]) * Linv[j];
+        }
         snew[u] = in ? sc[u] + a : 0.f;
       }
       if (p.pick_victim) {
@@ -1003,7 +1044,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_onepass_kernel(DecodePa
     ored[idx] = acc;
   }
   __syncthreads();
-  split_finish<D, G, LOGITS, MASKED>(p, ored, Mh, Lh, split, n_splits, b, g);
+  split_finish<D, G, LOGITS, MASKED, false>(p, ored, Mh, Lh, split, n_splits, b, g);
 }
 
 // ---------------------------------------------------------------- two-pass kernel
@@ -1289,8 +1330,6 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
         const int key = key0 + slot_u[i] * KPI;
         if (!TAIL || key < cnt) {
           xs[key * G + slot_j[i]] = d[i];
-          if constexpr (LOGITS)
-            store_dev(&p.logits[((size_t)b * p.Hq + g * G + slot_j[i]) * p.C + s_begin + key], d[i]);
         }
       }
     }
@@ -1428,6 +1467,18 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
     for (; base + VSTEP <= cnt; base += VSTEP) v_iter(base, std::false_type{});
     if (base < cnt) v_iter(base, std::true_type{});
   }
+  if constexpr (LOGITS) {
+    // the H2O epilogue's inputs: the range's weights 2^(x - m) per query head (m: the
+    // range's maximum; a head with no live key in the range stores zeros), stored after the
+    // V pass rather than key by key in the K pass: a wave's memory requests complete in
+    // order, so device-coherent stores among the K loads would hold back every later load
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const bool live = Mh[j] > -INFINITY;
+      float* dst = p.logits + ((size_t)b * p.Hq + g * G + j) * p.C + s_begin;
+      for (int key = threadIdx.x; key < cnt; key += kDecodeThreads) store_dev(&dst[key], live ? xs[key * G + j] : 0.f);
+    }
+  }
   __syncthreads();  // xs is reused as the waves' output buffer below
 
   // ---- merge the key groups of each wave, then the 4 waves
@@ -1453,7 +1504,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
   for (int idx = threadIdx.x; idx < G * D; idx += kDecodeThreads)  // each thread reads only its idx
     ored[idx] = ored[idx] + ored[G * D + idx] + ored[2 * G * D + idx] + ored[3 * G * D + idx];
   __syncthreads();
-  split_finish<D, G, LOGITS, MASKED>(p, ored, Mh, Lh, split, n_splits, b, g);
+  split_finish<D, G, LOGITS, MASKED, true>(p, ored, Mh, Lh, split, n_splits, b, g);
 }
 
 // Victim choice for a seeded H2O layer (no decode step has run yet): the lowest score

@@ -28,7 +28,8 @@ struct DecodeParams {
   float* out;          // [B][Hq][D] float32
   float* part_o;       // [splits][B][Hq][D]
   float* part_ml;      // [splits][B][Hq][2]  (max, sum) in the log2 domain
-  float* logits;       // [B][Hq][C] log2-domain logits (logits mode)
+  float* logits;       // [B][Hq][C] per slot: log2-domain logit (one-pass kernel) or the
+                       // split's weight 2^(x - m_s) (two-pass kernel) (logits mode)
   int* arrivals;       // layer [B][Hkv] arrival counters, zero between calls
   // H2O epilogue (logits mode)
   float* score;        // layer [B][Hkv][C]
