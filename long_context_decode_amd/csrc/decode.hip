@@ -53,6 +53,9 @@ constexpr int kMergeSu = 4;  // split merge: splits whose loads are issued toget
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // W 32-bit words of one row piece, loaded in one instruction (W = 4: 16 bytes, W = 2: 8).
 template <int W>
@@ -263,13 +266,15 @@ constexpr size_t onepass_lds_bytes() {
   return ((size_t)4 * G * D + 14 * G) * sizeof(float);
 }
 
-// Dynamic LDS of the two-pass kernel: the logits [chunk][G] (reused for the 4 waves'
-// outputs [4][G][D] after the V pass), cross-wave reductions [4][G] and the
-// workgroup's (m, l) [2][G].
+// Dynamic LDS of the two-pass kernel: the logits [G][chunk + kXsPad] (reused for the
+// output after the V pass: [4][G][D] for float32 caches, [G][D] for bf16), cross-wave
+// reductions [4][G] and the workgroup's (m, l) [2][G].  The padding shifts each query
+// head's row by 16 bytes, so the V pass's reads of G rows at one key fall in distinct banks.
 constexpr int kTwopassRed = 64;  // cross-wave reduction floats: 4 waves x (U * G <= 16)
+constexpr int kXsPad = 4;
 template <int D, int G>
 inline size_t twopass_lds_floats(int chunk) {
-  const size_t a = (size_t)chunk * G, o = (size_t)4 * G * D;
+  const size_t a = (size_t)(chunk + kXsPad) * G, o = (size_t)4 * G * D;
   return (a > o ? a : o) + kTwopassRed + 2 * G;
 }
 
@@ -681,7 +686,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_onepass_kernel(DecodePa
   constexpr int D2 = D / 2;
   using E = Elem<T, W>;
 
-  extern __shared__ float smem[];
+  extern __shared__ __attribute__((aligned(16))) float smem[];
   float* ored = smem;                 // [4][G][D] the waves' outputs, then [G][D] their merge
   float* wm = ored + 4 * G * D;       // [4][G] the waves' maxima
   float* wl = wm + 4 * G;             // [4][G] the waves' sums
@@ -1051,12 +1056,12 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_onepass_kernel(DecodePa
 // For 4 or more query heads per KV head.  K pass: every key of the range is loaded
 // once, rotated, dotted with the G queries; logits go to LDS.  Softmax: the range
 // maximum per query head, p = 2^(x - m) in LDS, l = sum p.  V pass: every value row is
-// loaded once and accumulated with the G weights.  Registers then hold either the
-// queries (K pass) or the outputs (V pass), never both, which keeps G * D-sized state
-// within two waves per SIMD at 16-byte pieces.
+// loaded once and accumulated with the G weights, on the matrix cores for bf16 values.
+// Registers then hold either the queries (K pass) or the outputs (V pass), never both,
+// which keeps G * D-sized state within two waves per SIMD at 16-byte pieces.
 //
-// With G >= 4 this kernel is bound by VALU issue (G multiply-adds per key element in
-// each pass, against one byte loaded per 1/2 element), so the loops carry no per-key
+// The K pass takes G multiply-adds per key element (against one byte loaded per 1/2
+// element), which makes it VALU-heavy, so its loop carries no per-key
 // work beyond that arithmetic: rows are addressed by 32-bit offsets from the range's
 // uniform base, a fused append's rows are written to the cache before the passes (so no
 // load selects between cache and input), in-cache positions come from the range's two
@@ -1077,9 +1082,10 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
   constexpr uint32_t ROW = D * sizeof(T);  // bytes per cache row
   static_assert(LPK >= 1 && LPK <= 64 && (64 % LPK) == 0, "lane mapping");
 
-  extern __shared__ float smem[];
-  const int region = (p.chunk * G > 4 * G * D ? p.chunk * G : 4 * G * D);
-  float* xs = smem;                 // [chunk][G] logits, then weights
+  extern __shared__ __attribute__((aligned(16))) float smem[];
+  const int XS = p.chunk + kXsPad;  // row stride of xs
+  const int region = (XS * G > 4 * G * D ? XS * G : 4 * G * D);
+  float* xs = smem;                 // [G][XS] logits, then weights
   float* ored = smem;               // [4][G][D] the waves' outputs (after the V pass), then [G][D]
   float* red = smem + region;       // [4][U * G] / [4][G] cross-wave reductions (kTwopassRed floats)
   float* Mh = red + kTwopassRed;    // [G] the range's maxima
@@ -1329,7 +1335,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
       for (int i = 0; i < NF; ++i) {
         const int key = key0 + slot_u[i] * KPI;
         if (!TAIL || key < cnt) {
-          xs[key * G + slot_j[i]] = d[i];
+          xs[slot_j[i] * XS + key] = d[i];
         }
       }
     }
@@ -1366,7 +1372,11 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
     }
   }
 
-  // first V rows are requested before the softmax barriers (their latency overlaps them)
+  // ---- V pass set-up.  bf16 values go through the matrix cores, float32 values through
+  // the vector ALUs; either way the first rows are requested before the softmax barriers
+  // (their latency overlaps them).
+  constexpr bool MV = sizeof(T) == 2;
+  // float32: UV rows per lane group per iteration, in registers
   constexpr int UV = G <= 6 ? 4 : 2;
   constexpr int VSTEP = KPI * UV;
   Words<4> vlo[UV], vhi[UV];
@@ -1378,7 +1388,45 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
       vhi[u] = load_words<4>(vw + (off + hi_off));
     }
   };
-  load_v(0);
+  // bf16: o^T = V^T P^T as 16 x 16 x 32 MFMAs (v_mfma_f32_16x16x32_bf16) over tiles of 32 keys.
+  // A wave owns 64 dims (one 128-byte line of every row) of the tiles of its key group: the
+  // D / 64 dim groups times 256 / D key groups make the 4 waves, key group k taking the
+  // range's tiles k, k + KGN, ...  A tile's rows come into registers PFT tiles ahead, are
+  // written to the wave's LDS staging area and read back transposed (ds_read_b64_tr_b16:
+  // lane n of each 16-lane group gets column n of a 4 x 16 block), so each lane holds 8 keys
+  // of one dim, the MFMA's B operand.  The A operand holds the weights of the 32 keys split
+  // exactly into two bf16 terms, hi = the weight with its low 16 bits cleared and lo =
+  // bf16(weight - hi) (relative error <= 2^-16): rows j < G of the 16 x 32 operand are
+  // query head j's hi terms, rows G + j its lo terms, the rest zero, so one MFMA per 16
+  // dims and 32 keys accumulates both; they are added together, and the key groups, at the end.
+  constexpr int NDG = D / 64;          // dim groups
+  constexpr int KGN = 4 / NDG;         // key groups
+  constexpr int KSTR = KGN * 32;       // keys between a key group's consecutive tiles
+  constexpr int IPT = 4;               // load instructions per tile (8 keys x 128 bytes each)
+  constexpr int NT = 4;                // 16-dim column tiles per wave
+  constexpr int PFT = 4;               // tiles in flight
+  constexpr int SROW = 128;            // bytes of a staged row
+  static_assert(!MV || 2 * G <= 16, "hi and lo weight rows of G query heads fill at most 16 rows");
+  // staged piece c of key k sits at piece c ^ swz(k) of its row: the transposed reads of
+  // 4 keys x 4 pieces per 16 lanes then cover all banks
+  auto swz = [](int key) { return 2 * (key & 3); };
+  __shared__ __attribute__((aligned(16))) char vstage[MV ? 4 * 32 * SROW : 16];
+  char* stg = vstage + wave * (32 * SROW);
+  const int vdg = wave % NDG, vkg = wave / NDG;  // the wave's dim group and key group
+  const int lr = lane / 8, lc = lane % 8;        // load instruction: key, piece
+  const uint32_t gl_off = (uint32_t)(vdg * SROW + lc * 16);
+  Words<4> vb[MV ? PFT : 1][IPT];
+  auto load_tile = [&](int kb, Words<4> (&r)[IPT]) {
+#pragma unroll
+    for (int i = 0; i < IPT; ++i)  // unconditional loads (keys past the range: the last row)
+      r[i] = load_words<4>(vw + ((uint32_t)min(kb + i * 8 + lr, cnt - 1) * ROW + gl_off));
+  };
+  if constexpr (MV) {
+#pragma unroll
+    for (int t = 0; t < PFT; ++t) load_tile(vkg * 32 + t * KSTR, vb[t]);
+  } else {
+    load_v(0);
+  }
 
   // ---- range maximum per query head: each value slot across the wave's key groups, the
   // slots of the writer lanes of key group 0 into LDS [4 waves][U * G], then across waves
@@ -1413,8 +1461,8 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
   for (int key = threadIdx.x; key < cnt; key += kDecodeThreads) {
 #pragma unroll
     for (int j = 0; j < G; ++j) {
-      const float e = exp2f(xs[key * G + j] - M[j]);
-      xs[key * G + j] = e;
+      const float e = exp2f(xs[j * XS + key] - M[j]);
+      xs[j * XS + key] = e;
       ls[j] += e;
     }
   }
@@ -1427,8 +1475,75 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
   if (threadIdx.x < G)
     Lh[threadIdx.x] = red[threadIdx.x] + red[G + threadIdx.x] + red[2 * G + threadIdx.x] + red[3 * G + threadIdx.x];
 
-  // ---- V pass: UV rows per lane group per iteration; the next iteration's rows are
-  // requested before this iteration's arithmetic (software pipelining)
+  // ---- V pass, bf16: PFT tiles in flight; each tile is staged, its slot refilled with the
+  // tile PFT ahead, then multiplied
+  f32x4 acc[MV ? NT : 1];
+  if constexpr (MV) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const uint32_t st_off = (uint32_t)(lr * SROW + 16 * (lc ^ swz(lr)));  // (swz(8 i + lr) = swz(lr))
+    // transposed reads: lane (g, e, q) = (lane / 16, lane / 4 % 4, lane % 4) addresses key
+    // 8 g + e (+ 4 for the second read), dims 16 t + 4 q .. + 3 of column tile t
+    const int tk = 8 * (lane >> 4) + ((lane >> 2) & 3), tq = lane & 3;
+    uint32_t tr_off[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) tr_off[t] = (uint32_t)(tk * SROW + 16 * ((2 * t + (tq >> 1)) ^ swz(tk)) + 8 * (tq & 1));
+    // A operand: lane (g, m) = (lane / 16, lane % 16) holds row m for keys 8 g .. 8 g + 7
+    const int am = lane & 15, ag = lane >> 4;
+    const bool a_hi = am < G, a_lo = am >= G && am < 2 * G;
+    const uint32_t m_hi = a_hi ? ~0u : 0u, m_lo = a_lo ? ~0u : 0u;  // masks: no branch per pair
+    const float* wsrc = xs + (a_hi ? am : a_lo ? am - G : 0) * XS + 8 * ag;
+    auto stage = [&](const Words<4> (&r)[IPT]) {
+#pragma unroll
+      for (int i = 0; i < IPT; ++i)
+        *reinterpret_cast<u32x4*>(stg + st_off + i * 1024) = u32x4{r[i].w[0], r[i].w[1], r[i].w[2], r[i].w[3]};
+    };
+    auto multiply = [&](int kb, auto tail) {
+      constexpr bool TAIL = decltype(tail)::value;  // keys may lie past the range
+      const f32x4 w0 = *reinterpret_cast<const f32x4*>(wsrc + kb);
+      const f32x4 w1 = *reinterpret_cast<const f32x4*>(wsrc + kb + 4);
+      float w[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+      if constexpr (TAIL) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w[i] = kb + 8 * ag + i < cnt ? w[i] : 0.f;
+      }
+      u32x4 a;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t h0 = __float_as_uint(w[2 * k]) & 0xffff0000u, h1 = __float_as_uint(w[2 * k + 1]) & 0xffff0000u;
+        const bf16x2 lo = {(__bf16)(w[2 * k] - __uint_as_float(h0)), (__bf16)(w[2 * k + 1] - __uint_as_float(h1))};
+        a[k] = (((h0 >> 16) | h1) & m_hi) | (__builtin_bit_cast(uint32_t, lo) & m_lo);
+      }
+      const bf16x8 A = __builtin_bit_cast(bf16x8, a);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+        const i16x4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(stg + tr_off[t]));
+        const i16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(stg + tr_off[t] + 4 * SROW));
+        const bf16x8 B = __builtin_bit_cast(bf16x8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[t], 0, 0, 0);
+      }
+    };
+    int kb = vkg * 32;
+    for (; kb + (PFT - 1) * KSTR + 32 <= cnt; kb += PFT * KSTR) {  // PFT whole tiles
+#pragma unroll
+      for (int t = 0; t < PFT; ++t) {
+        stage(vb[t]);
+        load_tile(kb + (t + PFT) * KSTR, vb[t]);  // unconditional (past the range: clamped rows)
+        multiply(kb + t * KSTR, std::false_type{});
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < PFT; ++t) {  // the key group's last tiles, already in flight
+      if (kb + t * KSTR < cnt) {
+        stage(vb[t]);
+        multiply(kb + t * KSTR, std::true_type{});
+      }
+    }
+  }
+
+  // ---- V pass, float32: UV rows per lane group per iteration; the next iteration's rows
+  // are requested before this iteration's arithmetic (software pipelining)
   float o[G][EPL];
 #pragma unroll
   for (int j = 0; j < G; ++j)
@@ -1452,7 +1567,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
         E::cvt(chi[u], hi);
 #pragma unroll
         for (int j = 0; j < G; ++j) {
-          const float w = xs[key * G + j];
+          const float w = xs[j * XS + key];
 #pragma unroll
           for (int e = 0; e < HALF; ++e) {
             o[j][e] = fmaf(w, lo[e], o[j][e]);
@@ -1462,7 +1577,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
       }
     }
   };
-  {
+  if constexpr (!MV) {
     int base = 0;
     for (; base + VSTEP <= cnt; base += VSTEP) v_iter(base, std::false_type{});
     if (base < cnt) v_iter(base, std::true_type{});
@@ -1476,10 +1591,40 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
     for (int j = 0; j < G; ++j) {
       const bool live = Mh[j] > -INFINITY;
       float* dst = p.logits + ((size_t)b * p.Hq + g * G + j) * p.C + s_begin;
-      for (int key = threadIdx.x; key < cnt; key += kDecodeThreads) store_dev(&dst[key], live ? xs[key * G + j] : 0.f);
+      for (int key = threadIdx.x; key < cnt; key += kDecodeThreads) store_dev(&dst[key], live ? xs[j * XS + key] : 0.f);
     }
   }
-  __syncthreads();  // xs is reused as the waves' output buffer below
+  __syncthreads();  // xs is reused as the output buffer below
+
+  if constexpr (MV) {
+    // lane (g, n) holds rows 4 g .. 4 g + 3 of column n of each tile: the hi rows first (key
+    // group k into ored[k][G][D]), then the lo rows added to them, then the key groups summed
+    const int ag = lane >> 4, n = lane & 15;
+    float* mine = ored + vkg * G * D + vdg * 64 + n;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (4 * ag + r < G) mine[(4 * ag + r) * D + 16 * t] = acc[t][r];
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (4 * ag + r >= G && 4 * ag + r < 2 * G) mine[(4 * ag + r - G) * D + 16 * t] += acc[t][r];
+    __syncthreads();
+    if constexpr (KGN > 1) {
+      for (int idx = threadIdx.x; idx < G * D; idx += kDecodeThreads) {  // each thread reads only its idx
+        float x = ored[idx];
+#pragma unroll
+        for (int k = 1; k < KGN; ++k) x += ored[k * G * D + idx];
+        ored[idx] = x;
+      }
+      __syncthreads();
+    }
+    split_finish<D, G, LOGITS, MASKED, true>(p, ored, Mh, Lh, split, n_splits, b, g);
+    return;
+  }
 
   // ---- merge the key groups of each wave, then the 4 waves
 #pragma unroll
@@ -1592,9 +1737,10 @@ static hipError_t launch_t(int D, int G, int mode, const DecodeParams& p, hipStr
 
 int decode_chunk_cap(int G) {
   if (G <= kOnepassMaxG) return 1 << 24;  // the one-pass kernel keeps no per-slot state in LDS
-  // two-pass: chunk * G logits + the reduction and (max, sum) floats within 64 KiB, 256
-  // bytes kept for the static shared variables
-  return (16384 - 64 - kTwopassRed - 2 * G) / G / 64 * 64;
+  // two-pass: (chunk + kXsPad) * G logits + the reduction and (max, sum) floats within 64 KiB,
+  // 256 bytes kept for the small static shared variables (the bf16 V pass's 16 KiB staging
+  // area brings a workgroup to at most 80 KiB, two per compute unit)
+  return ((16384 - 64 - kTwopassRed - 2 * G) / G - kXsPad) / 64 * 64;
 }
 
 bool decode_supported(int dtype, int D, int G) {
