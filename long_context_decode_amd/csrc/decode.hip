@@ -1395,8 +1395,8 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
   // written to the wave's LDS staging area and read back transposed (ds_read_b64_tr_b16:
   // lane n of each 16-lane group gets column n of a 4 x 16 block), so each lane holds 8 keys
   // of one dim, the MFMA's B operand.  The A operand holds the weights of the 32 keys split
-  // exactly into two bf16 terms, hi = the weight with its low 16 bits cleared and lo =
-  // bf16(weight - hi) (relative error <= 2^-16): rows j < G of the 16 x 32 operand are
+  // into two bf16 terms, hi = the weight with its low 16 bits cleared and lo =
+  // bf16(weight - hi) (relative error < 2^-15): rows j < G of the 16 x 32 operand are
   // query head j's hi terms, rows G + j its lo terms, the rest zero, so one MFMA per 16
   // dims and 32 keys accumulates both; they are added together, and the key groups, at the end.
   constexpr int NDG = D / 64;          // dim groups
