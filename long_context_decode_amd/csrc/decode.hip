@@ -757,13 +757,13 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_onepass_kernel(DecodePa
   }
 
   // ---- RoPE angles of the keys.  With few query heads (G <= 2, where the kernel is
-  // far from ALU-bound) a lane group's U keys of one iteration take one table row: they
-  // sit KPI slots apart, and where their in-cache positions are also KPI apart
-  // (everywhere except across the ring's wrap point and the sink boundary) the cos/sin
-  // of key u+1 follow from key u's by one angle addition with the per-lane constant
-  // rotation (cos, sin)(KPI * theta_i).  Waves that straddle a discontinuity read every
-  // key's row.  With more query heads every key reads its own row (the split's table
-  // slice stays in its XCD's L2).
+  // far from ALU-bound) a lane group's keys sit KPI slots apart, and where their in-cache
+  // positions are also KPI apart (everywhere except across the ring's wrap point and the
+  // sink boundary) the cos/sin of a key follow from the previous key's by one angle
+  // addition with the per-lane constant rotation (cos, sin)(KPI * theta_i), across
+  // iterations too: a table row is read only in every other iteration (an anchor), and
+  // waves whose keys break the rank sequence read every key's row.  With more query heads
+  // every key reads its own row (the split's table slice stays in its XCD's L2).
   constexpr bool REC = ROPE && G <= 2;
   constexpr int NCS = ROPE ? (REC ? 1 : U) : 1;  // table rows held per iteration
   float dc[HALF], ds[HALF];
@@ -784,6 +784,14 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_onepass_kernel(DecodePa
     load_floats<HALF>(p.cos_t + (size_t)rank * D2 + i0, c);
     load_floats<HALF>(p.sin_t + (size_t)rank * D2 + i0, sn);
   };
+  auto advance = [&](float (&c)[HALF], float (&sn)[HALF]) {  // by KPI ranks
+#pragma unroll
+    for (int e = 0; e < HALF; ++e) {
+      const float cc = c[e] * dc[e] - sn[e] * ds[e];
+      sn[e] = sn[e] * dc[e] + c[e] * ds[e];
+      c[e] = cc;
+    }
+  };
 
   // one iteration's registers: the raw K and V pieces of U keys, and the table rows
   struct Buf {
@@ -791,7 +799,9 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_onepass_kernel(DecodePa
     float c[NCS][HALF], sn[NCS][HALF];
     int mp[U];  // H2O blocks: the slots' positions (< 0: empty)
   };
-  auto load_iter = [&](int base, Buf& bf) {
+  // TABLE: an anchor iteration, which also loads its first key's table row
+  auto load_iter = [&](int base, Buf& bf, auto table) {
+    constexpr bool TABLE = decltype(table)::value;
     const int key0 = base + wave * KPW + kg;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -819,11 +829,14 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_onepass_kernel(DecodePa
         bf.mp[u] = key >= cnt ? -1 : key == new_key ? 0 : (key > emp_lo && key < emp_hi) ? -1 : v;
       }
     }
-    if constexpr (ROPE) {
+    if constexpr (ROPE && (TABLE || !REC)) {
 #pragma unroll
       for (int u = 0; u < NCS; ++u) load_cs(rank_of(s_begin + min(key0 + u * KPI, cnt - 1)), bf.c[u], bf.sn[u]);
     }
   };
+  // REC: the table row of the lane group's current key and its rank
+  float rc[HALF], rs[HALF];
+  int rrank = 0;
 
   // running softmax state of this lane group (identical in its LPK lanes)
   float m[G], l[G], o[G][EPL];
@@ -835,16 +848,21 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_onepass_kernel(DecodePa
     for (int e = 0; e < EPL; ++e) o[j][e] = 0.f;
   }
 
-  auto compute_iter = [&](int base, Buf& bf) {
+  auto compute_iter = [&](int base, Buf& bf, auto anchor) {
+    constexpr bool ANCHOR = decltype(anchor)::value;
     const int key0 = base + wave * KPW + kg;
-    bool stepwise = false;  // REC: this wave straddles a rank discontinuity
+    bool stepwise = false;  // REC: this wave's keys break the rank sequence
+    int rk[U];              // REC: the keys' ranks
     if constexpr (REC) {
-      const int rank0 = rank_of(s_begin + min(key0, cnt - 1));
+      // an anchor starts at its loaded row; otherwise the first key continues the previous
+      // iteration's last one
+      const int rank0 = ANCHOR ? rank_of(s_begin + min(key0, cnt - 1)) : rrank + KPI;
       bool disc = false;
 #pragma unroll
-      for (int u = 1; u < U; ++u) {
+      for (int u = 0; u < U; ++u) {
         const int key = key0 + u * KPI;
-        disc |= key < cnt && rank_of(s_begin + key) != rank0 + u * KPI;
+        rk[u] = rank_of(s_begin + min(key, cnt - 1));
+        if (u > 0 || !ANCHOR) disc |= key < cnt && rk[u] != rank0 + u * KPI;
       }
       stepwise = __any(disc);
     }
@@ -873,27 +891,29 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_onepass_kernel(DecodePa
         float lo[HALF], hi[HALF];
         E::cvt(bf.klo[u], lo);
         E::cvt(bf.khi[u], hi);
-        if constexpr (ROPE) {
-          const int ci = REC ? 0 : u;
-          if constexpr (REC) {
-            if (u > 0) {
-              if (stepwise) {
-                load_cs(rank_of(s_begin + min(key0 + u * KPI, cnt - 1)), bf.c[0], bf.sn[0]);
-                wait_loads();  // complete here, so the common path keeps the next set's loads in flight
-              } else {
+        if constexpr (REC) {
+          if (u == 0 && ANCHOR) {
 #pragma unroll
-                for (int e = 0; e < HALF; ++e) {
-                  const float cc = bf.c[0][e] * dc[e] - bf.sn[0][e] * ds[e];
-                  bf.sn[0][e] = bf.sn[0][e] * dc[e] + bf.c[0][e] * ds[e];
-                  bf.c[0][e] = cc;
-                }
-              }
+            for (int e = 0; e < HALF; ++e) {
+              rc[e] = bf.c[0][e];
+              rs[e] = bf.sn[0][e];
             }
-          }
+          } else if (stepwise) {
+            load_cs(rk[u], rc, rs);
+            wait_loads();  // complete here, so the common path keeps the next set's loads in flight
+          } else if (u > 0) {
+            advance(rc, rs);
+          }  // (u = 0 otherwise: advanced after the previous iteration)
 #pragma unroll
           for (int e = 0; e < HALF; ++e) {
-            kf[e] = lo[e] * bf.c[ci][e] - hi[e] * bf.sn[ci][e];
-            kf[HALF + e] = lo[e] * bf.sn[ci][e] + hi[e] * bf.c[ci][e];
+            kf[e] = lo[e] * rc[e] - hi[e] * rs[e];
+            kf[HALF + e] = lo[e] * rs[e] + hi[e] * rc[e];
+          }
+        } else if constexpr (ROPE) {
+#pragma unroll
+          for (int e = 0; e < HALF; ++e) {
+            kf[e] = lo[e] * bf.c[u][e] - hi[e] * bf.sn[u][e];
+            kf[HALF + e] = lo[e] * bf.sn[u][e] + hi[e] * bf.c[u][e];
           }
         } else {
 #pragma unroll
@@ -910,6 +930,10 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_onepass_kernel(DecodePa
         for (int e = 0; e < EPL; ++e) acc = fmaf(qf[j][e], kf[e], acc);
         d[u * G + j] = acc;
       }
+    }
+    if constexpr (REC) {  // the row of the next iteration's first key
+      advance(rc, rs);
+      rrank = (stepwise ? rk[U - 1] : (ANCHOR ? rk[0] : rrank + KPI) + (U - 1) * KPI);
     }
     group_sum_n<LPK, U * G>(d);
     if constexpr (DOT2) {
@@ -982,14 +1006,16 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_onepass_kernel(DecodePa
   // ---- the pass: two register sets alternate, the next iteration's loads are issued
   // before this iteration's arithmetic (a third set measured no faster)
   {
+    const std::true_type yes{};  // A's iterations are the anchors
+    const std::false_type no{};
     Buf A, B;
-    load_iter(0, A);
+    load_iter(0, A, yes);
     for (int base = 0; base < cnt; base += 2 * STEP) {
-      load_iter(base + STEP, B);  // unconditional (past the range: clamped rows)
-      compute_iter(base, A);
+      load_iter(base + STEP, B, no);  // unconditional (past the range: clamped rows)
+      compute_iter(base, A, yes);
       if (base + STEP >= cnt) break;
-      load_iter(base + 2 * STEP, A);
-      compute_iter(base + STEP, B);
+      load_iter(base + 2 * STEP, A, yes);
+      compute_iter(base + STEP, B, no);
     }
   }
 
@@ -1183,12 +1209,16 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
 
   // ---- K pass: U keys per lane group per iteration, the next iteration's loads issued
   // before this iteration's arithmetic (two register sets alternate; G = 8 has room for
-  // one).  RoPE: one table row per iteration, the following keys' angles by angle
-  // addition of (cos, sin)(KPI * theta_i), except in a wave whose keys of the iteration
-  // straddle a rank breakpoint, which reads every key's row.
+  // one).  RoPE: a lane group's keys of consecutive iterations are KPI slots apart, and
+  // (except across a rank breakpoint) so are their ranks, so each key's table row is the
+  // previous key's advanced by angle addition of (cos, sin)(KPI * theta_i).  A row is read
+  // from the table only in every other iteration (an anchor, which bounds the rounding
+  // carried along to 2U - 1 additions) and wherever the recurrence would cross a
+  // breakpoint: table loads share the K rows' load path, and one row per iteration made the
+  // GQA launch 3.5% slower (one per key, slower still; one per four iterations, no faster).
   constexpr int U = G <= 4 ? (ROPE ? 3 : 4) : 2;
   static_assert(U * G % 4 == 0 && U * G <= 16, "lane-group sums leave U * G / 4 values per lane");
-  constexpr bool REC = ROPE;  // (reading every key's table row instead measured 10-20% slower)
+  constexpr bool REC = ROPE;
   constexpr int STEP = KPI * U;
   float dc[HALF], ds[HALF];
   if constexpr (REC) {
@@ -1201,7 +1231,9 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
     float c[NC][HALF], sn[NC][HALF];  // RoPE: table rows (with angle additions: the first key's)
     int mp[U];                        // H2O blocks: the slots' positions (< 0: empty)
   };
-  auto load_iter = [&](int base, KBuf& bf) {
+  // TABLE: an anchor iteration, which also loads its first key's table row
+  auto load_iter = [&](int base, KBuf& bf, auto table) {
+    constexpr bool TABLE = decltype(table)::value;
     const int key0 = base + wave * KPW + kg;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -1221,7 +1253,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
         bf.mp[u] = key >= cnt ? -1 : key == new_key ? 0 : (key > emp_lo && key < emp_hi) ? -1 : v;
       }
     }
-    if constexpr (ROPE) {
+    if constexpr (ROPE && TABLE) {
 #pragma unroll
       for (int u = 0; u < NC; ++u) load_cs(rank_of_key(min(key0 + u * KPI, cnt - 1)), bf.c[u], bf.sn[u]);
     }
@@ -1231,6 +1263,21 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
     const int lo = base + wave * KPW, hi = lo + KPW - 1 + (U - 1) * KPI;
     return (kb1 > lo && kb1 <= hi) || (kb2 > lo && kb2 <= hi);
   };
+  // does a breakpoint lie between the wave's keys of the previous iteration and this one's
+  // first keys (wave-uniform)?
+  auto jumps_before = [&](int base) {
+    const int lo = base + wave * KPW - KPI, hi = base + wave * KPW + KPW - 1;
+    return (kb1 > lo && kb1 <= hi) || (kb2 > lo && kb2 <= hi);
+  };
+  auto advance = [&](float (&c)[HALF], float (&sn)[HALF]) {  // by KPI ranks
+#pragma unroll
+    for (int e = 0; e < HALF; ++e) {
+      const float cc = c[e] * dc[e] - sn[e] * ds[e];
+      sn[e] = sn[e] * dc[e] + c[e] * ds[e];
+      c[e] = cc;
+    }
+  };
+  float rc[HALF], rs[HALF];  // RoPE: the table row of the lane group's current key
   // after the lane-group sums a lane holds NF = U * G / 4 of the iteration's U * G logits:
   // value index vbase + i, i.e. key step slot_u[i] and query head slot_j[i]; the lanes that
   // hold totals and write them ("writers") are one per index class of each key group
@@ -1246,11 +1293,15 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
   float mxs[NF];  // running maxima of this lane's value slots
 #pragma unroll
   for (int i = 0; i < NF; ++i) mxs[i] = -INFINITY;
-  auto compute_iter = [&](int base, KBuf& bf, auto tail) {
+  auto compute_iter = [&](int base, KBuf& bf, auto tail, auto anchor) {
     constexpr bool TAIL = decltype(tail)::value;  // keys may lie past the range
+    constexpr bool ANCHOR = decltype(anchor)::value;
     const int key0 = base + wave * KPW + kg;
-    bool stepwise = false;
-    if constexpr (REC) stepwise = straddles(base);
+    bool stepwise = false, gap = false;
+    if constexpr (REC) {
+      stepwise = straddles(base);
+      if constexpr (!ANCHOR) gap = jumps_before(base);
+    }
     float d[U * G];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -1275,26 +1326,27 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
         E::cvt(bf.lo[u], lo);
         E::cvt(bf.hi[u], hi);
         if constexpr (ROPE) {
-          const int ci = REC ? 0 : u;
-          if constexpr (REC) {
-            if (u > 0) {
-              if (stepwise) {
-                load_cs(rank_of_key(min(key0 + u * KPI, cnt - 1)), bf.c[0], bf.sn[0]);
-                wait_loads();  // complete here, so the common path keeps the next set's loads in flight
-              } else {
+          if (u == 0) {
+            if constexpr (ANCHOR) {
 #pragma unroll
-                for (int e = 0; e < HALF; ++e) {
-                  const float cc = bf.c[0][e] * dc[e] - bf.sn[0][e] * ds[e];
-                  bf.sn[0][e] = bf.sn[0][e] * dc[e] + bf.c[0][e] * ds[e];
-                  bf.c[0][e] = cc;
-                }
+              for (int e = 0; e < HALF; ++e) {
+                rc[e] = bf.c[0][e];
+                rs[e] = bf.sn[0][e];
               }
-            }
+            } else if (gap) {
+              load_cs(rank_of_key(min(key0, cnt - 1)), rc, rs);
+              wait_loads();  // complete here, so the common path keeps the next set's loads in flight
+            }  // else rc / rs already hold this key's row (advanced after the previous iteration)
+          } else if (stepwise) {
+            load_cs(rank_of_key(min(key0 + u * KPI, cnt - 1)), rc, rs);
+            wait_loads();
+          } else {
+            advance(rc, rs);
           }
 #pragma unroll
           for (int e = 0; e < HALF; ++e) {
-            kf[e] = lo[e] * bf.c[ci][e] - hi[e] * bf.sn[ci][e];
-            kf[HALF + e] = lo[e] * bf.sn[ci][e] + hi[e] * bf.c[ci][e];
+            kf[e] = lo[e] * rc[e] - hi[e] * rs[e];
+            kf[HALF + e] = lo[e] * rs[e] + hi[e] * rc[e];
           }
         } else {
 #pragma unroll
@@ -1312,6 +1364,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
         d[u * G + j] = acc;
       }
     }
+    if constexpr (REC) advance(rc, rs);  // the row of the next iteration's first key
     // keys past the range (last iteration) and empty slots of a block cache: logit -inf in
     // every lane of the group, so their totals are -inf
     if constexpr (TAIL || MASKED) {
@@ -1343,31 +1396,34 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
   {
     constexpr bool KPF = G <= 6;
     if constexpr (KPF) {
+      // A's iterations are the anchors
+      const std::true_type yes{};
+      const std::false_type no{};
       KBuf A, B;
-      load_iter(0, A);
+      load_iter(0, A, yes);
       int base = 0;
       for (; base + 2 * STEP <= cnt; base += 2 * STEP) {  // both iterations wholly inside the range
-        load_iter(base + STEP, B);
-        compute_iter(base, A, std::false_type{});
-        load_iter(base + 2 * STEP, A);  // unconditional (past the range: clamped rows)
-        compute_iter(base + STEP, B, std::false_type{});
+        load_iter(base + STEP, B, no);
+        compute_iter(base, A, no, yes);
+        load_iter(base + 2 * STEP, A, yes);  // unconditional (past the range: clamped rows)
+        compute_iter(base + STEP, B, no, no);
       }
       if (base < cnt) {  // one or two more iterations, the last partial
-        load_iter(base + STEP, B);
-        compute_iter(base, A, std::true_type{});
-        if (base + STEP < cnt) compute_iter(base + STEP, B, std::true_type{});
+        load_iter(base + STEP, B, no);
+        compute_iter(base, A, yes, yes);
+        if (base + STEP < cnt) compute_iter(base + STEP, B, yes, no);
       }
-    } else {
+    } else {  // every iteration an anchor
       int base = 0;
       for (; base + STEP <= cnt; base += STEP) {
         KBuf A;
-        load_iter(base, A);
-        compute_iter(base, A, std::false_type{});
+        load_iter(base, A, std::true_type{});
+        compute_iter(base, A, std::false_type{}, std::true_type{});
       }
       if (base < cnt) {
         KBuf A;
-        load_iter(base, A);
-        compute_iter(base, A, std::true_type{});
+        load_iter(base, A, std::true_type{});
+        compute_iter(base, A, std::true_type{}, std::true_type{});
       }
     }
   }
