@@ -1149,6 +1149,19 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
   // H2O blocks: a freed block reopened by this step holds only the new token
   const int new_key = nslot - s_begin;
   const int emp_lo = p.new_block ? new_key : INT_MAX, emp_hi = p.new_block ? new_key + p.bs : INT_MIN;
+  // LDS staging area of the bf16 V pass (16 KiB: 4 waves x 32 rows x 128 bytes).  Until the
+  // V pass it holds the H2O block cache's slot positions of the range (at most 4096 with
+  // the chunk cap), so that the K pass reads them from LDS instead of issuing a global load
+  // per key beside its K rows.
+  constexpr bool MV = sizeof(T) == 2;
+  constexpr int kStageBytes = 4 * 32 * 128;
+  __shared__ __attribute__((aligned(16))) char vstage[MV || MASKED ? kStageBytes : 16];
+  const int* msk = reinterpret_cast<const int*>(vstage);
+  if constexpr (MASKED) {
+    const int* mrow = p.mask_pos + ((size_t)b * p.Hkv + g) * p.C + s_begin;
+    for (int i = threadIdx.x; i < cnt; i += kDecodeThreads) reinterpret_cast<int*>(vstage)[i] = mrow[i];
+    __syncthreads();
+  }
 
   // ---- queries of the group: load, rotate at the query's position, pre-scale.  Without
   // RoPE, bf16 queries stay packed: the K pass takes exact bf16 x bf16 pair products
@@ -1244,11 +1257,10 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
       bf.hi[u] = load_words<4>(kw + (off + hi_off));
     }
     if constexpr (MASKED) {  // an in-range index for every lane, then a select on the value
-      const int* mrow = p.mask_pos + ((size_t)b * p.Hkv + g) * p.C + s_begin;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int key = key0 + u * KPI;
-        const int v = mrow[min(key, cnt - 1)];
+        const int v = msk[min(key, cnt - 1)];
         // the new token's slot is filled; the rest of a reopened block is empty
         bf.mp[u] = key >= cnt ? -1 : key == new_key ? 0 : (key > emp_lo && key < emp_hi) ? -1 : v;
       }
@@ -1431,7 +1443,6 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
   // ---- V pass set-up.  bf16 values go through the matrix cores, float32 values through
   // the vector ALUs; either way the first rows are requested before the softmax barriers
   // (their latency overlaps them).
-  constexpr bool MV = sizeof(T) == 2;
   // float32: UV rows per lane group per iteration, in registers
   constexpr int UV = G <= 6 ? 4 : 2;
   constexpr int VSTEP = KPI * UV;
@@ -1466,7 +1477,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
   // staged piece c of key k sits at piece c ^ swz(k) of its row: the transposed reads of
   // 4 keys x 4 pieces per 16 lanes then cover all banks
   auto swz = [](int key) { return 2 * (key & 3); };
-  __shared__ __attribute__((aligned(16))) char vstage[MV ? 4 * 32 * SROW : 16];
+  static_assert(4 * 32 * SROW == kStageBytes, "staging area");
   char* stg = vstage + wave * (32 * SROW);
   const int vdg = wave % NDG, vkg = wave / NDG;  // the wave's dim group and key group
   const int lr = lane / 8, lc = lane % 8;        // load instruction: key, piece
@@ -1753,6 +1764,8 @@ static hipError_t launch_tdg(int mode, const DecodeParams& p, hipStream_t s) {
       default: return hipErrorInvalidValue;
     }
   } else {
+    // the block cache's slot positions of a range are staged in the kernel's 16 KiB area
+    if (mode == kModeMaskedLogits && (size_t)p.chunk * sizeof(int) > 16384) return hipErrorInvalidValue;
     const size_t lds = twopass_lds_floats<D, G>(p.chunk) * sizeof(float);
     switch (mode) {
       case kModeRope: hipLaunchKernelGGL((decode_twopass_kernel<T, D, G, kModeRope>), grid, block, lds, s, p); break;
