@@ -530,21 +530,26 @@ __device__ inline void split_finish(const DecodeParams& p, float* ored, const fl
         __syncthreads();
       }
       for (int s1 = 0; s1 < ns; s1 += SU) {
+        // every load in range and unconditional (past the splits: the last split's partial,
+        // dropped below), so none waits for another: a load under a branch would make the
+        // compiler wait for it at the branch's end
         float x[SU][EPT];
 #pragma unroll
         for (int u = 0; u < SU; ++u)
 #pragma unroll
           for (int k = 0; k < EPT; ++k) {
-            const int idx = threadIdx.x + k * kDecodeThreads;
-            const bool in = s1 + u < ns && idx < G * D;
-            x[u][k] = in ? load_dev(&p.part_o[((size_t)(s0 + s1 + u) * BH + bh0) * D + idx]) : 0.f;
+            const int idx = min((int)threadIdx.x + k * kDecodeThreads, G * D - 1);
+            const int sp = min(s0 + s1 + u, n_splits - 1);
+            x[u][k] = load_dev(&p.part_o[((size_t)sp * BH + bh0) * D + idx]);
           }
 #pragma unroll
         for (int u = 0; u < SU; ++u)
 #pragma unroll
           for (int k = 0; k < EPT; ++k) {
-            const int idx = threadIdx.x + k * kDecodeThreads;
-            if (s1 + u < ns && idx < G * D) acc[k] = fmaf(x[u][k], wsp[(s1 + u) * G + idx / D], acc[k]);
+            const int idx = min((int)threadIdx.x + k * kDecodeThreads, G * D - 1);
+            const int su = min(s1 + u, ns - 1);  // an in-range weight (the select drops it)
+            const float t = fmaf(x[u][k], wsp[su * G + idx / D], acc[k]);
+            acc[k] = s1 + u < ns ? t : acc[k];
           }
       }
       __syncthreads();  // wsp is rewritten by the next group
