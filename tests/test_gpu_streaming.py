@@ -170,6 +170,24 @@ def test_fused_step_bf16_shapes(L, G, D, S, W, pre, steps):
     _run_stream(L, w, checks, sample_bg=[(0, 0), (1, 1)], check_slots=True, fused=True)
 
 
+@pytest.mark.parametrize("G,D,steps", [
+    (1, 128, 130),  # one-pass kernel: anchors every 128 keys of a lane group
+    (4, 128, 200),  # two-pass, RoPE at G = 4: anchors every 192 keys
+    (6, 256, 70),   # two-pass, G = 6, D = 256: anchors every 64 keys
+    (8, 128, 40),   # two-pass, G = 8: a table row every iteration
+])
+def test_rope_rows_across_breakpoints(L, G, D, steps):
+    """Keys' RoPE table rows are carried from key to key by angle addition and read only at
+    anchors and where a rank breakpoint (the sink boundary, the ring's oldest slot) interrupts
+    the sequence.  A wrapped 4 + 2044 ring of 16 rows x 8 KV heads (4 splits of 512 slots per
+    row and head) is stepped while the oldest slot sweeps every phase of the anchor period
+    inside a split, and every step is checked."""
+    w = scaled(WORKLOADS["llama2_7b_layer"], name=f"rope_rows_G{G}_D{D}", batch=16, n_kv_heads=8,
+               n_q_heads=8 * G, head_dim=D, n_sink=4, window=2044, prefill=2300, steps=steps)
+    print(f"[rope rows G={G} D={D}] {steps} steps, every step checked", flush=True)
+    _run_stream(L, w, set(range(steps)), sample_bg=[(0, 0), (9, 5)], fused=True)
+
+
 def test_many_splits_grouped_merge(L):
     """B=1, 4/1 heads, D=128, 4+8188 wrapped: the plan gives more than 64 splits of one
     (row, KV head), so the merge stages its per-split weights in more than one group."""
