@@ -41,11 +41,11 @@ struct bf16_t {
 constexpr int kUnrollG2 = 2;
 constexpr int kUnrollOnepassBig = 1;
 constexpr int kOnepassMaxG = 2;  // largest G served by the one-pass kernel
-// H2O epilogue: slots per thread per iteration (token-level, block-level eviction).  More
-// would keep more registers live in the merging workgroup than the main loop needs, and
-// the kernel's register count (its occupancy) is the larger of the two.
-constexpr int kH2oEu = 16;
-constexpr int kH2oEuBlk = 8;
+// H2O epilogue: slots per thread per iteration (token-level and block-level eviction).  Four
+// measured fastest at a budget of 4096 slots (1, 2, 6, 8, 12 and 16 were 0.5-3 us slower per
+// launch, at the same register count).
+constexpr int kH2oEu = 4;
+constexpr int kH2oEuBlk = 4;
 template <bool BLOCKS>
 constexpr int EU_OF() { return BLOCKS ? kH2oEuBlk : kH2oEu; }
 constexpr int kMergeSu = 4;  // split merge: splits whose loads are issued together
