@@ -221,6 +221,11 @@ __device__ inline void group_sum_n(float (&x)[M]) {
   }
 }
 
+// 2^x by the hardware instruction alone (v_exp_f32) for the softmax weights, x <= 0: it
+// differs from exp2f only where the result is below 2^-126, which exp2f rescales to get
+// subnormal results right; weights that small add nothing to a sum that holds a 1.
+__device__ inline float exp2_weight(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ inline float wave_max(float x) {
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
@@ -976,7 +981,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_onepass_kernel(DecodePa
     if (__any(grow)) {
 #pragma unroll
       for (int j = 0; j < G; ++j) {
-        const float corr = mn[j] == -INFINITY ? 1.f : exp2f(m[j] - mn[j]);
+        const float corr = mn[j] == -INFINITY ? 1.f : exp2_weight(m[j] - mn[j]);
         m[j] = mn[j];
         l[j] *= corr;
 #pragma unroll
@@ -989,7 +994,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_onepass_kernel(DecodePa
 #pragma unroll
       for (int j = 0; j < G; ++j) {
         const float x = d[u * G + j];
-        const float pw = x == -INFINITY ? 0.f : exp2f(x - m[j]);
+        const float pw = x == -INFINITY ? 0.f : exp2_weight(x - m[j]);
         d[u * G + j] = pw;
         l[j] += pw;
       }
@@ -1533,7 +1538,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
   for (int key = threadIdx.x; key < cnt; key += kDecodeThreads) {
 #pragma unroll
     for (int j = 0; j < G; ++j) {
-      const float e = exp2f(xs[j * XS + key] - M[j]);
+      const float e = exp2_weight(xs[j * XS + key] - M[j]);
       xs[j * XS + key] = e;
       ls[j] += e;
     }
