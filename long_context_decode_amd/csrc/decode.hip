@@ -1481,7 +1481,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_twopass_kernel(DecodePa
   constexpr int KSTR = KGN * 32;       // keys between a key group's consecutive tiles
   constexpr int IPT = 4;               // load instructions per tile (8 keys x 128 bytes each)
   constexpr int NT = 4;                // 16-dim column tiles per wave
-  constexpr int PFT = 4;               // tiles in flight
+  constexpr int PFT = 3;               // tiles in flight (2, 4, 6 and 8 measured slower)
   constexpr int SROW = 128;            // bytes of a staged row
   static_assert(!MV || 2 * G <= 16, "hi and lo weight rows of G query heads fill at most 16 rows");
   // staged piece c of key k sits at piece c ^ swz(k) of its row: the transposed reads of
